@@ -1,0 +1,152 @@
+/*
+ * specverify — batched verify-and-accept step of speculative decoding on MI355X (gfx950).
+ *
+ * For B sequences with K draft tokens each, the library takes the target model's and
+ * the draft model's logits over a vocabulary of V ids at every draft position and
+ * returns, per sequence, how many draft tokens are accepted and the tokens to emit.
+ *
+ * Operations and where they are defined (page title, section):
+ *  - Sampling verify: "推测性拒绝采样" (speculative rejection sampling), steps 2-4
+ *    (parallel verification, probability-ratio acceptance, truncation at the first
+ *    rejection, replacement drawn at that position) and its "key guarantee" section
+ *    (output distribution identical to the target's), which fixes the replacement law
+ *    as the normalised residual max(0, p - q); the bonus token after K acceptances is
+ *    the gamma+1 draw of the "Speculative Contrastive Decoding" review, SCD section.
+ *  - Greedy blockwise verify: "Blockwise Parallel Decoding", section 3.5 (Verify and
+ *    Accept: longest prefix on which the target's argmax equals the proposals).
+ *  - Contrastive-target verify: "Speculative Contrastive Decoding" review, sections on
+ *    contrastive decoding (large-model minus small-model distribution) and SCD.
+ *
+ * Conventions for every entry point below:
+ *  - All array pointers are DEVICE pointers owned by the caller; arrays are row-major and
+ *    contiguous.  Logits are float32 (SPECVERIFY_F32) or bfloat16 (SPECVERIFY_BF16) and
+ *    must be aligned to their element size; int32 / float arrays to 4 bytes.
+ *  - hip_stream is a hipStream_t (NULL = the default stream).  Calls only enqueue work on
+ *    it and return; results are valid once the caller has synchronised that stream.
+ *  - The context owns a device workspace sized at creation; one call may be in flight per
+ *    context at a time (use one context per concurrent stream).  Only specverify_create
+ *    allocates device memory.
+ *  - Host-detectable errors return before anything is enqueued and leave all outputs
+ *    untouched: NULL context or required pointer, negative sizes, V < 1, a non-positive or
+ *    non-finite temperature, or a misaligned pointer -> SPECVERIFY_EINVAL; B, K or V above
+ *    the context's capacity -> SPECVERIFY_ECAPACITY; an unknown dtype ->
+ *    SPECVERIFY_EUNSUPPORTED; a failed launch -> SPECVERIFY_EHIP.
+ *  - Token ids cannot be checked on the host without a synchronisation.  A sequence whose
+ *    draft tokens / proposals fall outside [0, V) gets accepted_len = -1, all-(-1) tokens
+ *    and NaN out_probs; the other sequences are unaffected.
+ *  - B = 0 is a no-op.  K = 0 is plain sampling from p_0 (or the argmax of row 0).
+ *  - Logits may be -inf (zero probability) provided every row has a finite entry; NaN
+ *    and +inf are outside the contract.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct specverify_ctx specverify_ctx;
+
+enum specverify_dtype { SPECVERIFY_F32 = 0, SPECVERIFY_BF16 = 1 };
+
+enum specverify_status {
+    SPECVERIFY_OK = 0,
+    SPECVERIFY_EINVAL = -1,
+    SPECVERIFY_EUNSUPPORTED = -2,
+    SPECVERIFY_ENOMEM = -3,
+    SPECVERIFY_EHIP = -4,
+    SPECVERIFY_ECAPACITY = -5
+};
+
+/* Largest K a context accepts (one wave64 lane per draft position). */
+#define SPECVERIFY_MAX_K 63
+
+/*
+ * Create a context on HIP device `device` for calls with B <= max_batch, K <= max_k and
+ * V <= max_vocab, allocating its device workspace there (a few MB for the largest
+ * vocabularies; see specverify_workspace_bytes).  On success *out receives the context.
+ * Errors: EINVAL (out NULL, sizes < 1, max_k > SPECVERIFY_MAX_K), EHIP (bad device),
+ * ENOMEM (allocation failed).
+ */
+int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab);
+
+/* Bytes of device workspace the context holds. */
+int64_t specverify_workspace_bytes(const specverify_ctx *ctx);
+
+/*
+ * Sampling verify.  With T the temperature, p_j = softmax(l_target[b,j,:] / T) for
+ * j in [0, K] and q_j = softmax(l_draft[b,j,:] / T) for j < K:
+ *  - draft token x_j is accepted iff p_j(x_j) > 0 and u[b,j] * q_j(x_j) <= p_j(x_j)
+ *    (kept outright when the target favours it, else with probability p/q);
+ *  - L = the first rejected position, or K if none;
+ *  - the emitted token at position L is drawn by inverse CDF (ascending id, first id
+ *    whose inclusive prefix sum exceeds u[b,K] * W) from w = max(0, p_L - q_L) when
+ *    L < K, or from w = p_K when every draft token is accepted (if rounding leaves
+ *    the residual empty, from p_L).
+ *  target_logits [B][K+1][V], draft_logits [B][K][V] (dtype), draft_tokens [B][K] int32,
+ *  uniforms [B][K+1] float in [0,1]: u[b,0..K-1] accept tests, u[b,K] the replacement or
+ *  bonus draw.
+ *  Outputs: accepted_len [B] int32 (L, or -1 for bad ids), out_tokens [B][K+1] int32
+ *  (x_0..x_{L-1}, the drawn token, then -1), out_probs [B][K][2] float
+ *  (p_j(x_j), q_j(x_j) for every j < K) or NULL.
+ *  Arithmetic: fp32 row statistics from one read of every logit, fp64 combination,
+ *  decisions and residual prefix sums.
+ */
+int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
+                            int V, float temperature, const void *target_logits,
+                            const void *draft_logits, const int32_t *draft_tokens,
+                            const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                            float *out_probs);
+
+/*
+ * Greedy blockwise verify.  g_j = the lowest id among the maxima of l_target[b,j,:]
+ * (raw value comparison) for j in [0, K]; L = the first j < K with proposals[b,j] != g_j,
+ * else K.  target_logits [B][K+1][V] (dtype), proposals [B][K] int32.
+ * Outputs: accepted_len [B] (L or -1 for bad ids), out_tokens [B][K+1] (g_0..g_L, then -1).
+ */
+int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
+                          const void *target_logits, const int32_t *proposals,
+                          int32_t *accepted_len, int32_t *out_tokens);
+
+/*
+ * Contrastive-target verify: as specverify_run_sampling with the target law
+ * p_j = softmax((l_expert[b,j,:] - l_amateur[b,j,:]) / tau) for j in [0, K] (the
+ * difference formed in fp32) and the draft law q_j = softmax(l_amateur[b,j,:]) for j < K.
+ * expert_logits and amateur_logits are both [B][K+1][V] (dtype); the amateur rows
+ * 0..K-1 are the draft model's.
+ */
+int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
+                               int V, float tau, const void *expert_logits,
+                               const void *amateur_logits, const int32_t *draft_tokens,
+                               const float *uniforms, int32_t *accepted_len,
+                               int32_t *out_tokens, float *out_probs);
+
+/* Release the context and its workspace.  NULL-safe; returns SPECVERIFY_OK. */
+int specverify_destroy(specverify_ctx *ctx);
+
+/* Static description of a status code. */
+const char *specverify_strerror(int status);
+
+/*
+ * Kernel timing.  Kernel kinds, in launch order within a call:
+ *   0 row statistics (sampling / contrastive), 1 accept + first-reject scan,
+ *   2 residual chunk sums, 3 residual / bonus draw, 4 row argmax (greedy),
+ *   5 greedy compare + emit.
+ * specverify_profile_begin(ctx, max_calls) creates hipEvent pairs for up to max_calls
+ * subsequent run_* calls and records one pair around every kernel they launch, on the
+ * call's stream.  specverify_profile_end(ctx, ms, launches) synchronises on the recorded
+ * events, writes the summed milliseconds and launch counts per kind into the two
+ * SPECVERIFY_NUM_KERNELS-long arrays (either may be NULL), and releases the events.
+ * Errors: EINVAL (NULL ctx, max_calls < 1, end without begin), EHIP.
+ */
+#define SPECVERIFY_NUM_KERNELS 6
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls);
+int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

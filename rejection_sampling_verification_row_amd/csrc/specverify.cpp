@@ -1,0 +1,311 @@
+// C-ABI runtime: context and workspace, host-side argument validation, launch sequencing on
+// the caller's stream, kernel timing.  The kernels live in sv_kernels.hip.
+#include "specverify.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "sv_internal.h"
+
+struct specverify_ctx {
+    int device;
+    int max_batch, max_k, max_vocab, max_nch;
+    void *mem;
+    size_t bytes;
+    sv::Workspace ws;
+    // timing
+    bool prof;
+    int prof_cap, prof_calls;
+    std::vector<hipEvent_t> events;       // prof_cap * 2 * SPECVERIFY_NUM_KERNELS
+    std::vector<unsigned> launched;       // per recorded call: bit k = kernel kind k ran
+};
+
+namespace {
+
+constexpr int NK = SPECVERIFY_NUM_KERNELS;
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = (err == hipSuccess);
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (changed)
+            (void)hipSetDevice(prev);
+    }
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned_to(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(const specverify_ctx *ctx, int dtype, int B, int K, int V)
+{
+    if (!ctx)
+        return SPECVERIFY_EINVAL;
+    if (dtype != SPECVERIFY_F32 && dtype != SPECVERIFY_BF16)
+        return SPECVERIFY_EUNSUPPORTED;
+    if (B < 0 || K < 0 || V < 1)
+        return SPECVERIFY_EINVAL;
+    if (B > ctx->max_batch || K > ctx->max_k || V > ctx->max_vocab)
+        return SPECVERIFY_ECAPACITY;
+    return SPECVERIFY_OK;
+}
+
+bool bad_temperature(float t) { return !(t > 0.0f) || !isfinite(t); }
+
+// event pair array for the next call when timing is on, NULL otherwise
+hipEvent_t *next_events(specverify_ctx *ctx)
+{
+    if (!ctx->prof || ctx->prof_calls >= ctx->prof_cap)
+        return nullptr;
+    return ctx->events.data() + (size_t)ctx->prof_calls * 2 * NK;
+}
+
+void note_call(specverify_ctx *ctx, hipEvent_t *ev, unsigned kinds)
+{
+    if (ev) {
+        ctx->launched[ctx->prof_calls] = kinds;
+        ctx->prof_calls++;
+    }
+}
+
+int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, int B, int K, int V,
+                      float temperature, const void *tgt, const void *drf, const int32_t *tokens,
+                      const float *unif, int32_t *acc_len, int32_t *out_tokens, float *out_probs)
+{
+    int rc = check_common(ctx, dtype, B, K, V);
+    if (rc != SPECVERIFY_OK)
+        return rc;
+    if (bad_temperature(temperature))
+        return SPECVERIFY_EINVAL;
+    if (B == 0)
+        return SPECVERIFY_OK;
+    const bool need_draft = (mode == sv::CONTRASTIVE) || K > 0;
+    if (!tgt || !unif || !acc_len || !out_tokens || (need_draft && !drf) || (K > 0 && !tokens))
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(tgt, es) || (drf && !aligned_to(drf, es)) || (tokens && !aligned_to(tokens, 4)) ||
+        !aligned_to(unif, 4) || !aligned_to(acc_len, 4) || !aligned_to(out_tokens, 4) ||
+        (out_probs && !aligned_to(out_probs, 4)))
+        return SPECVERIFY_EINVAL;
+
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    const sv::Scale sp = sv::make_scale((double)temperature);
+    const sv::Scale sq = (mode == sv::CONTRASTIVE) ? sv::make_scale(1.0) : sp;
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(stream), ev};
+    hipError_t e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
+                                       unif, acc_len, out_tokens, out_probs);
+    note_call(ctx, ev, 0xFu);
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab)
+{
+    if (!out || max_batch < 1 || max_k < 0 || max_k > SPECVERIFY_MAX_K || max_vocab < 1)
+        return SPECVERIFY_EINVAL;
+    *out = nullptr;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+        return SPECVERIFY_EHIP;
+    DeviceGuard g(device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+
+    const size_t nch = (size_t)sv::max_chunks(max_vocab);
+    const size_t rows = (size_t)max_batch * (2 * (size_t)max_k + 1);
+    const size_t b_m = align_up(rows * nch * sizeof(float));
+    const size_t b_s = align_up(rows * nch * sizeof(double));
+    const size_t b_i = align_up(rows * nch * sizeof(int));
+    const size_t b_q = align_up((size_t)max_batch * sizeof(sv::SeqInfo));
+    const size_t b_r = align_up((size_t)max_batch * nch * 2 * sizeof(double));
+    const size_t total = b_m + b_s + b_i + b_q + b_r;
+
+    specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
+    if (!ctx)
+        return SPECVERIFY_ENOMEM;
+    if (hipMalloc(&ctx->mem, total) != hipSuccess) {
+        delete ctx;
+        return SPECVERIFY_ENOMEM;
+    }
+    char *p = static_cast<char *>(ctx->mem);
+    ctx->ws.part_m = reinterpret_cast<float *>(p);
+    p += b_m;
+    ctx->ws.part_s = reinterpret_cast<double *>(p);
+    p += b_s;
+    ctx->ws.part_i = reinterpret_cast<int *>(p);
+    p += b_i;
+    ctx->ws.seq = reinterpret_cast<sv::SeqInfo *>(p);
+    p += b_q;
+    ctx->ws.resid = reinterpret_cast<double *>(p);
+    ctx->device = device;
+    ctx->max_batch = max_batch;
+    ctx->max_k = max_k;
+    ctx->max_vocab = max_vocab;
+    ctx->max_nch = (int)nch;
+    ctx->bytes = total;
+    ctx->prof = false;
+    ctx->prof_cap = ctx->prof_calls = 0;
+    *out = ctx;
+    return SPECVERIFY_OK;
+}
+
+int64_t specverify_workspace_bytes(const specverify_ctx *ctx) { return ctx ? (int64_t)ctx->bytes : 0; }
+
+int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
+                            float temperature, const void *target_logits, const void *draft_logits,
+                            const int32_t *draft_tokens, const float *uniforms,
+                            int32_t *accepted_len, int32_t *out_tokens, float *out_probs)
+{
+    return run_sampling_like(ctx, hip_stream, sv::SAMPLING, dtype, B, K, V, temperature,
+                             target_logits, draft_logits, draft_tokens, uniforms, accepted_len,
+                             out_tokens, out_probs);
+}
+
+int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
+                               int V, float tau, const void *expert_logits,
+                               const void *amateur_logits, const int32_t *draft_tokens,
+                               const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                               float *out_probs)
+{
+    return run_sampling_like(ctx, hip_stream, sv::CONTRASTIVE, dtype, B, K, V, tau, expert_logits,
+                             amateur_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                             out_probs);
+}
+
+int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
+                          const void *target_logits, const int32_t *proposals,
+                          int32_t *accepted_len, int32_t *out_tokens)
+{
+    int rc = check_common(ctx, dtype, B, K, V);
+    if (rc != SPECVERIFY_OK)
+        return rc;
+    if (B == 0)
+        return SPECVERIFY_OK;
+    if (!target_logits || !accepted_len || !out_tokens || (K > 0 && !proposals))
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(target_logits, es) || (proposals && !aligned_to(proposals, 4)) ||
+        !aligned_to(accepted_len, 4) || !aligned_to(out_tokens, 4))
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev};
+    hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
+                                     accepted_len, out_tokens);
+    note_call(ctx, ev, 0x30u);
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_destroy(specverify_ctx *ctx)
+{
+    if (!ctx)
+        return SPECVERIFY_OK;
+    {
+        DeviceGuard g(ctx->device);
+        for (hipEvent_t e : ctx->events)
+            (void)hipEventDestroy(e);
+        if (ctx->mem)
+            (void)hipFree(ctx->mem);
+    }
+    delete ctx;
+    return SPECVERIFY_OK;
+}
+
+const char *specverify_strerror(int status)
+{
+    switch (status) {
+    case SPECVERIFY_OK: return "ok";
+    case SPECVERIFY_EINVAL: return "invalid argument (null or misaligned pointer, bad size or temperature)";
+    case SPECVERIFY_EUNSUPPORTED: return "unsupported dtype";
+    case SPECVERIFY_ENOMEM: return "device memory allocation failed";
+    case SPECVERIFY_EHIP: return "HIP runtime or launch error";
+    case SPECVERIFY_ECAPACITY: return "batch, draft length or vocabulary exceeds the context's capacity";
+    default: return "unknown status";
+    }
+}
+
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls)
+{
+    if (!ctx || max_calls < 1 || ctx->prof)
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    ctx->events.assign((size_t)max_calls * 2 * NK, nullptr);
+    for (auto &e : ctx->events) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto &f : ctx->events)
+                if (f)
+                    (void)hipEventDestroy(f);
+            ctx->events.clear();
+            return SPECVERIFY_EHIP;
+        }
+    }
+    ctx->launched.assign((size_t)max_calls, 0u);
+    ctx->prof = true;
+    ctx->prof_cap = max_calls;
+    ctx->prof_calls = 0;
+    return SPECVERIFY_OK;
+}
+
+int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches)
+{
+    if (!ctx || !ctx->prof)
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    double tot[NK] = {0};
+    int cnt[NK] = {0};
+    int rc = (g.err == hipSuccess) ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+    for (int c = 0; c < ctx->prof_calls && rc == SPECVERIFY_OK; ++c) {
+        for (int k = 0; k < NK; ++k) {
+            if (!(ctx->launched[c] & (1u << k)))
+                continue;
+            hipEvent_t a = ctx->events[((size_t)c * NK + k) * 2];
+            hipEvent_t b = ctx->events[((size_t)c * NK + k) * 2 + 1];
+            float t = 0.0f;
+            if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&t, a, b) != hipSuccess) {
+                rc = SPECVERIFY_EHIP;
+                break;
+            }
+            tot[k] += t;
+            cnt[k] += 1;
+        }
+    }
+    for (hipEvent_t e : ctx->events)
+        (void)hipEventDestroy(e);
+    ctx->events.clear();
+    ctx->launched.clear();
+    ctx->prof = false;
+    ctx->prof_cap = ctx->prof_calls = 0;
+    if (ms)
+        for (int k = 0; k < NK; ++k)
+            ms[k] = tot[k];
+    if (launches)
+        for (int k = 0; k < NK; ++k)
+            launches[k] = cnt[k];
+    return rc;
+}
+
+}  // extern "C"

@@ -201,6 +201,11 @@ class Workload:
             seed=self.seed, meta=dict(self.meta))
 
 
+def _f32(t: float) -> float:
+    """Temperatures cross the C-ABI as float32; keep the float32 value everywhere."""
+    return float(np.float32(t))
+
+
 def _store(x: np.ndarray, dtype: int) -> np.ndarray:
     return f32_to_bf16_bits(x) if dtype == BF16 else np.ascontiguousarray(x, dtype=np.float32)
 
@@ -240,7 +245,7 @@ def make_sampling(B: int, K: int, V: int, dtype: int, temperature: float, seed: 
     tokens = gumbel_max_tokens(s_tokens, decode(draft, dtype), temperature).astype(np.int32)
     uniforms = lattice_uniforms(np.random.Generator(np.random.PCG64(s_unif)), (B, K + 1))
     return Workload(name=name, mode=SAMPLING, dtype=dtype, B=B, K=K, V=V,
-                    temperature=float(temperature), target=target, draft=draft,
+                    temperature=_f32(temperature), target=target, draft=draft,
                     tokens=np.ascontiguousarray(tokens.reshape(B, K)), uniforms=uniforms, seed=seed)
 
 
@@ -279,7 +284,7 @@ def make_contrastive(B: int, K: int, V: int, dtype: int, tau: float, seed: int, 
     tokens = gumbel_max_tokens(s_tokens, decode(amateur[:, :K, :], dtype), 1.0).astype(np.int32)
     uniforms = lattice_uniforms(np.random.Generator(np.random.PCG64(s_unif)), (B, K + 1))
     return Workload(name=name, mode=CONTRASTIVE, dtype=dtype, B=B, K=K, V=V,
-                    temperature=float(tau), target=expert, draft=amateur,
+                    temperature=_f32(tau), target=expert, draft=amateur,
                     tokens=np.ascontiguousarray(tokens.reshape(B, K)), uniforms=uniforms, seed=seed)
 
 

@@ -1,0 +1,69 @@
+"""The C-ABI library without a GPU: it builds for gfx950, loads, exports every entry point
+the header declares, and rejects a NULL context before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from rejection_sampling_verification_row_amd import binding as sv
+from rejection_sampling_verification_row_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specverify_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("specverify_create", "specverify_run_sampling", "specverify_run_greedy",
+                 "specverify_run_contrastive", "specverify_destroy", "specverify_strerror"):
+        assert want in names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = sv.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (specverify_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_gfx950_code(tmp_path):
+    """The embedded device code is built for gfx950 and nothing else."""
+    fb = str(tmp_path / "fatbin.bin")
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", build.LIB, fb],
+                   check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          "--input=" + fb], capture_output=True, text=True, check=True).stdout
+    targets = [t for t in out.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), out
+
+
+def test_strerror_covers_every_status():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert sv.specverify_strerror(code) != "unknown status"
+    assert sv.specverify_strerror(12345) == "unknown status"
+
+
+def test_null_context_is_rejected_on_the_host():
+    lib = sv.load()
+    assert lib.specverify_run_sampling(None, None, 1, 1, 1, 8, 1.0, *([None] * 7)) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_run_contrastive(None, None, 1, 1, 1, 8, 1.0, *([None] * 7)) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_run_greedy(None, None, 1, 1, 1, 8, None, None, None, None) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_destroy(None) == sv.SPECVERIFY_OK
+    assert lib.specverify_profile_begin(None, 4) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_end(None, None, None) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_workspace_bytes(None) == 0
+    h = ctypes.c_void_p()
+    assert lib.specverify_create(None, 0, 1, 1, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_create(ctypes.byref(h), 0, 0, 1, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_create(ctypes.byref(h), 0, 1, 64, 1) == sv.SPECVERIFY_EINVAL

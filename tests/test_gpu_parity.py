@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle (needs an MI355X).
+
+Full-size workloads run exactly as the benchmark launches them; at the two largest sizes
+the oracle checks a seeded sample of sequences (it computes each sequence on its own).
+Smaller shapes span several chunks, ragged tails, misaligned rows and the degenerate cases.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_support import compare, dev, run
+from rejection_sampling_verification_row_amd import binding as sv
+from rejection_sampling_verification_row_amd import synth
+from rejection_sampling_verification_row_amd.synth import BF16, F32
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    h = sv.specverify_create(0, 1024, 16, 160000)
+    yield h
+    sv.specverify_destroy(h)
+
+
+def _report(name, rep):
+    print("\n[%s] %s" % (name, rep), flush=True)
+
+
+# ----------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("cfg,sample", [("c1", None), ("c2", None), ("c3", 48), ("c4", None),
+                                        ("c5", 40)])
+def test_full_size_workload(ctx, cfg, sample):
+    print("\n[%s] generating" % cfg, flush=True)
+    w = synth.CONFIGS[cfg]()
+    g = run(ctx, w)
+    if sample is None:
+        seqs = list(range(w.B))
+        o = oracle.run_workload(w)
+    else:
+        seqs = sorted(np.random.default_rng(77).choice(w.B, sample, replace=False).tolist())
+        o = oracle.run_workload(w.subset(seqs))
+    rep = compare(w, g, o, seqs)
+    _report(w.name, rep)
+    # every sequence of the batch (sampled or not) is well formed
+    for b in range(w.B):
+        L = int(g.accepted_len[b])
+        assert 0 <= L <= w.K
+        assert np.array_equal(g.out_tokens[b, :L], w.tokens[b, :L]) or w.mode == "greedy"
+        assert 0 <= g.out_tokens[b, L] < w.V and np.all(g.out_tokens[b, L + 1:] == -1)
+
+
+# ----------------------------------------------------------------- small shapes
+
+SMALL = [
+    # mode, dtype, B, K, V
+    ("sampling", F32, 3, 2, 1),
+    ("sampling", F32, 5, 0, 37),
+    ("sampling", BF16, 7, 3, 2),
+    ("sampling", BF16, 37, 5, 1001),
+    ("sampling", F32, 11, 4, 8193),      # one f32 chunk (8192 ids) and one id
+    ("sampling", BF16, 9, 3, 16385),     # one bf16 chunk (16384 ids) and one id
+    ("sampling", BF16, 6, 12, 50001),
+    ("sampling", F32, 4, 7, 40000),
+    ("contrastive", BF16, 13, 3, 999),
+    ("contrastive", F32, 5, 0, 8191),
+    ("contrastive", BF16, 8, 4, 40003),
+    ("greedy", BF16, 40, 6, 33),
+    ("greedy", F32, 9, 0, 5),
+    ("greedy", BF16, 12, 8, 70001),
+    ("greedy", F32, 10, 3, 16400),
+]
+
+
+def _small(mode, dtype, B, K, V, seed):
+    if mode == "sampling":
+        return synth.make_sampling(B, K, V, dtype, 0.85, seed, target_sigma=2.5, draft_sigma=1.0)
+    if mode == "contrastive":
+        return synth.make_contrastive(B, K, V, dtype, 1.3, seed)
+    return synth.make_greedy(B, K, V, dtype, seed, sigma=1.0 if dtype == BF16 else 3.0)
+
+
+@pytest.mark.parametrize("mode,dtype,B,K,V", SMALL)
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_small_shapes(ctx, mode, dtype, B, K, V, misalign):
+    w = _small(mode, dtype, B, K, V, seed=100 + B * 7 + K * 3 + V)
+    g = run(ctx, w, misalign=misalign)
+    rep = compare(w, g, oracle.run_workload(w))
+    _report("%s %s B=%d K=%d V=%d misalign=%d" % (mode, synth.DTYPE_NAMES[dtype], B, K, V,
+                                                   misalign), rep)
+
+
+def test_neg_inf_logits(ctx):
+    w = synth.make_sampling(24, 3, 3000, BF16, 1.0, 9, target_sigma=2.0)
+    rng = np.random.default_rng(1)
+    ninf = synth.f32_to_bf16_bits(np.float32([-np.inf]))[0]
+    for arr in (w.target, w.draft):
+        mask = rng.random(arr.shape) < 0.3
+        arr[mask] = ninf
+    # keep the drafted ids at finite draft logits so that they could have been drawn
+    for b in range(w.B):
+        for j in range(w.K):
+            w.draft[b, j, w.tokens[b, j]] = synth.f32_to_bf16_bits(np.float32([1.0]))[0]
+    rep = compare(w, run(ctx, w), oracle.run_workload(w))
+    _report("-inf logits", rep)
+
+
+def test_bad_ids_become_sentinels(ctx):
+    for mode in ("sampling", "contrastive", "greedy"):
+        w = _small(mode, BF16, 10, 3, 500, seed=3)
+        w.tokens[2, 1] = 500
+        w.tokens[7, 0] = -1
+        g = run(ctx, w)
+        rep = compare(w, g, oracle.run_workload(w))
+        assert rep.sentinel == 2
+        for b in (2, 7):
+            assert g.accepted_len[b] == -1 and np.all(g.out_tokens[b] == -1)
+
+
+def test_empty_batch_is_a_no_op(ctx):
+    acc = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    sv.specverify_run_sampling(ctx, None, BF16, 0, 3, 100, 1.0, None, None, None, None, None, None)
+    sv.specverify_run_greedy(ctx, None, BF16, 0, 3, 100, None, None, acc, None)
+    torch.cuda.synchronize()
+    assert int(acc.item()) == 5
+
+
+# ----------------------------------------------------------------- the pages' examples
+
+def test_worked_examples(ctx):
+    f = json.load(open(os.path.join(GOLDEN, "p3_blockwise_in_the_car.json")))
+    ids = {w: i for i, w in enumerate(f["vocab"])}
+    K, V = f["K"], len(f["vocab"])
+    t = dev(np.array(f["target_logits"], np.float32)[None])
+    x = dev(np.array([[ids[w] for w in f["proposals"]]], np.int32))
+    acc = torch.empty(1, dtype=torch.int32, device="cuda")
+    tok = torch.empty((1, K + 1), dtype=torch.int32, device="cuda")
+    sv.specverify_run_greedy(ctx, None, F32, 1, K, V, t, x, acc, tok)
+    want = [-1 if w is None else ids[w] for w in f["expected_tokens"]]
+    assert int(acc.item()) == f["expected_accepted_len"] and tok.cpu().tolist()[0] == want
+
+    f = json.load(open(os.path.join(GOLDEN, "p4_the_quick_fast.json")))
+    ids = {w: i for i, w in enumerate(f["vocab"])}
+    K, V = f["K"], len(f["vocab"])
+    t = dev(np.array(f["target_logits"], np.float32)[None])
+    d = dev(np.array(f["draft_logits"], np.float32)[None])
+    x = dev(np.array([[ids[w] for w in f["draft_tokens"]]], np.int32))
+    u = dev(np.array([f["uniforms"]], np.float32))
+    acc = torch.empty(1, dtype=torch.int32, device="cuda")
+    tok = torch.empty((1, K + 1), dtype=torch.int32, device="cuda")
+    sv.specverify_run_sampling(ctx, None, F32, 1, K, V, f["temperature"], t, d, x, u, acc, tok)
+    want = [-1 if w is None else ids[w] for w in f["expected_tokens"]]
+    assert int(acc.item()) == f["expected_accepted_len"] and tok.cpu().tolist()[0] == want
+
+
+# ----------------------------------------------------------------- distribution invariance
+
+def test_distribution_invariance_on_the_batch_axis(ctx):
+    """V=8, K=2: every (x_0, u_0, u_2) grid point is one sequence of the batch; the law of
+    the first emitted token must be p_0 within the grid's 3/N (and every sequence must
+    match the oracle under the parity rule)."""
+    rng = np.random.default_rng(2024)
+    t = (np.round(rng.normal(0, 1.2, (3, 8)) * 16) / 16).astype(np.float32)
+    d = (np.round((t[:2] + rng.normal(0, 0.9, (2, 8))) * 16) / 16).astype(np.float32)
+    N = 128
+    g1 = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    U0, U2 = [a.ravel() for a in np.meshgrid(g1, g1, indexing="ij")]
+    X0 = np.repeat(np.arange(8), N * N)
+    B = X0.size
+    w = synth.Workload(name="v8 grid", mode="sampling", dtype=F32, B=B, K=2, V=8,
+                       temperature=1.0,
+                       target=np.ascontiguousarray(np.broadcast_to(t, (B, 3, 8))),
+                       draft=np.ascontiguousarray(np.broadcast_to(d, (B, 2, 8))),
+                       tokens=np.stack([X0, np.zeros(B, np.int64)], 1).astype(np.int32),
+                       uniforms=np.stack([np.tile(U0, 8), np.full(B, 0.5, np.float32),
+                                          np.tile(U2, 8)], 1).astype(np.float32))
+    h = sv.specverify_create(0, B, 2, 8)
+    try:
+        g = run(h, w)
+    finally:
+        sv.specverify_destroy(h)
+    rep = compare(w, g, oracle.run_workload(w))
+    _report("v8 grid", rep)
+    p = np.exp(t[0].astype(np.float64))
+    p /= p.sum()
+    q = np.exp(d[0].astype(np.float64))
+    q /= q.sum()
+    law = np.zeros(8)
+    for x0 in range(8):
+        y0 = g.out_tokens[X0 == x0, 0]
+        law += q[x0] * np.bincount(y0, minlength=8) / y0.size
+    assert np.max(np.abs(law - p)) <= 3.0 / N
+
+
+# ----------------------------------------------------------------- runtime behaviour
+
+def test_deterministic_and_stream_ordered(ctx):
+    w = synth.c2_sampling_mid(B=16)
+    s = torch.cuda.Stream()
+    a = run(ctx, w, stream=s)
+    b = run(ctx, w)
+    assert np.array_equal(a.accepted_len, b.accepted_len)
+    assert np.array_equal(a.out_tokens, b.out_tokens)
+    assert np.array_equal(a.out_probs.view(np.uint32), b.out_probs.view(np.uint32))
+
+
+def test_null_out_probs(ctx):
+    w = synth.c1_sampling_tiny(B=8, seed=5)
+    a = run(ctx, w, with_probs=False)
+    b = run(ctx, w)
+    assert np.array_equal(a.out_tokens, b.out_tokens)
+
+
+def test_host_side_errors(ctx):
+    w = synth.c1_sampling_tiny(B=2, seed=3)
+    t, d, x, u = dev(w.target), dev(w.draft), dev(w.tokens), dev(w.uniforms)
+    acc = torch.empty(2, dtype=torch.int32, device="cuda")
+    tok = torch.full((2, 5), 9, dtype=torch.int32, device="cuda")
+    E = sv.SpecVerifyError
+
+    def status(fn):
+        with pytest.raises(E) as ei:
+            fn()
+        return ei.value.status
+
+    run_s = sv.specverify_run_sampling
+    assert status(lambda: run_s(ctx, None, 7, 2, 4, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EUNSUPPORTED
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 0.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, float("nan"), t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 1.0, None, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 1.0, t, d, x, u, acc, None)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 17, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_ECAPACITY
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 200000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_ECAPACITY
+    assert status(lambda: run_s(ctx, None, F32, 2000, 4, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_ECAPACITY
+    assert status(lambda: run_s(ctx, None, F32, -1, 4, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 0, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 1.0, t.data_ptr() + 2, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: sv.specverify_run_greedy(ctx, None, BF16, 2, 4, 1000, t, None, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: sv.specverify_create(0, 0, 4, 10)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: sv.specverify_create(0, 4, 64, 10)) == sv.SPECVERIFY_EINVAL
+    torch.cuda.synchronize()
+    assert torch.all(tok == 9)  # nothing was written by any rejected call
+
+
+def test_profile_api(ctx):
+    w = synth.c2_sampling_mid(B=8)
+    sv.specverify_profile_begin(ctx, 4)
+    for _ in range(3):
+        run(ctx, w)
+    ms, n = sv.specverify_profile_end(ctx)
+    assert n["row_stats"] == 3 and n["draw"] == 3 and n["row_argmax"] == 0
+    assert all(v >= 0 for v in ms.values()) and ms["row_stats"] > 0
