@@ -130,10 +130,10 @@ int specverify_destroy(specverify_ctx *ctx);
 const char *specverify_strerror(int status);
 
 /*
- * Kernel timing.  Kernel kinds, in launch order within a call:
- *   0 row statistics (sampling / contrastive), 1 accept + first-reject scan,
- *   2 residual chunk sums, 3 residual / bonus draw, 4 row argmax (greedy),
- *   5 greedy compare + emit.
+ * Kernel timing.  Kernel kinds:
+ *   0 row statistics (sampling, contrastive), 1 accept test and first-rejection scan,
+ *   2 residual / bonus weight sums, 3 inverse-CDF draw, 4 row argmax (greedy),
+ *   5 proposal compare and emit (greedy).
  * specverify_profile_begin(ctx, max_calls) creates hipEvent pairs for up to max_calls
  * subsequent run_* calls and records one pair around every kernel they launch, on the
  * call's stream.  specverify_profile_end(ctx, ms, launches) synchronises on the recorded

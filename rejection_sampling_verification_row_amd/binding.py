@@ -26,7 +26,7 @@ SPECVERIFY_ECAPACITY = -5
 
 SPECVERIFY_MAX_K = 63
 SPECVERIFY_NUM_KERNELS = 6
-KERNEL_NAMES = ("row_stats", "accept_scan", "residual_chunks", "draw", "row_argmax",
+KERNEL_NAMES = ("row_stats", "accept_scan", "residual_sums", "draw", "row_argmax",
                 "greedy_emit")
 
 _lib = None

@@ -27,6 +27,7 @@ struct specverify_ctx {
 namespace {
 
 constexpr int NK = SPECVERIFY_NUM_KERNELS;
+static_assert(NK == sv::NUM_KINDS, "kernel kinds out of step with the header");
 
 struct DeviceGuard {
     int prev = -1;
@@ -111,7 +112,8 @@ int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, in
     sv::Launch ln{static_cast<hipStream_t>(stream), ev};
     hipError_t e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
                                        unif, acc_len, out_tokens, out_probs);
-    note_call(ctx, ev, 0xFu);
+    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_ACCEPT) | (1u << sv::KIND_RESID) |
+                           (1u << sv::KIND_DRAW));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 
@@ -133,12 +135,10 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
 
     const size_t nch = (size_t)sv::max_chunks(max_vocab);
     const size_t rows = (size_t)max_batch * (2 * (size_t)max_k + 1);
-    const size_t b_m = align_up(rows * nch * sizeof(float));
-    const size_t b_s = align_up(rows * nch * sizeof(double));
-    const size_t b_i = align_up(rows * nch * sizeof(int));
+    const size_t b_p = align_up(rows * nch * sv::WAVES * sizeof(float2));
     const size_t b_q = align_up((size_t)max_batch * sizeof(sv::SeqInfo));
-    const size_t b_r = align_up((size_t)max_batch * nch * 2 * sizeof(double));
-    const size_t total = b_m + b_s + b_i + b_q + b_r;
+    const size_t b_r = align_up((size_t)max_batch * nch * sv::NV_RESID * sizeof(double));
+    const size_t total = b_p + b_q + b_r;
 
     specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
     if (!ctx)
@@ -148,12 +148,8 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
         return SPECVERIFY_ENOMEM;
     }
     char *p = static_cast<char *>(ctx->mem);
-    ctx->ws.part_m = reinterpret_cast<float *>(p);
-    p += b_m;
-    ctx->ws.part_s = reinterpret_cast<double *>(p);
-    p += b_s;
-    ctx->ws.part_i = reinterpret_cast<int *>(p);
-    p += b_i;
+    ctx->ws.part = reinterpret_cast<float2 *>(p);
+    p += b_p;
     ctx->ws.seq = reinterpret_cast<sv::SeqInfo *>(p);
     p += b_q;
     ctx->ws.resid = reinterpret_cast<double *>(p);
@@ -214,7 +210,7 @@ int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int 
     sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev};
     hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
                                      accepted_len, out_tokens);
-    note_call(ctx, ev, 0x30u);
+    note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 

@@ -8,18 +8,26 @@
 
 namespace sv {
 
-// Work geometry shared by every streaming kernel.  A row of V logits is cut into chunks of
-// CHUNK_VECS 16-byte vectors; one 256-thread workgroup handles one chunk, each thread NV
-// vectors.  Chunks are aligned to element indices (chunk c covers ids [c*CE, (c+1)*CE)).
+// Work geometry.  A row of V logits is cut into chunks aligned to element ids: chunk c of a
+// pass with NV vectors per thread covers ids [c*CE, (c+1)*CE), CE = WG * NV * (16 / bytes).
+// One 256-thread workgroup handles one chunk; thread t loads vectors i*WG + t, i < NV, so a
+// wave's loads are 1 KiB contiguous.
 constexpr int WG = 256;               // threads per workgroup (4 wave64)
-constexpr int NV = 8;                 // 16-byte vectors per thread per chunk
-constexpr int CHUNK_VECS = WG * NV;   // 2048 vectors = 32 KiB of logits per chunk
+constexpr int WAVES = WG / 64;
+constexpr int NV_STATS = 8;           // sampling row statistics: 32 KiB per workgroup
+constexpr int NV_PAIR = 4;            // contrastive row pairs: 2 x 16 KiB per workgroup
+constexpr int NV_RESID = 8;           // residual / bonus weights
+constexpr int NV_ARGMAX = 8;          // greedy argmax
+constexpr int MAX_ROWS = 2 * 63 + 1;  // rows per sequence at the largest K
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
-inline int chunk_elems(int dtype) { return CHUNK_VECS * elems_per_vec(dtype); }
-inline int num_chunks(int dtype, int V) { return (V + chunk_elems(dtype) - 1) / chunk_elems(dtype); }
-// the most chunks any dtype needs for a row of V ids (float32 rows have the smaller chunks)
-inline int max_chunks(int V) { return num_chunks(0, V); }
+inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
+inline int num_chunks(int nv, int dtype, int V)
+{
+    return (V + chunk_elems(nv, dtype) - 1) / chunk_elems(nv, dtype);
+}
+// the most chunks any pass needs for a row of V ids (float32 pairs have the smallest chunks)
+inline int max_chunks(int V) { return num_chunks(NV_PAIR, 0, V); }
 
 // log2(e) / T split into two floats so that d * hi + d * lo carries ~48 bits of the
 // product: the exponent argument of every term then loses only one fp32 rounding.
@@ -31,28 +39,36 @@ struct Scale {
 };
 Scale make_scale(double temperature);
 
-// What the draw kernels need to know about one sequence after the accept scan.
+// What the residual / bonus pass needs to know about one sequence after the accept scan.
 struct SeqInfo {
     int L;           // first rejected position, K if none, -1 for bad ids
-    int pad;
     float Mp, Mq;    // row maxima of the target row L and of the draft row L (L < K)
-    double inv_sp;   // 1 / S of target row L
-    double inv_sq;   // 1 / S of draft row L (L < K)
+    float isp, isq;  // 1 / S of those rows
+    int pad[3];
 };
 
 enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };
 
 struct Workspace {
-    float *part_m;      // [rows][nch] chunk maxima (also argmax values in greedy mode)
-    double *part_s;     // [rows][nch] chunk sums of exp2((l - m) * c), relative to part_m
-    int *part_i;        // [rows][nch] chunk argmax ids (greedy)
+    float2 *part;       // [rows][nch][WAVES] per-wave (max, sum of exp2) or (max, id) partials
     SeqInfo *seq;       // [B]
-    double *resid;      // [B][nch][2] chunk sums of the draw weights: residual, target law
+    double *resid;      // [B][nch][NV_RESID] draw-weight totals of each chunk's vector rows
 };
 
 struct Launch {
     hipStream_t stream;
-    hipEvent_t *ev;     // NULL, or 2 events per kernel to time (start, stop)
+    hipEvent_t *ev;     // NULL, or 2 events per kernel kind to time (start, stop)
+};
+
+// kernel kinds for timing
+enum Kind {
+    KIND_STATS = 0,
+    KIND_ACCEPT = 1,
+    KIND_RESID = 2,
+    KIND_DRAW = 3,
+    KIND_ARGMAX = 4,
+    KIND_GREEDY_EMIT = 5,
+    NUM_KINDS = 6
 };
 
 hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,

@@ -1,15 +1,18 @@
 // gfx950 kernels for the batched verify-and-accept step of speculative decoding.
 //
-// Data path for one sampling / contrastive call (all on the caller's stream):
-//   k_stats_*      one read of every logit row: per 32 KiB chunk, the row maximum m and
-//                  S = sum exp2((l - m) * log2(e)/T) (fp32 terms, fp64 across threads)
-//   k_accept       one wave64 per sequence: merge chunk statistics (fp64), gather
-//                  p_j(x_j), q_j(x_j), accept iff p > 0 and u * q <= p, first rejection L
-//   k_resid_chunks re-read row L (target and draft, or target alone for the bonus draw):
-//                  per chunk, sum of w = max(0, p - q) (or p) and of p, in fp64
-//   k_draw         one workgroup per sequence: locate the chunk holding t = u_K * W, scan
-//                  it (fp64 block scan), emit the first id whose prefix sum exceeds t
-// Greedy blockwise calls run k_argmax (first maximum per chunk) and k_greedy_final.
+// A sampling or contrastive call is four launches on the caller's stream:
+//   k_stats_*  one read of every logit row (nontemporal 128-bit loads).  Each 256-thread
+//              workgroup reduces one chunk of a row to per-wave (max, sum exp2) partials.
+//   k_accept   one workgroup per sequence merges its partials in fp64, gathers
+//              p_j(x_j), q_j(x_j), accepts iff p > 0 and u * q <= p, finds the first
+//              rejection L and records row L.
+//   k_resid    re-read of row L (target and draft, or the target alone for the bonus
+//              draw): per chunk, the sum of w = max(0, p - q) (or p).
+//   k_draw     one workgroup per sequence finds the chunk holding t = u_K * W, then the
+//              vector and the id inside it (block scans), and emits the first id whose
+//              prefix weight exceeds t.
+// A greedy blockwise call is two launches: k_argmax reduces chunks to (max, first id) and
+// k_greedy_final compares each sequence's row argmaxes with its proposals.
 //
 // The operations follow the speculative rejection sampling page (steps 2-4, and the
 // "key guarantee" that fixes the residual law), the blockwise parallel decoding page
@@ -40,14 +43,24 @@ Scale make_scale(double temperature)
 
 // ------------------------------------------------------------------ element access
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load that streams past the caches (logits are read once per pass)
+__device__ inline uint4 load_stream(const char *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline uint4 load_plain(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
+
 template <int DT> struct Elt;
 
 template <> struct Elt<0> {  // float32
     static constexpr int EPV = 4;
     static constexpr int BYTES = 4;
-    __device__ static inline void vec(const char *p, float (&x)[4])
+    __device__ static inline void unpack(const uint4 v, float (&x)[4])
     {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p);
         x[0] = __uint_as_float(v.x);
         x[1] = __uint_as_float(v.y);
         x[2] = __uint_as_float(v.z);
@@ -62,9 +75,8 @@ template <> struct Elt<0> {  // float32
 template <> struct Elt<1> {  // bfloat16 = the upper half of a float32: widening is exact
     static constexpr int EPV = 8;
     static constexpr int BYTES = 2;
-    __device__ static inline void vec(const char *p, float (&x)[8])
+    __device__ static inline void unpack(const uint4 v, float (&x)[8])
     {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p);
         x[0] = __uint_as_float(v.x << 16);
         x[1] = __uint_as_float(v.x & 0xffff0000u);
         x[2] = __uint_as_float(v.y << 16);
@@ -90,7 +102,7 @@ __device__ inline void load_elems(const char *row, bool aligned, int e0, int V, 
 {
     constexpr int E = Elt<DT>::EPV;
     if (aligned && e0 + E <= V) {
-        Elt<DT>::vec(row + (size_t)e0 * Elt<DT>::BYTES, x);
+        Elt<DT>::unpack(load_plain(row + (size_t)e0 * Elt<DT>::BYTES), x);
     } else {
 #pragma unroll
         for (int k = 0; k < E; ++k)
@@ -98,7 +110,7 @@ __device__ inline void load_elems(const char *row, bool aligned, int e0, int V, 
     }
 }
 
-// 2^((d) * log2(e)/T) for d <= 0 with the scale split in two floats (see Scale).
+// 2^(d * log2(e)/T) for d <= 0 with the scale split in two floats (see Scale).
 __device__ inline float exp2s(float d, float hi, float lo)
 {
     float a = d * hi;
@@ -125,11 +137,31 @@ __device__ inline float wave_max(float v)
     return v;
 }
 
+__device__ inline float wave_sum_f(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
 __device__ inline double wave_sum(double v)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
         v += __shfl_xor(v, o);
+    return v;
+}
+
+// inclusive prefix sum over the wave's lanes (fixed order)
+__device__ inline double wave_incl_scan(double v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double n = __shfl_up(v, o);
+        if (lane >= o)
+            v += n;
+    }
     return v;
 }
 
@@ -152,59 +184,12 @@ __device__ inline void wave_argmax(float &v, int &i)
     }
 }
 
-// Combine per-thread (m, s) with s relative to m into the block's (M, S), S relative to M;
-// thread 0 stores them.  The rescale factors are formed in fp64.
-__device__ inline void block_stats(float m, float s, double c, float *out_m, double *out_s)
-{
-    __shared__ float sm[WG / 64];
-    __shared__ double ss[WG / 64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    __syncthreads();  // the arrays may still be read by a previous call
-    float M = wave_max(m);
-    if (lane == 0)
-        sm[w] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    double e = (s > 0.0f) ? (double)s * exp2(((double)m - (double)M) * c) : 0.0;
-    e = wave_sum(e);
-    if (lane == 0)
-        ss[w] = e;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        *out_m = M;
-        *out_s = ((ss[0] + ss[1]) + ss[2]) + ss[3];
-    }
-}
-
-__device__ inline void block_sum2(double a, double b, double *out_a, double *out_b)
-{
-    __shared__ double sa[WG / 64], sb[WG / 64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane == 0) {
-        sa[w] = a;
-        sb[w] = b;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        *out_a = ((sa[0] + sa[1]) + sa[2]) + sa[3];
-        *out_b = ((sb[0] + sb[1]) + sb[2]) + sb[3];
-    }
-}
-
 // exclusive prefix sum over the workgroup in thread order (fp64, fixed order)
 __device__ inline double block_exclusive_scan(double v)
 {
-    __shared__ double wtot[WG / 64];
+    __shared__ double wtot[WAVES];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double n = __shfl_up(inc, o);
-        if (lane >= o)
-            inc += n;
-    }
+    const double inc = wave_incl_scan(v, lane);
     double exc = __shfl_up(inc, 1);
     if (lane == 0)
         exc = 0.0;
@@ -217,10 +202,15 @@ __device__ inline double block_exclusive_scan(double v)
     return off + exc;
 }
 
-// ------------------------------------------------------------------ K1: row statistics
+// ------------------------------------------------------------------ row statistics
 
-// Per-thread (max, sum of exp2) over NV vectors already in registers.
-template <int E>
+// Per-thread (max, sum of exp2 relative to that max) over NV vectors in registers.
+// Each exponent argument is formed as fma(x, lo, fma(x, hi, -R)) with R = fl(m * hi): one
+// rounding of a value of the argument's own size, like (x - m) * c, but two instructions.
+// Every argument carries the same shift e = m * lo + (m * hi - R) (the second term exact
+// through fma), which is removed once from the thread's sum.  Needs |x * log2(e)/T| below
+// the float range.
+template <int E, int NV>
 __device__ inline void thread_stats(float (&x)[NV][E], const Scale &sc, float &m, float &s)
 {
     m = -INFINITY;
@@ -230,125 +220,137 @@ __device__ inline void thread_stats(float (&x)[NV][E], const Scale &sc, float &m
         for (int k = 0; k < E; ++k)
             m = fmaxf(m, x[i][k]);
     const float mr = (m == -INFINITY) ? 0.0f : m;  // an all -inf thread sums exact zeros
+    const float R = mr * sc.hi;
+    const float shift = __builtin_fmaf(mr, sc.lo, __builtin_fmaf(mr, sc.hi, -R));
     s = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         float t[E];
 #pragma unroll
         for (int k = 0; k < E; ++k)
-            t[k] = exp2s(x[i][k] - mr, sc.hi, sc.lo);
+            t[k] = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(x[i][k], sc.lo, __builtin_fmaf(x[i][k], sc.hi, -R)));
         s += tree_sum<E>(t);
+    }
+    s *= __builtin_amdgcn_exp2f(-shift);
+}
+
+// per-wave (M, S): S = sum over lanes of s * exp2((m - M) * log2(e)/T)
+__device__ inline float2 wave_stats(float m, float s, const Scale &sc)
+{
+    const float M = wave_max(m);
+    const float e = (s > 0.0f) ? s * exp2s(m - M, sc.hi, sc.lo) : 0.0f;
+    return make_float2(M, wave_sum_f(e));
+}
+
+// Store the workgroup's four per-wave partials from one thread after a barrier: a single
+// 32-byte write per workgroup streams better than four single-lane writes from the waves.
+__device__ inline void store_wave_partials(float2 v, float2 *dst)
+{
+    __shared__ float4 sp[WAVES / 2];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0)
+        reinterpret_cast<float2 *>(sp)[w] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float4 *d = reinterpret_cast<float4 *>(dst);
+        d[0] = sp[0];
+        d[1] = sp[1];
     }
 }
 
-// rows b*(2K+1)+k: k <= K target row (b, k), else draft row (b, k-K-1)
-template <int DT>
-__global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ tgt,
-                                                       const char *__restrict__ drf, int K, int V,
-                                                       int nch, Scale sc, float *part_m,
-                                                       double *part_s)
+// Load NV vectors per thread of chunk `cbase` of a row: streamed 16-byte loads when the
+// whole chunk is inside an aligned row, element loads (ids >= V as -inf) otherwise.
+template <int DT, int NV>
+__device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
+                                  float (&x)[NV][Elt<DT>::EPV])
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
-    const int R = 2 * K + 1;
-    const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
-    const int b = row / R, k = row - b * R;
-    const char *rp = (k <= K) ? tgt + ((size_t)b * (K + 1) + k) * (size_t)V * BY
-                              : drf + ((size_t)b * K + (k - K - 1)) * (size_t)V * BY;
-    const int cbase = c * CHUNK_VECS * E;
-    const bool al = aligned16(rp);
-    float x[NV][E];
-    if (al && cbase + CHUNK_VECS * E <= V) {
+    if (al && cbase + WG * NV * E <= V) {
+        uint4 raw[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            Elt<DT>::vec(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY, x[i]);
+            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            Elt<DT>::unpack(raw[i], x[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             load_elems<DT>(rp, al, cbase + (i * WG + threadIdx.x) * E, V, -INFINITY, x[i]);
     }
-    float m, s;
-    thread_stats<E>(x, sc, m, s);
-    block_stats(m, s, sc.c, part_m + blockIdx.x, part_s + blockIdx.x);
 }
 
-// one workgroup per (row pair (b, j), chunk): target values l_e - l_a (fp32), draft values l_a
-template <int DT>
-__global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
-                                                          const char *__restrict__ am, int K, int V,
-                                                          int nch, Scale sp, Scale sq,
-                                                          float *part_m, double *part_s)
-{
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
-    const int P = K + 1, R = 2 * K + 1;
-    const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
-    const int b = pr / P, j = pr - b * P;
-    const size_t off = ((size_t)b * P + j) * (size_t)V * BY;
-    const char *re = ex + off, *ra = am + off;
-    const int cbase = c * CHUNK_VECS * E;
-    const bool al = aligned16(re) && aligned16(ra);
-    float xd[NV][E], xa[NV][E];
-    if (al && cbase + CHUNK_VECS * E <= V) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const size_t o = (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY;
-            Elt<DT>::vec(re + o, xd[i]);
-            Elt<DT>::vec(ra + o, xa[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                xd[i][k] = xd[i][k] - xa[i][k];
-    } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e0 = cbase + (i * WG + threadIdx.x) * E;
-            load_elems<DT>(re, al, e0, V, -INFINITY, xd[i]);
-            load_elems<DT>(ra, al, e0, V, -INFINITY, xa[i]);
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                xd[i][k] = (e0 + k < V) ? xd[i][k] - xa[i][k] : -INFINITY;
-        }
-    }
-    float m, s;
-    thread_stats<E>(xd, sp, m, s);
-    const size_t prow = (size_t)b * R + j;
-    block_stats(m, s, sp.c, part_m + prow * nch + c, part_s + prow * nch + c);
-    if (j < K) {  // uniform across the workgroup
-        thread_stats<E>(xa, sq, m, s);
-        const size_t qrow = (size_t)b * R + K + 1 + j;
-        block_stats(m, s, sq.c, part_m + qrow * nch + c, part_s + qrow * nch + c);
-    }
-}
-
-// ------------------------------------------------------------------ K2+K3: accept and scan
+// Sequence b after its rows' statistics: merge the per-wave partials of its 2K+1 rows (fp64),
+// then wave 0 runs the accept tests and the first-rejection scan, one lane per draft
+// position, and records what the residual pass needs.  The draft tokens and their logits
+// are fetched first and the sequence's partials are staged in LDS in one coalesced pass,
+// so the merge waits on memory once.
+constexpr int ACCEPT_STAGE = 4096;  // partials staged in LDS (32 KiB), else read in place
 
 template <int DT, int MODE>
-__global__ __launch_bounds__(64) void k_accept(const char *__restrict__ tgt,
-                                               const char *__restrict__ drf,
-                                               const int32_t *__restrict__ tokens,
-                                               const float *__restrict__ unif, int K, int V,
-                                               int nch, Scale sp, Scale sq,
-                                               const float *__restrict__ part_m,
-                                               const double *__restrict__ part_s, int32_t *acc_len,
-                                               int32_t *out_tokens, float *out_probs, SeqInfo *seq)
+__device__ __forceinline__ void accept_block(const char *tgt, const char *drf, const int32_t *tokens,
+                             const float *unif, int b, int K, int V, int nch, const Scale &sp,
+                             const Scale &sq, const float2 *part, int32_t *acc_len,
+                             int32_t *out_tokens, float *out_probs, SeqInfo *seq)
 {
-    extern __shared__ double smem[];
-    const int R = 2 * K + 1, b = blockIdx.x, lane = threadIdx.x;
-    double *sS = smem;
-    float *sM = reinterpret_cast<float *>(smem + R);
-    for (int r = 0; r < R; ++r) {
-        const size_t base = ((size_t)b * R + r) * nch;
-        float ml = -INFINITY;
-        for (int c = lane; c < nch; c += 64)
-            ml = fmaxf(ml, part_m[base + c]);
-        const float M = wave_max(ml);
+    __shared__ float sM[MAX_ROWS];
+    __shared__ double sS[MAX_ROWS];
+    __shared__ float2 stage[ACCEPT_STAGE];
+    const int R = 2 * K + 1, np = nch * WAVES, total = R * np;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+
+    int32_t x = 0;
+    float lp = 0.0f, lq = 0.0f, u = 0.0f;
+    bool bad = false;
+    if (w == 0 && lane < K) {
+        x = tokens[(size_t)b * K + lane];
+        u = unif[(size_t)b * (K + 1) + lane];
+        bad = (x < 0 || x >= V);
+        if (!bad) {
+            const size_t it = ((size_t)b * (K + 1) + lane) * (size_t)V + x;
+            if (MODE == SAMPLING) {
+                lp = Elt<DT>::one(tgt, it);
+                lq = Elt<DT>::one(drf, ((size_t)b * K + lane) * (size_t)V + x);
+            } else {
+                const float le = Elt<DT>::one(tgt, it), la = Elt<DT>::one(drf, it);
+                lp = le - la;
+                lq = la;
+            }
+        }
+    }
+
+    const float2 *pb = part + (size_t)b * total;
+    const bool staged = total <= ACCEPT_STAGE;
+    if (staged) {
+        for (int i0 = 0; i0 < total; i0 += 4 * WG) {
+            float2 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * WG + t;
+                v[k] = (i < total) ? pb[i] : make_float2(0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * WG + t;
+                if (i < total)
+                    stage[i] = v[k];
+            }
+        }
+        __syncthreads();
+    }
+    for (int r = w; r < R; r += WAVES) {
+        const int r0 = r * np;
         const double cc = (r <= K) ? sp.c : sq.c;
+        float ml = -INFINITY;
+        for (int i = lane; i < np; i += 64)
+            ml = fmaxf(ml, (staged ? stage[r0 + i] : pb[r0 + i]).x);
+        const float M = wave_max(ml);
         double sl = 0.0;
-        for (int c = lane; c < nch; c += 64) {
-            const double s = part_s[base + c];
-            if (s > 0.0)
-                sl += s * exp2(((double)part_m[base + c] - (double)M) * cc);
+        for (int i = lane; i < np; i += 64) {
+            const float2 v = staged ? stage[r0 + i] : pb[r0 + i];
+            if (v.y > 0.0f)
+                sl += (double)v.y * exp2(((double)v.x - (double)M) * cc);
         }
         const double S = wave_sum(sl);
         if (lane == 0) {
@@ -357,9 +359,9 @@ __global__ __launch_bounds__(64) void k_accept(const char *__restrict__ tgt,
         }
     }
     __syncthreads();
+    if (w != 0)
+        return;
 
-    const int32_t x = (lane < K) ? tokens[(size_t)b * K + lane] : 0;
-    const bool bad = (lane < K) && (x < 0 || x >= V);
     int32_t *ot = out_tokens + (size_t)b * (K + 1);
     if (__ballot(bad) != 0) {
         if (lane <= K)
@@ -378,23 +380,13 @@ __global__ __launch_bounds__(64) void k_accept(const char *__restrict__ tgt,
     }
     bool acc = false;
     if (lane < K) {
-        const size_t it = ((size_t)b * (K + 1) + lane) * (size_t)V + x;
-        float lp, lq;
-        if (MODE == SAMPLING) {
-            lp = Elt<DT>::one(tgt, it);
-            lq = Elt<DT>::one(drf, ((size_t)b * K + lane) * (size_t)V + x);
-        } else {
-            const float le = Elt<DT>::one(tgt, it), la = Elt<DT>::one(drf, it);
-            lp = le - la;
-            lq = la;
-        }
         const double P = exp(((double)lp - (double)sM[lane]) * sp.inv_t) / sS[lane];
         const double Q = exp(((double)lq - (double)sM[K + 1 + lane]) * sq.inv_t) / sS[K + 1 + lane];
         if (out_probs) {
             out_probs[((size_t)b * K + lane) * 2] = (float)P;
             out_probs[((size_t)b * K + lane) * 2 + 1] = (float)Q;
         }
-        acc = (P > 0.0) && ((double)unif[(size_t)b * (K + 1) + lane] * Q <= P);
+        acc = (P > 0.0) && ((double)u * Q <= P);
     }
     const unsigned long long am = __ballot(acc);
     const int L = __builtin_ctzll(~am);  // lanes >= K never accept, so L <= K
@@ -407,24 +399,103 @@ __global__ __launch_bounds__(64) void k_accept(const char *__restrict__ tgt,
         SeqInfo si = {};
         si.L = L;
         si.Mp = sM[L];
-        si.inv_sp = 1.0 / sS[L];
+        si.isp = (float)(1.0 / sS[L]);
         if (L < K) {
             si.Mq = sM[K + 1 + L];
-            si.inv_sq = 1.0 / sS[K + 1 + L];
+            si.isq = (float)(1.0 / sS[K + 1 + L]);
         }
         seq[b] = si;
     }
 }
 
-// ------------------------------------------------------------------ K4: residual / bonus draw
+// rows b*(2K+1)+k: k <= K target row (b, k), else draft row (b, k-K-1); each wave stores its
+// (max, sum) partial at part[blockIdx.x * WAVES + wave]
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ tgt,
+                                                       const char *__restrict__ drf, int K, int V,
+                                                       int nch, Scale sc, float2 *part)
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    const int R = 2 * K + 1;
+    const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
+    const int b = row / R, k = row - b * R;
+    const char *rp = (k <= K) ? tgt + ((size_t)b * (K + 1) + k) * (size_t)V * BY
+                              : drf + ((size_t)b * K + (k - K - 1)) * (size_t)V * BY;
+    float x[NV_STATS][E];
+    load_chunk<DT, NV_STATS>(rp, aligned16(rp), c * WG * NV_STATS * E, V, x);
+    float m, s;
+    thread_stats<E, NV_STATS>(x, sc, m, s);
+    store_wave_partials(wave_stats(m, s, sc), part + (size_t)blockIdx.x * WAVES);
+}
+
+// one workgroup per (row pair (b, j), chunk): target values l_e - l_a (fp32), draft values l_a
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
+                                                          const char *__restrict__ am, int K, int V,
+                                                          int nch, Scale sp, Scale sq, float2 *part)
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    const int P = K + 1, R = 2 * K + 1;
+    const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
+    const int b = pr / P, j = pr - b * P;
+    const size_t off = ((size_t)b * P + j) * (size_t)V * BY;
+    const char *re = ex + off, *ra = am + off;
+    const int cbase = c * WG * NV_PAIR * E;
+    const bool al = aligned16(re) && aligned16(ra);
+    float xd[NV_PAIR][E], xa[NV_PAIR][E];
+    load_chunk<DT, NV_PAIR>(re, al, cbase, V, xd);
+    load_chunk<DT, NV_PAIR>(ra, al, cbase, V, xa);
+    if (cbase + WG * NV_PAIR * E <= V) {
+#pragma unroll
+        for (int i = 0; i < NV_PAIR; ++i)
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                xd[i][k] = xd[i][k] - xa[i][k];
+    } else {  // ids past V are -inf on both sides: keep the difference at -inf
+#pragma unroll
+        for (int i = 0; i < NV_PAIR; ++i)
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int id = cbase + (i * WG + threadIdx.x) * E + k;
+                xd[i][k] = (id < V) ? xd[i][k] - xa[i][k] : -INFINITY;
+            }
+    }
+    float m, s;
+    thread_stats<E, NV_PAIR>(xd, sp, m, s);
+    store_wave_partials(wave_stats(m, s, sp), part + (((size_t)b * R + j) * nch + c) * WAVES);
+    if (j < K) {  // uniform across the workgroup
+        thread_stats<E, NV_PAIR>(xa, sq, m, s);
+        __syncthreads();  // the LDS staging of the first store is free again
+        store_wave_partials(wave_stats(m, s, sq),
+                            part + (((size_t)b * R + K + 1 + j) * nch + c) * WAVES);
+    }
+}
+
+// one workgroup per sequence
+template <int DT, int MODE>
+__global__ __launch_bounds__(WG) void k_accept(const char *__restrict__ tgt,
+                                               const char *__restrict__ drf,
+                                               const int32_t *__restrict__ tokens,
+                                               const float *__restrict__ unif, int K, int V,
+                                               int nch, Scale sp, Scale sq,
+                                               const float2 *__restrict__ part, int32_t *acc_len,
+                                               int32_t *out_tokens, float *out_probs, SeqInfo *seq)
+{
+    accept_block<DT, MODE>(tgt, drf, tokens, unif, blockIdx.x, K, V, nch, sp, sq, part, acc_len,
+                           out_tokens, out_probs, seq);
+}
+
+// ------------------------------------------------------------------ residual / bonus draw
 
 // The rows a sequence's draw reads: the target side (sampling: target row L; contrastive:
 // expert and amateur rows L) and, when L < K, the draft side (sampling: draft row L;
 // contrastive: the amateur row again).
 struct DrawRows {
-    const char *p0, *p1, *q;
-    bool resid;
-    bool al;
+    const char *p0;   // target row L (sampling) or expert row L (contrastive)
+    const char *p1;   // draft row L (sampling, L < K only) or amateur row L (contrastive)
+    bool two;         // p1 is read
+    bool resid;       // L < K: w = max(0, p - q); else w = p
+    bool al;          // every row read is 16-byte aligned
 };
 
 template <int DT, int MODE>
@@ -433,238 +504,355 @@ __device__ inline DrawRows draw_rows(const char *tgt, const char *drf, int b, in
     constexpr int BY = Elt<DT>::BYTES;
     DrawRows r;
     r.resid = L < K;
-    const size_t ot = ((size_t)b * (K + 1) + L) * (size_t)V * BY;
+    r.p0 = tgt + ((size_t)b * (K + 1) + L) * (size_t)V * BY;
     if (MODE == SAMPLING) {
-        r.p0 = tgt + ot;
-        r.p1 = nullptr;
-        r.q = r.resid ? drf + ((size_t)b * K + L) * (size_t)V * BY : nullptr;
-        r.al = aligned16(r.p0) && (!r.resid || aligned16(r.q));
+        r.two = r.resid;
+        r.p1 = r.resid ? drf + ((size_t)b * K + L) * (size_t)V * BY : nullptr;
     } else {
-        r.p0 = tgt + ot;
-        r.p1 = drf + ot;
-        r.q = r.p1;
-        r.al = aligned16(r.p0) && aligned16(r.p1);
+        r.two = true;
+        r.p1 = drf + ((size_t)b * (K + 1) + L) * (size_t)V * BY;
     }
+    r.al = aligned16(r.p0) && (!r.two || aligned16(r.p1));
     return r;
 }
 
-// target-side and draft-side values of EPV ids from e0 (ids >= V are never used)
+// Draw weight of one id from its target-side value pv and draft-side value qv (fp32):
+// p = 2^((pv - Mp) log2(e)/T) / S_p; w = max(0, p - q) for a replacement, p for the bonus
+// (or when `target_law` asks for p).  The same instructions run in k_resid and in the
+// search, so both see identical weights.
+__device__ inline float draw_weight(float pv, float qv, bool resid, bool target_law,
+                                    const SeqInfo &si, const Scale &sp, const Scale &sq)
+{
+    const float p = exp2s(pv - si.Mp, sp.hi, sp.lo) * si.isp;
+    if (!resid || target_law)
+        return p;
+    const float q = exp2s(qv - si.Mq, sq.hi, sq.lo) * si.isq;
+    return fmaxf(p - q, 0.0f);
+}
+
+// Weights of the EPV ids from e0 (ids >= V weigh 0), element by element: the path for
+// chunks that touch the end of a row or rows that are not 16-byte aligned.
 template <int DT, int MODE>
-__device__ inline void load_draw(const DrawRows &r, int e0, int V, float (&pv)[Elt<DT>::EPV],
-                                 float (&qv)[Elt<DT>::EPV])
+__device__ inline void vec_weights_masked(const DrawRows &r, int e0, int V, bool target_law,
+                                          const SeqInfo &si, const Scale &sp, const Scale &sq,
+                                          float (&wv)[Elt<DT>::EPV])
 {
     constexpr int E = Elt<DT>::EPV;
-    if (MODE == SAMPLING) {
-        load_elems<DT>(r.p0, r.al, e0, V, 0.0f, pv);
-        if (r.resid)
-            load_elems<DT>(r.q, r.al, e0, V, 0.0f, qv);
-    } else {
-        load_elems<DT>(r.p0, r.al, e0, V, 0.0f, pv);
+    float pv[E], qv[E];
+    load_elems<DT>(r.p0, r.al, e0, V, 0.0f, pv);
+    if (r.two)
         load_elems<DT>(r.p1, r.al, e0, V, 0.0f, qv);
 #pragma unroll
-        for (int k = 0; k < E; ++k)
+    for (int k = 0; k < E; ++k) {
+        if (MODE == CONTRASTIVE)
             pv[k] = pv[k] - qv[k];
+        wv[k] = (e0 + k < V) ? draw_weight(pv[k], qv[k], r.resid, target_law, si, sp, sq) : 0.0f;
     }
 }
 
-// Draw weights of one id: p = target probability; w = max(0, p - q) when drawing the
-// replacement (L < K), w = p for the bonus draw.  Identical in k_resid_chunks and k_draw.
-__device__ inline void draw_weight(float pv, float qv, bool resid, const SeqInfo &si,
-                                   const Scale &sp, const Scale &sq, double &w, double &p)
-{
-    p = (double)exp2s(pv - si.Mp, sp.hi, sp.lo) * si.inv_sp;
-    if (resid) {
-        const double q = (double)exp2s(qv - si.Mq, sq.hi, sq.lo) * si.inv_sq;
-        const double d = p - q;
-        w = d > 0.0 ? d : 0.0;
-    } else {
-        w = p;
-    }
-}
-
+// Weights of one whole 16-byte vector from its raw words.
 template <int DT, int MODE>
-__global__ __launch_bounds__(WG) void k_resid_chunks(const char *__restrict__ tgt,
-                                                     const char *__restrict__ drf, int K, int V,
-                                                     int nch, Scale sp, Scale sq,
-                                                     const SeqInfo *__restrict__ seq,
-                                                     double *resid)
+__device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint4 &q,
+                                   bool target_law, const SeqInfo &si, const Scale &sp,
+                                   const Scale &sq, float (&wv)[Elt<DT>::EPV])
 {
     constexpr int E = Elt<DT>::EPV;
-    const int b = blockIdx.x / nch, c = blockIdx.x - b * nch;
-    const SeqInfo si = seq[b];
-    double ws = 0.0, ps = 0.0;
-    if (si.L >= 0) {
-        const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
-        const int cbase = c * CHUNK_VECS * E;
-        for (int i = 0; i < NV; ++i) {
-            const int e0 = cbase + (i * WG + threadIdx.x) * E;
-            if (e0 >= V)
-                break;
-            float pv[E], qv[E];
-            load_draw<DT, MODE>(r, e0, V, pv, qv);
+    float pv[E], qv[E];
+    Elt<DT>::unpack(a, pv);
+    if (r.two)
+        Elt<DT>::unpack(q, qv);
 #pragma unroll
-            for (int k = 0; k < E; ++k) {
-                if (e0 + k < V) {
-                    double w, p;
-                    draw_weight(pv[k], qv[k], r.resid, si, sp, sq, w, p);
-                    ws += w;
-                    ps += p;
-                }
-            }
-        }
+    for (int k = 0; k < E; ++k) {
+        if (MODE == CONTRASTIVE)
+            pv[k] = pv[k] - qv[k];
+        wv[k] = draw_weight(pv[k], qv[k], r.resid, target_law, si, sp, sq);
     }
-    block_sum2(ws, ps, resid + ((size_t)b * nch + c) * 2, resid + ((size_t)b * nch + c) * 2 + 1);
 }
 
+// NV_RESID vectors of this thread from ids e0(i) = base + i * WG * E (the coalesced pattern
+// of one chunk), both rows, all loads issued before any arithmetic.  Returns false (nothing
+// loaded) when some vector is not whole or the rows are not aligned; the caller then takes
+// the element path.
+template <int DT, bool NT>
+__device__ inline bool load_draw_vectors(const DrawRows &r, int base, int V,
+                                         uint4 (&a)[NV_RESID], uint4 (&q)[NV_RESID])
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = WG * Elt<DT>::EPV;
+    if (!r.al || base + (NV_RESID - 1) * STRIDE + E > V)
+        return false;
+#pragma unroll
+    for (int i = 0; i < NV_RESID; ++i) {
+        const size_t o = (size_t)(base + i * STRIDE) * BY;
+        a[i] = NT ? load_stream(r.p0 + o) : load_plain(r.p0 + o);
+    }
+    if (r.two)
+#pragma unroll
+        for (int i = 0; i < NV_RESID; ++i) {
+            const size_t o = (size_t)(base + i * STRIDE) * BY;
+            q[i] = NT ? load_stream(r.p1 + o) : load_plain(r.p1 + o);
+        }
+    return true;
+}
+
+// This thread's draw-weight sums over chunk c, one per vector i (fp32 tree over the
+// vector's ids); vector i covers ids c*CE + (i*WG + t)*E + [0, E).  The same instructions
+// run in k_resid (which sums them) and in k_draw (which searches them), so both see the
+// same weights.
+template <int DT, int MODE, bool NT>
+__device__ inline void thread_vector_weights(const DrawRows &r, int c, int V, bool target_law,
+                                             const SeqInfo &si, const Scale &sp, const Scale &sq,
+                                             float (&vs)[NV_RESID], uint4 (&a)[NV_RESID],
+                                             uint4 (&q)[NV_RESID], bool &whole)
+{
+    constexpr int E = Elt<DT>::EPV;
+    const int base = c * WG * NV_RESID * E + threadIdx.x * E;
+    whole = load_draw_vectors<DT, NT>(r, base, V, a, q);
+#pragma unroll
+    for (int i = 0; i < NV_RESID; ++i) {
+        const int e0 = base + i * WG * E;
+        float wv[E];
+        if (whole) {
+            raw_weights<DT, MODE>(r, a[i], q[i], target_law, si, sp, sq, wv);
+            vs[i] = tree_sum<E>(wv);
+        } else if (e0 < V) {
+            vec_weights_masked<DT, MODE>(r, e0, V, target_law, si, sp, sq, wv);
+            vs[i] = tree_sum<E>(wv);
+        } else {
+            vs[i] = 0.0f;
+        }
+    }
+}
+
+// Per chunk c of row L, the totals of its NV_RESID vector rows: unit (c, i) covers the
+// contiguous ids c*CE + i*WG*E + [0, WG*E) and its weight sum goes to
+// resid[(b * nch + c) * NV_RESID + i] (per-thread fp32 vector sums, fp64 above them).
+template <int DT, int MODE>
+__global__ __launch_bounds__(WG) void k_resid(const char *__restrict__ tgt,
+                                              const char *__restrict__ drf, int K, int V, int nch,
+                                              Scale sp, Scale sq, const SeqInfo *__restrict__ seq,
+                                              double *resid)
+{
+    __shared__ double s_units[NV_RESID][WAVES];
+    const int b = blockIdx.x / nch, c = blockIdx.x - b * nch;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const SeqInfo si = seq[b];
+    if (si.L < 0)
+        return;
+    const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
+    float vs[NV_RESID];
+    uint4 a[NV_RESID], q[NV_RESID];
+    bool whole;
+    thread_vector_weights<DT, MODE, true>(r, c, V, false, si, sp, sq, vs, a, q, whole);
+#pragma unroll
+    for (int i = 0; i < NV_RESID; ++i) {
+        const double us = wave_sum((double)vs[i]);
+        if (lane == 0)
+            s_units[i][w] = us;
+    }
+    __syncthreads();
+    if (threadIdx.x < NV_RESID) {
+        const int i = threadIdx.x;
+        resid[(size_t)blockIdx.x * NV_RESID + i] =
+            ((s_units[i][0] + s_units[i][1]) + s_units[i][2]) + s_units[i][3];
+    }
+}
+
+// Among `nu` units with totals unit(u) (ascending ids), wave 0 finds the first unit whose
+// running total exceeds tt = u01 * W (W = the sum of all units, fixed order), or if rounding
+// leaves t at or past the last one, the last unit of positive weight (*fb = 1).  Returns the
+// unit (or -1 when every unit weighs 0) and writes its starting weight *base and tt.
+template <typename F>
+__device__ inline int find_unit(F unit, int nu, float u01, double *base, double *tt, int *fb)
+{
+    const int lane = threadIdx.x & 63;
+    double W = 0.0;
+    for (int s0 = 0; s0 < nu; s0 += 64)
+        W += wave_sum((s0 + lane < nu) ? unit(s0 + lane) : 0.0);
+    *tt = (double)u01 * W;
+    double run = 0.0, found_base = 0.0, last_base = 0.0;
+    int us = -1, last = -1;
+    for (int s0 = 0; s0 < nu && us < 0; s0 += 64) {
+        const double wu = (s0 + lane < nu) ? unit(s0 + lane) : 0.0;
+        const double inc = wave_incl_scan(wu, lane);
+        double exc = __shfl_up(inc, 1);
+        if (lane == 0)
+            exc = 0.0;
+        const unsigned long long hit = __ballot(W > 0.0 && wu > 0.0 && run + inc > *tt);
+        const unsigned long long pos = __ballot(wu > 0.0);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            us = s0 + l;
+            found_base = run + __shfl(exc, l);
+        } else if (pos) {
+            const int l = 63 - __builtin_clzll(pos);
+            last = s0 + l;
+            last_base = run + __shfl(exc, l);
+        }
+        run += __shfl(inc, 63);
+    }
+    *fb = (us < 0);
+    *base = (us >= 0) ? found_base : last_base;
+    return (us >= 0) ? us : last;
+}
+
+// Inside unit (c, i): thread t weighs vector i*WG + t of chunk c (the same instructions as
+// k_resid), a block scan of the vector sums finds the vector, and its owner emits the first
+// id whose running weight exceeds tt (fb: the last id of positive weight).
+template <int DT, int MODE>
+__device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si, int V, int unit,
+                                            double base, double tt, bool fb, bool target_law,
+                                            const Scale &sp, const Scale &sq, int32_t *out)
+{
+    constexpr int E = Elt<DT>::EPV;
+    __shared__ int s_first, s_last;
+    const int t = threadIdx.x;
+    const int c = unit / NV_RESID, i = unit - c * NV_RESID;
+    const int e0 = c * WG * NV_RESID * E + (i * WG + t) * E;
+    float wv[E];
+    if (e0 < V) {
+        vec_weights_masked<DT, MODE>(r, e0, V, target_law, si, sp, sq, wv);
+    } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            wv[k] = 0.0f;
+    }
+    const float vsum = tree_sum<E>(wv);
+    if (t == 0) {
+        s_first = WG;
+        s_last = -1;
+    }
+    const double bt = base + block_exclusive_scan((double)vsum);  // has a barrier
+    if (!fb && vsum > 0.0f && bt + (double)vsum > tt)
+        atomicMin(&s_first, t);
+    if (vsum > 0.0f)
+        atomicMax(&s_last, t);
+    __syncthreads();
+    const bool fb2 = fb || s_first == WG;
+    if (t != (fb2 ? s_last : s_first))
+        return;
+    double run = bt;
+    int y = -1, lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        if (wv[k] > 0.0f) {
+            run += (double)wv[k];
+            lastpos = e0 + k;
+            if (!fb2 && y < 0 && run > tt)
+                y = e0 + k;
+        }
+    }
+    // rounding may put t past this vector's ids: then its last id of positive weight
+    *out = (y >= 0) ? y : lastpos;
+}
+
+// One workgroup per sequence: the unit holding t = u_K * W (from k_resid's unit totals),
+// then the id inside it.  If rounding left the residual empty, draw from the target law p_L
+// instead: its unit totals are computed here (essentially never taken).
 template <int DT, int MODE>
 __global__ __launch_bounds__(WG) void k_draw(const char *__restrict__ tgt,
                                              const char *__restrict__ drf,
                                              const float *__restrict__ unif, int K, int V, int nch,
                                              Scale sp, Scale sq, const SeqInfo *__restrict__ seq,
-                                             const double *__restrict__ resid, int32_t *out_tokens)
+                                             const double *__restrict__ resid,
+                                             int32_t *out_tokens)
 {
-    constexpr int E = Elt<DT>::EPV;
-    const int b = blockIdx.x, t = threadIdx.x;
+    __shared__ int s_unit, s_fb;
+    __shared__ double s_base, s_t;
+    __shared__ double s_units[NV_RESID][WAVES];
+    const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int nu = nch * NV_RESID;
+    const double *ub = resid + (size_t)b * nu;
     const SeqInfo si = seq[b];
     if (si.L < 0)
-        return;  // uniform: the whole workgroup leaves
-    __shared__ int s_chunk, s_which, s_fb, s_first, s_last;
-    __shared__ double s_base, s_t;
-    if (t == 0) {
-        const double *rb = resid + (size_t)b * nch * 2;
-        double W = 0.0;
-        for (int c = 0; c < nch; ++c)
-            W += rb[2 * c];
-        const int which = (W > 0.0) ? 0 : 1;  // 1: residual empty by rounding, use p_L
-        double tot = W;
-        if (which) {
-            tot = 0.0;
-            for (int c = 0; c < nch; ++c)
-                tot += rb[2 * c + 1];
-        }
-        const double tt = (double)unif[(size_t)b * (K + 1) + K] * tot;
-        double acc = 0.0, acc_last = 0.0;
-        int cs = -1, last = -1;
-        for (int c = 0; c < nch; ++c) {
-            const double wc = rb[2 * c + which];
-            if (wc > 0.0) {
-                if (acc + wc > tt) {
-                    cs = c;
-                    break;
-                }
-                last = c;
-                acc_last = acc;
-            }
-            acc += wc;
-        }
-        int fb = 0;
-        if (cs < 0) {  // t at or beyond the rounded total: the last id of positive weight
-            cs = last;
-            acc = acc_last;
-            fb = 1;
-        }
-        s_chunk = cs;
-        s_which = which;
-        s_fb = fb;
-        s_base = acc;
-        s_t = tt;
-        s_first = WG;
-        s_last = -1;
-    }
-    __syncthreads();
-    const int cs = s_chunk;
-    if (cs < 0)
-        return;  // no weight anywhere: outside the contract (a row without finite logits)
-    const int which = s_which;
+        return;
+    const float u01 = unif[(size_t)b * (K + 1) + K];
+    int32_t *out = out_tokens + (size_t)b * (K + 1) + si.L;
     const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
-    const int e_begin = cs * CHUNK_VECS * E + t * NV * E;  // this thread's contiguous ids
-
-    double T = 0.0;
-    for (int i = 0; i < NV; ++i) {
-        const int e0 = e_begin + i * E;
-        if (e0 >= V)
-            break;
-        float pv[E], qv[E];
-        load_draw<DT, MODE>(r, e0, V, pv, qv);
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            if (e0 + k < V) {
-                double w, p;
-                draw_weight(pv[k], qv[k], r.resid, si, sp, sq, w, p);
-                T += which ? p : w;
-            }
+    if (t < 64) {
+        double base, tt;
+        int fb;
+        const int us = find_unit([&](int k) { return ub[k]; }, nu, u01, &base, &tt, &fb);
+        if (lane == 0) {
+            s_unit = us;
+            s_base = base;
+            s_t = tt;
+            s_fb = fb;
         }
     }
-    const double base = s_base + block_exclusive_scan(T);
-    const bool pred = !s_fb && (T > 0.0) && (base + T > s_t);
-    if (pred)
-        atomicMin(&s_first, t);
-    if (T > 0.0)
-        atomicMax(&s_last, t);
     __syncthreads();
-    const bool fb = (s_first == WG);
-    const int owner = fb ? s_last : s_first;
-    if (t == owner) {
-        // Re-walk this thread's ids with the same arithmetic as T: the running sum reaches T
-        // exactly, so the predicate that chose this thread holds at one of its ids.  In the
-        // fallback case keep the last id of positive weight.
-        double run = 0.0;
-        int y = -1;
-        bool done = false;
-        for (int i = 0; i < NV && !done; ++i) {
-            const int e0 = e_begin + i * E;
-            if (e0 >= V)
-                break;
-            float pv[E], qv[E];
-            load_draw<DT, MODE>(r, e0, V, pv, qv);
-            for (int k = 0; k < E; ++k) {
-                if (e0 + k >= V)
-                    break;
-                double w, p;
-                draw_weight(pv[k], qv[k], r.resid, si, sp, sq, w, p);
-                const double wv = which ? p : w;
-                run += wv;
-                if (wv > 0.0) {
-                    y = e0 + k;
-                    if (!fb && base + run > s_t) {
-                        done = true;
-                        break;
+    bool target_law = false;
+    if (s_unit < 0) {
+        // The residual is empty by rounding: draw from the target law p_L.  Its unit totals
+        // are computed here chunk by chunk, twice (the total, then the scan), in LDS only.
+        target_law = true;
+        double run = 0.0, tt = 0.0, last_base = 0.0;
+        int found = -1, last = -1;
+        for (int pass = 0; pass < 2 && found < 0; ++pass) {
+            run = 0.0;
+            for (int c = 0; c < nch && found < 0; ++c) {
+                float vs[NV_RESID];
+                uint4 a[NV_RESID], q[NV_RESID];
+                bool whole;
+                thread_vector_weights<DT, MODE, false>(r, c, V, true, si, sp, sq, vs, a, q, whole);
+                __syncthreads();  // s_units of the previous chunk have been read
+#pragma unroll
+                for (int i = 0; i < NV_RESID; ++i) {
+                    const double v = wave_sum((double)vs[i]);
+                    if (lane == 0)
+                        s_units[i][w] = v;
+                }
+                __syncthreads();
+                for (int i = 0; i < NV_RESID && found < 0; ++i) {  // every thread, same order
+                    const double ui =
+                        ((s_units[i][0] + s_units[i][1]) + s_units[i][2]) + s_units[i][3];
+                    if (pass == 1 && ui > 0.0) {
+                        if (run + ui > tt) {
+                            found = c * NV_RESID + i;
+                        } else {
+                            last = c * NV_RESID + i;
+                            last_base = run;
+                        }
                     }
+                    if (found < 0)
+                        run += ui;
                 }
             }
+            if (pass == 0)
+                tt = (double)u01 * run;
         }
-        out_tokens[(size_t)b * (K + 1) + si.L] = y;
+        const int us = (found >= 0) ? found : last;
+        if (us < 0) {
+            if (t == 0)
+                *out = -1;  // a row without finite logits: outside the contract
+            return;
+        }
+        search_unit<DT, MODE>(r, si, V, us, (found >= 0) ? run : last_base, tt, found < 0, true,
+                              sp, sq, out);
+        return;
     }
+    search_unit<DT, MODE>(r, si, V, s_unit, s_base, s_t, s_fb != 0, false, sp, sq, out);
 }
 
-// ------------------------------------------------------------------ K5: greedy blockwise
+// ------------------------------------------------------------------ greedy blockwise
 
+// per chunk of a row: (max, first id of the max) per wave
 template <int DT>
 __global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int V, int nch,
-                                               float *part_v, int *part_i)
+                                               float2 *part)
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
     const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
     const char *rp = tgt + (size_t)row * (size_t)V * BY;
-    const int cbase = c * CHUNK_VECS * E;
-    const bool al = aligned16(rp);
-    float x[NV][E];
-    if (al && cbase + CHUNK_VECS * E <= V) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            Elt<DT>::vec(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY, x[i]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            load_elems<DT>(rp, al, cbase + (i * WG + threadIdx.x) * E, V, -INFINITY, x[i]);
-    }
+    const int cbase = c * WG * NV_ARGMAX * E;
+    float x[NV_ARGMAX][E];
+    load_chunk<DT, NV_ARGMAX>(rp, aligned16(rp), cbase, V, x);
     // this thread's ids ascend with (i, k); start from its first id so that an all -inf
     // run still reports the lowest id
     const int first = cbase + threadIdx.x * E;
     float bv = -INFINITY;
     int bi = (first < V) ? first : INT_MAX;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV_ARGMAX; ++i)
 #pragma unroll
         for (int k = 0; k < E; ++k)
             if (x[i][k] > bv) {
@@ -672,45 +860,35 @@ __global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int
                 bi = cbase + (i * WG + threadIdx.x) * E + k;
             }
     wave_argmax(bv, bi);
-    __shared__ float sv[WG / 64];
-    __shared__ int si[WG / 64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) {
-        sv[w] = bv;
-        si[w] = bi;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float v = sv[0];
-        int id = si[0];
-        for (int k = 1; k < WG / 64; ++k)
-            take_better(v, id, sv[k], si[k]);
-        part_v[blockIdx.x] = v;
-        part_i[blockIdx.x] = id;
-    }
+    store_wave_partials(make_float2(bv, __int_as_float(bi)), part + (size_t)blockIdx.x * WAVES);
 }
 
-__global__ __launch_bounds__(64) void k_greedy_final(const int32_t *__restrict__ props, int K,
+// one workgroup per sequence: row argmaxes g_j, then the longest matching prefix
+__global__ __launch_bounds__(WG) void k_greedy_final(const int32_t *__restrict__ props, int K,
                                                      int V, int nch,
-                                                     const float *__restrict__ part_v,
-                                                     const int *__restrict__ part_i,
+                                                     const float2 *__restrict__ part,
                                                      int32_t *acc_len, int32_t *out_tokens)
 {
-    extern __shared__ int sg[];
-    const int b = blockIdx.x, lane = threadIdx.x;
-    for (int j = 0; j <= K; ++j) {
-        const size_t base = ((size_t)b * (K + 1) + j) * nch;
+    __shared__ int sg[64];
+    const int b = blockIdx.x, P = K + 1;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, np = nch * WAVES;
+    for (int j = w; j < P; j += WAVES) {
+        const float2 *pr = part + ((size_t)b * P + j) * np;
         float v = -INFINITY;
         int id = INT_MAX;
-        for (int c = lane; c < nch; c += 64)
-            take_better(v, id, part_v[base + c], part_i[base + c]);
+        for (int i = lane; i < np; i += 64) {
+            const float2 e = pr[i];
+            take_better(v, id, e.x, __float_as_int(e.y));
+        }
         wave_argmax(v, id);
         if (lane == 0)
             sg[j] = id;
     }
     __syncthreads();
-    const int32_t x = (lane < K) ? props[(size_t)b * K + lane] : 0;
-    const bool bad = (lane < K) && (x < 0 || x >= V);
+    if (w != 0)
+        return;
+    const int32_t xp = (lane < K) ? props[(size_t)b * K + lane] : 0;
+    const bool bad = (lane < K) && (xp < 0 || xp >= V);
     int32_t *ot = out_tokens + (size_t)b * (K + 1);
     if (__ballot(bad) != 0) {
         if (lane <= K)
@@ -719,7 +897,7 @@ __global__ __launch_bounds__(64) void k_greedy_final(const int32_t *__restrict__
             acc_len[b] = -1;
         return;
     }
-    const unsigned long long mm = __ballot(lane < K && x != sg[lane]);
+    const unsigned long long mm = __ballot(lane < K && xp != sg[lane]);
     const int L = mm ? __builtin_ctzll(mm) : K;
     if (lane <= K)
         ot[lane] = (lane <= L) ? sg[lane] : -1;
@@ -737,12 +915,12 @@ struct Timer {
     Timer(const Launch &l, int k) : ln(l), kind(k)
     {
         if (ln.ev)
-            hipEventRecord(ln.ev[2 * kind], ln.stream);
+            (void)hipEventRecord(ln.ev[2 * kind], ln.stream);
     }
     ~Timer()
     {
         if (ln.ev)
-            hipEventRecord(ln.ev[2 * kind + 1], ln.stream);
+            (void)hipEventRecord(ln.ev[2 * kind + 1], ln.stream);
     }
 };
 
@@ -752,37 +930,36 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
                          const int32_t *tokens, const float *unif, int32_t *acc_len,
                          int32_t *out_tokens, float *out_probs)
 {
-    const int nch = num_chunks(DT, V);
     const char *t = static_cast<const char *>(tgt);
     const char *d = static_cast<const char *>(drf);
+    const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
     {
-        Timer tm(ln, 0);
+        Timer tm(ln, KIND_STATS);
         if (MODE == SAMPLING) {
             const unsigned grid = (unsigned)((size_t)B * (2 * K + 1) * nch);
             hipLaunchKernelGGL(k_stats_sampling<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
-                               V, nch, sp, ws.part_m, ws.part_s);
+                               V, nch, sp, ws.part);
         } else {
             const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
             hipLaunchKernelGGL(k_stats_contrastive<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d,
-                               K, V, nch, sp, sq, ws.part_m, ws.part_s);
+                               K, V, nch, sp, sq, ws.part);
         }
     }
     {
-        Timer tm(ln, 1);
-        const size_t lds = (size_t)(2 * K + 1) * (sizeof(double) + sizeof(float));
-        hipLaunchKernelGGL((k_accept<DT, MODE>), dim3(B), dim3(64), lds, ln.stream, t, d, tokens,
-                           unif, K, V, nch, sp, sq, ws.part_m, ws.part_s, acc_len, out_tokens,
-                           out_probs, ws.seq);
+        Timer tm(ln, KIND_ACCEPT);
+        hipLaunchKernelGGL((k_accept<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, tokens,
+                           unif, K, V, nch, sp, sq, ws.part, acc_len, out_tokens, out_probs, ws.seq);
+    }
+    const int ncr = num_chunks(NV_RESID, DT, V);
+    {
+        Timer tm(ln, KIND_RESID);
+        hipLaunchKernelGGL((k_resid<DT, MODE>), dim3((unsigned)((size_t)B * ncr)), dim3(WG), 0,
+                           ln.stream, t, d, K, V, ncr, sp, sq, ws.seq, ws.resid);
     }
     {
-        Timer tm(ln, 2);
-        hipLaunchKernelGGL((k_resid_chunks<DT, MODE>), dim3((unsigned)((size_t)B * nch)), dim3(WG),
-                           0, ln.stream, t, d, K, V, nch, sp, sq, ws.seq, ws.resid);
-    }
-    {
-        Timer tm(ln, 3);
+        Timer tm(ln, KIND_DRAW);
         hipLaunchKernelGGL((k_draw<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, unif, K, V,
-                           nch, sp, sq, ws.seq, ws.resid, out_tokens);
+                           ncr, sp, sq, ws.seq, ws.resid, out_tokens);
     }
     return hipGetLastError();
 }
@@ -791,17 +968,17 @@ template <int DT>
 hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int V, const void *tgt,
                        const int32_t *props, int32_t *acc_len, int32_t *out_tokens)
 {
-    const int nch = num_chunks(DT, V);
+    const int nch = num_chunks(NV_ARGMAX, DT, V);
     {
-        Timer tm(ln, 4);
+        Timer tm(ln, KIND_ARGMAX);
         const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
         hipLaunchKernelGGL(k_argmax<DT>, dim3(grid), dim3(WG), 0, ln.stream,
-                           static_cast<const char *>(tgt), V, nch, ws.part_m, ws.part_i);
+                           static_cast<const char *>(tgt), V, nch, ws.part);
     }
     {
-        Timer tm(ln, 5);
-        hipLaunchKernelGGL(k_greedy_final, dim3(B), dim3(64), (size_t)(K + 1) * sizeof(int),
-                           ln.stream, props, K, V, nch, ws.part_m, ws.part_i, acc_len, out_tokens);
+        Timer tm(ln, KIND_GREEDY_EMIT);
+        hipLaunchKernelGGL(k_greedy_final, dim3(B), dim3(WG), 0, ln.stream, props, K, V, nch,
+                           ws.part, acc_len, out_tokens);
     }
     return hipGetLastError();
 }

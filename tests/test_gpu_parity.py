@@ -256,5 +256,7 @@ def test_profile_api(ctx):
     for _ in range(3):
         run(ctx, w)
     ms, n = sv.specverify_profile_end(ctx)
-    assert n["row_stats"] == 3 and n["draw"] == 3 and n["row_argmax"] == 0
+    assert n["row_stats"] == 3 and n["accept_scan"] == 3 and n["residual_sums"] == 3
+    assert n["draw"] == 3
+    assert n["row_argmax"] == 0 and n["greedy_emit"] == 0
     assert all(v >= 0 for v in ms.values()) and ms["row_stats"] > 0
