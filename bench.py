@@ -4,7 +4,7 @@
 Workload: B=256 sequences, K=8 draft tokens, V=128256, bfloat16 logits, T=0.7 (target
 ~N(0,4^2) plus +8 at 20 distinct ids per row, draft = target + N(0,1.5^2)), seeded and
 synthetic.  One step = one specverify_run_sampling call over the whole batch (row
-statistics, accept + first-reject scan, residual chunk sums, draw).  Inputs sit in HBM
+statistics, then accept + first-reject scan + residual/bonus draw).  Inputs sit in HBM
 before timing starts and alternate between two copies so that no step reads logits the
 previous one left in the 256 MB last-level cache.
 
@@ -48,9 +48,10 @@ def measured_traffic():
         return None
     vals = {}
     for line in open(TRAFFIC_FILE):
-        if ":" in line and line.strip().startswith(("traffic_bytes_per_launch", "kernel_source_sha256")):
+        line = line.strip().lstrip("-* ")
+        if ":" in line and line.startswith(("traffic_bytes_per_launch", "kernel_source_sha256")):
             k, v = line.split(":", 1)
-            vals[k.strip().strip("-* `")] = v.strip().strip("` ")
+            vals[k.strip().strip("`")] = v.strip().strip("` ")
     if vals.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
@@ -128,7 +129,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
-    sv.specverify_profile_begin(ctx, args.steps)
+    # HIP events around the row-statistics kernel only, on the call's stream
+    sv.specverify_profile_begin(ctx, args.steps, ["row_stats"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -137,6 +139,13 @@ def main():
     t1 = time.perf_counter()
     kms, kn = sv.specverify_profile_end(ctx)
     mean_L = float(acc.float().mean().item())
+    # per-kernel breakdown from a separate, untimed pass with events around every kernel
+    nb = min(args.steps, 20)
+    sv.specverify_profile_begin(ctx, nb)
+    for i in range(nb):
+        step(i)
+    torch.cuda.synchronize()
+    bms, bn = sv.specverify_profile_end(ctx)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -174,7 +183,7 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel": "k_stats_sampling<bf16>", "algorithmic_bytes": logit_bytes,
                      "avg_ms": stats_ms},
-        "kernels_ms_per_step": {k: kms[k] / max(kn[k], 1) for k in kms if kn[k]},
+        "kernels_ms_per_step": {k: bms[k] / bn[k] for k in bms if bn[k]},
         "mean_accepted_len": mean_L,
     }
     if args.cpu_seconds > 0:

@@ -63,12 +63,15 @@ enum specverify_status {
 /* Largest K a context accepts (one wave64 lane per draft position). */
 #define SPECVERIFY_MAX_K 63
 
+/* Largest vocabulary a context accepts (the draw keeps its per-slice weight sums on chip). */
+#define SPECVERIFY_MAX_VOCAB (1 << 20)
+
 /*
  * Create a context on HIP device `device` for calls with B <= max_batch, K <= max_k and
  * V <= max_vocab, allocating its device workspace there (a few MB for the largest
  * vocabularies; see specverify_workspace_bytes).  On success *out receives the context.
- * Errors: EINVAL (out NULL, sizes < 1, max_k > SPECVERIFY_MAX_K), EHIP (bad device),
- * ENOMEM (allocation failed).
+ * Errors: EINVAL (out NULL, sizes < 1, max_k > SPECVERIFY_MAX_K,
+ * max_vocab > SPECVERIFY_MAX_VOCAB), EHIP (bad device), ENOMEM (allocation failed).
  */
 int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab);
 
@@ -131,18 +134,19 @@ const char *specverify_strerror(int status);
 
 /*
  * Kernel timing.  Kernel kinds:
- *   0 row statistics (sampling, contrastive), 1 accept test and first-rejection scan,
- *   2 residual / bonus weight sums, 3 inverse-CDF draw, 4 row argmax (greedy),
- *   5 proposal compare and emit (greedy).
- * specverify_profile_begin(ctx, max_calls) creates hipEvent pairs for up to max_calls
- * subsequent run_* calls and records one pair around every kernel they launch, on the
- * call's stream.  specverify_profile_end(ctx, ms, launches) synchronises on the recorded
- * events, writes the summed milliseconds and launch counts per kind into the two
- * SPECVERIFY_NUM_KERNELS-long arrays (either may be NULL), and releases the events.
- * Errors: EINVAL (NULL ctx, max_calls < 1, end without begin), EHIP.
+ *   0 row statistics (sampling, contrastive), 1 accept scan and draw (sampling,
+ *   contrastive), 2 row argmax (greedy), 3 proposal compare and emit (greedy).
+ * specverify_profile_begin(ctx, max_calls, kinds) creates hipEvent pairs for up to
+ * max_calls subsequent run_* calls and records one pair around every kernel they launch
+ * whose kind k has bit (1 << k) set in `kinds` (0 = every kind), on the call's stream.
+ * specverify_profile_end(ctx, ms, launches) synchronises on the recorded events, writes the
+ * summed milliseconds and launch counts per kind into the two SPECVERIFY_NUM_KERNELS-long
+ * arrays (either may be NULL), and releases the events.
+ * Errors: EINVAL (NULL ctx, max_calls < 1, unknown kind bits, begin twice, end without
+ * begin), EHIP.
  */
-#define SPECVERIFY_NUM_KERNELS 6
-int specverify_profile_begin(specverify_ctx *ctx, int max_calls);
+#define SPECVERIFY_NUM_KERNELS 4
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds);
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
 
 #ifdef __cplusplus

@@ -25,9 +25,9 @@ SPECVERIFY_EHIP = -4
 SPECVERIFY_ECAPACITY = -5
 
 SPECVERIFY_MAX_K = 63
-SPECVERIFY_NUM_KERNELS = 6
-KERNEL_NAMES = ("row_stats", "accept_scan", "residual_sums", "draw", "row_argmax",
-                "greedy_emit")
+SPECVERIFY_MAX_VOCAB = 1 << 20
+SPECVERIFY_NUM_KERNELS = 4
+KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit")
 
 _lib = None
 _lock = threading.Lock()
@@ -68,7 +68,7 @@ def load():
         lib.specverify_destroy.restype = i
         lib.specverify_strerror.argtypes = [i]
         lib.specverify_strerror.restype = ctypes.c_char_p
-        lib.specverify_profile_begin.argtypes = [vp, i]
+        lib.specverify_profile_begin.argtypes = [vp, i, ctypes.c_uint]
         lib.specverify_profile_begin.restype = i
         lib.specverify_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                                ctypes.POINTER(ctypes.c_int)]
@@ -150,8 +150,12 @@ def specverify_destroy(ctx) -> None:
     _check(load().specverify_destroy(ctx), "specverify_destroy")
 
 
-def specverify_profile_begin(ctx, max_calls: int) -> None:
-    _check(load().specverify_profile_begin(ctx, max_calls), "specverify_profile_begin")
+def specverify_profile_begin(ctx, max_calls: int, kinds=None) -> None:
+    """kinds: kernel names (from KERNEL_NAMES) to time, or None for all of them."""
+    mask = 0
+    for k in kinds or ():
+        mask |= 1 << KERNEL_NAMES.index(k)
+    _check(load().specverify_profile_begin(ctx, max_calls, mask), "specverify_profile_begin")
 
 
 def specverify_profile_end(ctx):

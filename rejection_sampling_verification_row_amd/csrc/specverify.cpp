@@ -20,6 +20,7 @@ struct specverify_ctx {
     // timing
     bool prof;
     int prof_cap, prof_calls;
+    unsigned prof_mask;                   // kernel kinds to time
     std::vector<hipEvent_t> events;       // prof_cap * 2 * SPECVERIFY_NUM_KERNELS
     std::vector<unsigned> launched;       // per recorded call: bit k = kernel kind k ran
 };
@@ -78,7 +79,7 @@ hipEvent_t *next_events(specverify_ctx *ctx)
 void note_call(specverify_ctx *ctx, hipEvent_t *ev, unsigned kinds)
 {
     if (ev) {
-        ctx->launched[ctx->prof_calls] = kinds;
+        ctx->launched[ctx->prof_calls] = kinds & ctx->prof_mask;
         ctx->prof_calls++;
     }
 }
@@ -109,11 +110,10 @@ int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, in
     const sv::Scale sp = sv::make_scale((double)temperature);
     const sv::Scale sq = (mode == sv::CONTRASTIVE) ? sv::make_scale(1.0) : sp;
     hipEvent_t *ev = next_events(ctx);
-    sv::Launch ln{static_cast<hipStream_t>(stream), ev};
+    sv::Launch ln{static_cast<hipStream_t>(stream), ev, ctx->prof_mask};
     hipError_t e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
                                        unif, acc_len, out_tokens, out_probs);
-    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_ACCEPT) | (1u << sv::KIND_RESID) |
-                           (1u << sv::KIND_DRAW));
+    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_TAIL));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 
@@ -123,7 +123,8 @@ extern "C" {
 
 int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab)
 {
-    if (!out || max_batch < 1 || max_k < 0 || max_k > SPECVERIFY_MAX_K || max_vocab < 1)
+    if (!out || max_batch < 1 || max_k < 0 || max_k > SPECVERIFY_MAX_K || max_vocab < 1 ||
+        max_vocab > SPECVERIFY_MAX_VOCAB)
         return SPECVERIFY_EINVAL;
     *out = nullptr;
     int ndev = 0;
@@ -135,10 +136,7 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
 
     const size_t nch = (size_t)sv::max_chunks(max_vocab);
     const size_t rows = (size_t)max_batch * (2 * (size_t)max_k + 1);
-    const size_t b_p = align_up(rows * nch * sv::WAVES * sizeof(float2));
-    const size_t b_q = align_up((size_t)max_batch * sizeof(sv::SeqInfo));
-    const size_t b_r = align_up((size_t)max_batch * nch * sv::NV_RESID * sizeof(double));
-    const size_t total = b_p + b_q + b_r;
+    const size_t total = align_up(rows * nch * sv::WAVES * sizeof(float2));
 
     specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
     if (!ctx)
@@ -147,12 +145,7 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
         delete ctx;
         return SPECVERIFY_ENOMEM;
     }
-    char *p = static_cast<char *>(ctx->mem);
-    ctx->ws.part = reinterpret_cast<float2 *>(p);
-    p += b_p;
-    ctx->ws.seq = reinterpret_cast<sv::SeqInfo *>(p);
-    p += b_q;
-    ctx->ws.resid = reinterpret_cast<double *>(p);
+    ctx->ws.part = static_cast<float2 *>(ctx->mem);
     ctx->device = device;
     ctx->max_batch = max_batch;
     ctx->max_k = max_k;
@@ -161,6 +154,7 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     ctx->bytes = total;
     ctx->prof = false;
     ctx->prof_cap = ctx->prof_calls = 0;
+    ctx->prof_mask = 0;
     *out = ctx;
     return SPECVERIFY_OK;
 }
@@ -207,7 +201,7 @@ int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int 
     if (g.err != hipSuccess)
         return SPECVERIFY_EHIP;
     hipEvent_t *ev = next_events(ctx);
-    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev};
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
     hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
                                      accepted_len, out_tokens);
     note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
@@ -242,9 +236,9 @@ const char *specverify_strerror(int status)
     }
 }
 
-int specverify_profile_begin(specverify_ctx *ctx, int max_calls)
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds)
 {
-    if (!ctx || max_calls < 1 || ctx->prof)
+    if (!ctx || max_calls < 1 || ctx->prof || (kinds >> NK) != 0)
         return SPECVERIFY_EINVAL;
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess)
@@ -263,6 +257,7 @@ int specverify_profile_begin(specverify_ctx *ctx, int max_calls)
     ctx->prof = true;
     ctx->prof_cap = max_calls;
     ctx->prof_calls = 0;
+    ctx->prof_mask = kinds ? kinds : (1u << NK) - 1;
     return SPECVERIFY_OK;
 }
 

@@ -16,9 +16,18 @@ constexpr int WG = 256;               // threads per workgroup (4 wave64)
 constexpr int WAVES = WG / 64;
 constexpr int NV_STATS = 8;           // sampling row statistics: 32 KiB per workgroup
 constexpr int NV_PAIR = 4;            // contrastive row pairs: 2 x 16 KiB per workgroup
-constexpr int NV_RESID = 8;           // residual / bonus weights
 constexpr int NV_ARGMAX = 8;          // greedy argmax
 constexpr int MAX_ROWS = 2 * 63 + 1;  // rows per sequence at the largest K
+
+// The per-sequence tail (accept scan + draw) runs one 1024-thread workgroup per sequence;
+// its pass over row L loads NV_TAIL vectors per thread per row and iteration (64 KiB per
+// iteration when both rows are read, the next iteration's loads in flight while the current
+// one is weighed) and keeps one fp64 weight sum per wave and vector slot ("unit") in LDS.
+constexpr int TAIL_WG = 1024;
+constexpr int TAIL_WAVES = TAIL_WG / 64;
+constexpr int NV_TAIL = 2;
+constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the accept phase
+constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
@@ -28,6 +37,19 @@ inline int num_chunks(int nv, int dtype, int V)
 }
 // the most chunks any pass needs for a row of V ids (float32 pairs have the smallest chunks)
 inline int max_chunks(int V) { return num_chunks(NV_PAIR, 0, V); }
+inline int tail_units(int dtype, int V)
+{
+    const int ce = TAIL_WG * NV_TAIL * elems_per_vec(dtype);
+    return (V + ce - 1) / ce * NV_TAIL * TAIL_WAVES;
+}
+// dynamic LDS of the tail kernel: the staged partials, then (reusing it) the unit sums
+inline size_t tail_lds_bytes(int dtype, int K, int V, int nch)
+{
+    const size_t parts = (size_t)(2 * K + 1) * nch * WAVES;
+    const size_t stage = parts <= (size_t)ACCEPT_STAGE ? parts * 8 : 0;
+    const size_t units = (size_t)tail_units(dtype, V) * 8;
+    return stage > units ? stage : units;
+}
 
 // log2(e) / T split into two floats so that d * hi + d * lo carries ~48 bits of the
 // product: the exponent argument of every term then loses only one fp32 rounding.
@@ -39,11 +61,14 @@ struct Scale {
 };
 Scale make_scale(double temperature);
 
-// What the residual / bonus pass needs to know about one sequence after the accept scan.
+// What the draw needs to know about one sequence after the accept scan.
+// For the target row L (p) and the draft row L (q, L < K) with maximum M and sum S:
+// R = fl(M * hi) and is = 2^-e / S, e = fma(M, lo, fma(M, hi, -R)), so that a probability is
+// exp2(fma(x, lo, fma(x, hi, -R))) * is, the same form as the row statistics.
 struct SeqInfo {
     int L;           // first rejected position, K if none, -1 for bad ids
-    float Mp, Mq;    // row maxima of the target row L and of the draft row L (L < K)
-    float isp, isq;  // 1 / S of those rows
+    float Rp, Rq;
+    float isp, isq;
     int pad[3];
 };
 
@@ -51,24 +76,21 @@ enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };
 
 struct Workspace {
     float2 *part;       // [rows][nch][WAVES] per-wave (max, sum of exp2) or (max, id) partials
-    SeqInfo *seq;       // [B]
-    double *resid;      // [B][nch][NV_RESID] draw-weight totals of each chunk's vector rows
 };
 
 struct Launch {
     hipStream_t stream;
-    hipEvent_t *ev;     // NULL, or 2 events per kernel kind to time (start, stop)
+    hipEvent_t *ev;     // NULL, or 2 events per kernel kind (start, stop)
+    unsigned mask;      // kernel kinds whose events are recorded
 };
 
 // kernel kinds for timing
 enum Kind {
     KIND_STATS = 0,
-    KIND_ACCEPT = 1,
-    KIND_RESID = 2,
-    KIND_DRAW = 3,
-    KIND_ARGMAX = 4,
-    KIND_GREEDY_EMIT = 5,
-    NUM_KINDS = 6
+    KIND_TAIL = 1,
+    KIND_ARGMAX = 2,
+    KIND_GREEDY_EMIT = 3,
+    NUM_KINDS = 4
 };
 
 hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,

@@ -184,24 +184,6 @@ __device__ inline void wave_argmax(float &v, int &i)
     }
 }
 
-// exclusive prefix sum over the workgroup in thread order (fp64, fixed order)
-__device__ inline double block_exclusive_scan(double v)
-{
-    __shared__ double wtot[WAVES];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const double inc = wave_incl_scan(v, lane);
-    double exc = __shfl_up(inc, 1);
-    if (lane == 0)
-        exc = 0.0;
-    if (lane == 63)
-        wtot[w] = inc;
-    __syncthreads();
-    double off = 0.0;
-    for (int k = 0; k < w; ++k)
-        off += wtot[k];
-    return off + exc;
-}
-
 // ------------------------------------------------------------------ row statistics
 
 // Per-thread (max, sum of exp2 relative to that max) over NV vectors in registers.
@@ -259,8 +241,11 @@ __device__ inline void store_wave_partials(float2 v, float2 *dst)
     }
 }
 
-// Load NV vectors per thread of chunk `cbase` of a row: streamed 16-byte loads when the
-// whole chunk is inside an aligned row, element loads (ids >= V as -inf) otherwise.
+// Load NV vectors per thread of chunk `cbase` of a row, ids >= V as -inf.  In an aligned row
+// every vector that lies wholly below V is one streamed 16-byte load, all issued before any
+// use (a chunk at the end of the row only masks some of them off); only the vector that
+// straddles V, if V is not a multiple of the vector width, is read element by element.
+// Unaligned rows take element loads throughout.
 template <int DT, int NV>
 __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
                                   float (&x)[NV][Elt<DT>::EPV])
@@ -269,11 +254,36 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
     if (al && cbase + WG * NV * E <= V) {
         uint4 raw[NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+        for (int i = 0; i < NV; ++i) {
             raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY);
+        }
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             Elt<DT>::unpack(raw[i], x[i]);
+    } else if (al) {
+        constexpr uint32_t NEG_INF_WORD = (BY == 2) ? 0xff80ff80u : 0xff800000u;
+        uint4 raw[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e0 = cbase + (i * WG + threadIdx.x) * E;
+            if (e0 + E <= V)
+                raw[i] = load_stream(rp + (size_t)e0 * BY);
+            else
+                raw[i] = make_uint4(NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            Elt<DT>::unpack(raw[i], x[i]);
+        if (V % E != 0) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e0 = cbase + (i * WG + threadIdx.x) * E;
+                if (e0 < V && e0 + E > V)
+#pragma unroll
+                    for (int k = 0; k < E; ++k)
+                        x[i][k] = (e0 + k < V) ? Elt<DT>::one(rp, (size_t)(e0 + k)) : -INFINITY;
+            }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -281,22 +291,22 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
     }
 }
 
-// Sequence b after its rows' statistics: merge the per-wave partials of its 2K+1 rows (fp64),
-// then wave 0 runs the accept tests and the first-rejection scan, one lane per draft
-// position, and records what the residual pass needs.  The draft tokens and their logits
-// are fetched first and the sequence's partials are staged in LDS in one coalesced pass,
-// so the merge waits on memory once.
-constexpr int ACCEPT_STAGE = 4096;  // partials staged in LDS (32 KiB), else read in place
-
+// Sequence b after its rows' statistics (the first phase of k_tail): merge the per-wave
+// partials of its 2K+1 rows (fp64), then wave 0 runs the accept tests and the
+// first-rejection scan, one lane per draft position, writes accepted_len, the kept tokens,
+// -1 padding and out_probs, and leaves in *info what the draw needs (L = -1 for bad ids).
+// The draft tokens and their logits are fetched first and the partials are staged in LDS
+// in one coalesced pass when they fit, so the merge waits on memory once.
 template <int DT, int MODE>
-__device__ __forceinline__ void accept_block(const char *tgt, const char *drf, const int32_t *tokens,
-                             const float *unif, int b, int K, int V, int nch, const Scale &sp,
-                             const Scale &sq, const float2 *part, int32_t *acc_len,
-                             int32_t *out_tokens, float *out_probs, SeqInfo *seq)
+__device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
+                                             const int32_t *tokens, const float *unif, int b,
+                                             int K, int V, int nch, const Scale &sp,
+                                             const Scale &sq, const float2 *part, float2 *stage,
+                                             int32_t *acc_len, int32_t *out_tokens,
+                                             float *out_probs, SeqInfo *info)
 {
     __shared__ float sM[MAX_ROWS];
     __shared__ double sS[MAX_ROWS];
-    __shared__ float2 stage[ACCEPT_STAGE];
     const int R = 2 * K + 1, np = nch * WAVES, total = R * np;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 
@@ -323,23 +333,23 @@ __device__ __forceinline__ void accept_block(const char *tgt, const char *drf, c
     const float2 *pb = part + (size_t)b * total;
     const bool staged = total <= ACCEPT_STAGE;
     if (staged) {
-        for (int i0 = 0; i0 < total; i0 += 4 * WG) {
+        for (int i0 = 0; i0 < total; i0 += 4 * TAIL_WG) {
             float2 v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int i = i0 + k * WG + t;
+                const int i = i0 + k * TAIL_WG + t;
                 v[k] = (i < total) ? pb[i] : make_float2(0.0f, 0.0f);
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int i = i0 + k * WG + t;
+                const int i = i0 + k * TAIL_WG + t;
                 if (i < total)
                     stage[i] = v[k];
             }
         }
         __syncthreads();
     }
-    for (int r = w; r < R; r += WAVES) {
+    for (int r = w; r < R; r += TAIL_WAVES) {
         const int r0 = r * np;
         const double cc = (r <= K) ? sp.c : sq.c;
         float ml = -INFINITY;
@@ -374,7 +384,7 @@ __device__ __forceinline__ void accept_block(const char *tgt, const char *drf, c
             acc_len[b] = -1;
             SeqInfo si = {};
             si.L = -1;
-            seq[b] = si;
+            *info = si;
         }
         return;
     }
@@ -398,17 +408,21 @@ __device__ __forceinline__ void accept_block(const char *tgt, const char *drf, c
         acc_len[b] = L;
         SeqInfo si = {};
         si.L = L;
-        si.Mp = sM[L];
-        si.isp = (float)(1.0 / sS[L]);
+        const float Mp = sM[L];
+        si.Rp = Mp * sp.hi;
+        const float ep = __builtin_fmaf(Mp, sp.lo, __builtin_fmaf(Mp, sp.hi, -si.Rp));
+        si.isp = (float)(exp2(-(double)ep) / sS[L]);
         if (L < K) {
-            si.Mq = sM[K + 1 + L];
-            si.isq = (float)(1.0 / sS[K + 1 + L]);
+            const float Mq = sM[K + 1 + L];
+            si.Rq = Mq * sq.hi;
+            const float eq = __builtin_fmaf(Mq, sq.lo, __builtin_fmaf(Mq, sq.hi, -si.Rq));
+            si.isq = (float)(exp2(-(double)eq) / sS[K + 1 + L]);
         }
-        seq[b] = si;
+        *info = si;
     }
 }
 
-// rows b*(2K+1)+k: k <= K target row (b, k), else draft row (b, k-K-1); each wave stores its
+// rows b*(2K+1)+r: r <= K target row (b, r), else draft row (b, r-K-1); each wave stores its
 // (max, sum) partial at part[blockIdx.x * WAVES + wave]
 template <int DT>
 __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ tgt,
@@ -418,9 +432,9 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
     const int R = 2 * K + 1;
     const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
-    const int b = row / R, k = row - b * R;
-    const char *rp = (k <= K) ? tgt + ((size_t)b * (K + 1) + k) * (size_t)V * BY
-                              : drf + ((size_t)b * K + (k - K - 1)) * (size_t)V * BY;
+    const int b = row / R, r = row - b * R;
+    const char *rp = (r <= K) ? tgt + ((size_t)b * (K + 1) + r) * (size_t)V * BY
+                              : drf + ((size_t)b * K + (r - K - 1)) * (size_t)V * BY;
     float x[NV_STATS][E];
     load_chunk<DT, NV_STATS>(rp, aligned16(rp), c * WG * NV_STATS * E, V, x);
     float m, s;
@@ -428,7 +442,9 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
     store_wave_partials(wave_stats(m, s, sc), part + (size_t)blockIdx.x * WAVES);
 }
 
-// one workgroup per (row pair (b, j), chunk): target values l_e - l_a (fp32), draft values l_a
+// one workgroup per (row pair (b, j), chunk): target values l_e - l_a (fp32), draft values l_a;
+// the pair's expert row gives p_j's partials (row j of the sequence), its amateur row q_j's
+// (row K+1+j, j < K)
 template <int DT>
 __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
                                                           const char *__restrict__ am, int K, int V,
@@ -471,20 +487,6 @@ __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict
     }
 }
 
-// one workgroup per sequence
-template <int DT, int MODE>
-__global__ __launch_bounds__(WG) void k_accept(const char *__restrict__ tgt,
-                                               const char *__restrict__ drf,
-                                               const int32_t *__restrict__ tokens,
-                                               const float *__restrict__ unif, int K, int V,
-                                               int nch, Scale sp, Scale sq,
-                                               const float2 *__restrict__ part, int32_t *acc_len,
-                                               int32_t *out_tokens, float *out_probs, SeqInfo *seq)
-{
-    accept_block<DT, MODE>(tgt, drf, tokens, unif, blockIdx.x, K, V, nch, sp, sq, part, acc_len,
-                           out_tokens, out_probs, seq);
-}
-
 // ------------------------------------------------------------------ residual / bonus draw
 
 // The rows a sequence's draw reads: the target side (sampling: target row L; contrastive:
@@ -517,16 +519,21 @@ __device__ inline DrawRows draw_rows(const char *tgt, const char *drf, int b, in
 }
 
 // Draw weight of one id from its target-side value pv and draft-side value qv (fp32):
-// p = 2^((pv - Mp) log2(e)/T) / S_p; w = max(0, p - q) for a replacement, p for the bonus
-// (or when `target_law` asks for p).  The same instructions run in k_resid and in the
-// search, so both see identical weights.
+// p = 2^((pv - Mp) log2(e)/T) / S_p in the fma-reference form of the row statistics (see
+// SeqInfo); w = max(0, p - q) for a replacement, p for the bonus (or when `target_law` asks
+// for p).  The same instructions run in the unit pass and in the search, so both see
+// identical weights.
 __device__ inline float draw_weight(float pv, float qv, bool resid, bool target_law,
                                     const SeqInfo &si, const Scale &sp, const Scale &sq)
 {
-    const float p = exp2s(pv - si.Mp, sp.hi, sp.lo) * si.isp;
+    const float p =
+        __builtin_amdgcn_exp2f(__builtin_fmaf(pv, sp.lo, __builtin_fmaf(pv, sp.hi, -si.Rp))) *
+        si.isp;
     if (!resid || target_law)
         return p;
-    const float q = exp2s(qv - si.Mq, sq.hi, sq.lo) * si.isq;
+    const float q =
+        __builtin_amdgcn_exp2f(__builtin_fmaf(qv, sq.lo, __builtin_fmaf(qv, sq.hi, -si.Rq))) *
+        si.isq;
     return fmaxf(p - q, 0.0f);
 }
 
@@ -569,49 +576,49 @@ __device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint
     }
 }
 
-// NV_RESID vectors of this thread from ids e0(i) = base + i * WG * E (the coalesced pattern
-// of one chunk), both rows, all loads issued before any arithmetic.  Returns false (nothing
-// loaded) when some vector is not whole or the rows are not aligned; the caller then takes
-// the element path.
-template <int DT, bool NT>
-__device__ inline bool load_draw_vectors(const DrawRows &r, int base, int V,
-                                         uint4 (&a)[NV_RESID], uint4 (&q)[NV_RESID])
+// One k_tail iteration covers CE = TAIL_WG * NV_TAIL * E contiguous ids; thread t holds the
+// NV_TAIL vectors base + i*TAIL_WG*E + [0, E), base = the iteration's first id + t*E, so a
+// wave's loads are 1 KiB contiguous.  In an aligned row every vector wholly below V is one
+// streamed 16-byte load per row read (vectors at or past V load nothing).
+template <int DT>
+__device__ inline void tail_load(const DrawRows &r, int base, int V, uint4 (&a)[NV_TAIL],
+                                 uint4 (&q)[NV_TAIL])
 {
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = WG * Elt<DT>::EPV;
-    if (!r.al || base + (NV_RESID - 1) * STRIDE + E > V)
-        return false;
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = TAIL_WG * Elt<DT>::EPV;
+    if (!r.al)
+        return;
 #pragma unroll
-    for (int i = 0; i < NV_RESID; ++i) {
-        const size_t o = (size_t)(base + i * STRIDE) * BY;
-        a[i] = NT ? load_stream(r.p0 + o) : load_plain(r.p0 + o);
+    for (int i = 0; i < NV_TAIL; ++i) {
+        const int e0 = base + i * STRIDE;
+        if (e0 + E <= V)
+            a[i] = load_stream(r.p0 + (size_t)e0 * BY);
     }
     if (r.two)
 #pragma unroll
-        for (int i = 0; i < NV_RESID; ++i) {
-            const size_t o = (size_t)(base + i * STRIDE) * BY;
-            q[i] = NT ? load_stream(r.p1 + o) : load_plain(r.p1 + o);
+        for (int i = 0; i < NV_TAIL; ++i) {
+            const int e0 = base + i * STRIDE;
+            if (e0 + E <= V)
+                q[i] = load_stream(r.p1 + (size_t)e0 * BY);
         }
-    return true;
 }
 
-// This thread's draw-weight sums over chunk c, one per vector i (fp32 tree over the
-// vector's ids); vector i covers ids c*CE + (i*WG + t)*E + [0, E).  The same instructions
-// run in k_resid (which sums them) and in k_draw (which searches them), so both see the
-// same weights.
-template <int DT, int MODE, bool NT>
-__device__ inline void thread_vector_weights(const DrawRows &r, int c, int V, bool target_law,
-                                             const SeqInfo &si, const Scale &sp, const Scale &sq,
-                                             float (&vs)[NV_RESID], uint4 (&a)[NV_RESID],
-                                             uint4 (&q)[NV_RESID], bool &whole)
+// The draw-weight sums of this thread's vectors from tail_load (fp32 tree over each vector's
+// ids).  Vectors past V weigh 0; the one that straddles V (V not a multiple of the vector
+// width), and every vector of an unaligned row, is weighed element by element through
+// vec_weights_masked, which the unit search also uses: every id gets the same weight, bit
+// for bit, in both places.
+template <int DT, int MODE>
+__device__ inline void tail_weigh(const DrawRows &r, int base, int V, bool target_law,
+                                  const SeqInfo &si, const Scale &sp, const Scale &sq,
+                                  const uint4 (&a)[NV_TAIL], const uint4 (&q)[NV_TAIL],
+                                  float (&vs)[NV_TAIL])
 {
-    constexpr int E = Elt<DT>::EPV;
-    const int base = c * WG * NV_RESID * E + threadIdx.x * E;
-    whole = load_draw_vectors<DT, NT>(r, base, V, a, q);
+    constexpr int E = Elt<DT>::EPV, STRIDE = TAIL_WG * Elt<DT>::EPV;
 #pragma unroll
-    for (int i = 0; i < NV_RESID; ++i) {
-        const int e0 = base + i * WG * E;
+    for (int i = 0; i < NV_TAIL; ++i) {
+        const int e0 = base + i * STRIDE;
         float wv[E];
-        if (whole) {
+        if (r.al && e0 + E <= V) {
             raw_weights<DT, MODE>(r, a[i], q[i], target_law, si, sp, sq, wv);
             vs[i] = tree_sum<E>(wv);
         } else if (e0 < V) {
@@ -623,41 +630,49 @@ __device__ inline void thread_vector_weights(const DrawRows &r, int c, int V, bo
     }
 }
 
-// Per chunk c of row L, the totals of its NV_RESID vector rows: unit (c, i) covers the
-// contiguous ids c*CE + i*WG*E + [0, WG*E) and its weight sum goes to
-// resid[(b * nch + c) * NV_RESID + i] (per-thread fp32 vector sums, fp64 above them).
 template <int DT, int MODE>
-__global__ __launch_bounds__(WG) void k_resid(const char *__restrict__ tgt,
-                                              const char *__restrict__ drf, int K, int V, int nch,
-                                              Scale sp, Scale sq, const SeqInfo *__restrict__ seq,
-                                              double *resid)
+__device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV_TAIL],
+                                                 double *units)
 {
-    __shared__ double s_units[NV_RESID][WAVES];
-    const int b = blockIdx.x / nch, c = blockIdx.x - b * nch;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const SeqInfo si = seq[b];
-    if (si.L < 0)
-        return;
-    const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
-    float vs[NV_RESID];
-    uint4 a[NV_RESID], q[NV_RESID];
-    bool whole;
-    thread_vector_weights<DT, MODE, true>(r, c, V, false, si, sp, sq, vs, a, q, whole);
 #pragma unroll
-    for (int i = 0; i < NV_RESID; ++i) {
-        const double us = wave_sum((double)vs[i]);
+    for (int i = 0; i < NV_TAIL; ++i) {
+        const double s = wave_sum((double)vs[i]);
         if (lane == 0)
-            s_units[i][w] = us;
-    }
-    __syncthreads();
-    if (threadIdx.x < NV_RESID) {
-        const int i = threadIdx.x;
-        resid[(size_t)blockIdx.x * NV_RESID + i] =
-            ((s_units[i][0] + s_units[i][1]) + s_units[i][2]) + s_units[i][3];
+            units[(it * NV_TAIL + i) * TAIL_WAVES + w] = s;
     }
 }
 
-// Among `nu` units with totals unit(u) (ascending ids), wave 0 finds the first unit whose
+// One pass over row L (and the draft row L): unit u = (it*NV_TAIL + i)*TAIL_WAVES + w holds
+// the fp64 sum of wave w's draw weights at vector slot i of iteration it, i.e. the 64*E
+// contiguous ids it*CE + i*TAIL_WG*E + w*64*E + [0, 64*E); unit order is id order.  Two
+// register buffers alternate so that the next iteration's loads are in flight while the
+// current one is weighed.
+template <int DT, int MODE>
+__device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit, bool target_law,
+                                               const SeqInfo &si, const Scale &sp,
+                                               const Scale &sq, double *units)
+{
+    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
+    const int t0 = threadIdx.x * E;
+    uint4 a0[NV_TAIL], q0[NV_TAIL], a1[NV_TAIL], q1[NV_TAIL];
+    float vs[NV_TAIL];
+    tail_load<DT>(r, t0, V, a0, q0);
+    for (int it = 0; it < nit; it += 2) {
+        if (it + 1 < nit)
+            tail_load<DT>(r, (it + 1) * CE + t0, V, a1, q1);
+        tail_weigh<DT, MODE>(r, it * CE + t0, V, target_law, si, sp, sq, a0, q0, vs);
+        tail_store_units<DT, MODE>(it, vs, units);
+        if (it + 1 < nit) {
+            if (it + 2 < nit)
+                tail_load<DT>(r, (it + 2) * CE + t0, V, a0, q0);
+            tail_weigh<DT, MODE>(r, (it + 1) * CE + t0, V, target_law, si, sp, sq, a1, q1, vs);
+            tail_store_units<DT, MODE>(it + 1, vs, units);
+        }
+    }
+}
+
+// Among `nu` units with totals unit(u) (ascending ids), one wave finds the first unit whose
 // running total exceeds tt = u01 * W (W = the sum of all units, fixed order), or if rounding
 // leaves t at or past the last one, the last unit of positive weight (*fb = 1).  Returns the
 // unit (or -1 when every unit weighs 0) and writes its starting weight *base and tt.
@@ -695,19 +710,19 @@ __device__ inline int find_unit(F unit, int nu, float u01, double *base, double 
     return (us >= 0) ? us : last;
 }
 
-// Inside unit (c, i): thread t weighs vector i*WG + t of chunk c (the same instructions as
-// k_resid), a block scan of the vector sums finds the vector, and its owner emits the first
-// id whose running weight exceeds tt (fb: the last id of positive weight).
+// Inside unit `unit` (one wave): lane l weighs the unit's vector l with the instructions of
+// the unit pass, a wave scan of the vector sums from `base` finds the vector, and its lane
+// emits the first id whose running weight exceeds tt (fb: the last id of positive weight).
 template <int DT, int MODE>
 __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si, int V, int unit,
                                             double base, double tt, bool fb, bool target_law,
                                             const Scale &sp, const Scale &sq, int32_t *out)
 {
-    constexpr int E = Elt<DT>::EPV;
-    __shared__ int s_first, s_last;
-    const int t = threadIdx.x;
-    const int c = unit / NV_RESID, i = unit - c * NV_RESID;
-    const int e0 = c * WG * NV_RESID * E + (i * WG + t) * E;
+    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
+    const int lane = threadIdx.x & 63;
+    const int it = unit / (NV_TAIL * TAIL_WAVES), rem = unit - it * (NV_TAIL * TAIL_WAVES);
+    const int i = rem / TAIL_WAVES, ww = rem - i * TAIL_WAVES;
+    const int e0 = it * CE + i * TAIL_WG * E + (ww * 64 + lane) * E;
     float wv[E];
     if (e0 < V) {
         vec_weights_masked<DT, MODE>(r, e0, V, target_law, si, sp, sq, wv);
@@ -717,18 +732,21 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
             wv[k] = 0.0f;
     }
     const float vsum = tree_sum<E>(wv);
-    if (t == 0) {
-        s_first = WG;
-        s_last = -1;
+    const double inc = wave_incl_scan((double)vsum, lane);
+    double exc = __shfl_up(inc, 1);
+    if (lane == 0)
+        exc = 0.0;
+    const double bt = base + exc;
+    const unsigned long long hit = __ballot(!fb && vsum > 0.0f && bt + (double)vsum > tt);
+    const unsigned long long pos = __ballot(vsum > 0.0f);
+    if (pos == 0) {  // the unit's total is a sum of these vector sums, so this is not reached
+        if (lane == 0)
+            *out = -1;
+        return;
     }
-    const double bt = base + block_exclusive_scan((double)vsum);  // has a barrier
-    if (!fb && vsum > 0.0f && bt + (double)vsum > tt)
-        atomicMin(&s_first, t);
-    if (vsum > 0.0f)
-        atomicMax(&s_last, t);
-    __syncthreads();
-    const bool fb2 = fb || s_first == WG;
-    if (t != (fb2 ? s_last : s_first))
+    const bool fb2 = fb || hit == 0;
+    const int owner = fb2 ? 63 - __builtin_clzll(pos) : __builtin_ctzll(hit);
+    if (lane != owner)
         return;
     double run = bt;
     int y = -1, lastpos = -1;
@@ -745,92 +763,66 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
     *out = (y >= 0) ? y : lastpos;
 }
 
-// One workgroup per sequence: the unit holding t = u_K * W (from k_resid's unit totals),
-// then the id inside it.  If rounding left the residual empty, draw from the target law p_L
-// instead: its unit totals are computed here (essentially never taken).
+// One 1024-thread workgroup per sequence, after the row statistics: the accept phase
+// (merge, gather, accept tests, L), then one pass over row L (and draft row L) into unit sums
+// in LDS, then the unit holding t = u_K * W and the id inside it.  If rounding left the
+// residual empty, the pass is repeated with the target law p_L (essentially never taken).
+// Dynamic LDS: the staged partials during the accept phase, the unit sums afterwards.
 template <int DT, int MODE>
-__global__ __launch_bounds__(WG) void k_draw(const char *__restrict__ tgt,
-                                             const char *__restrict__ drf,
-                                             const float *__restrict__ unif, int K, int V, int nch,
-                                             Scale sp, Scale sq, const SeqInfo *__restrict__ seq,
-                                             const double *__restrict__ resid,
-                                             int32_t *out_tokens)
+__global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
+                                                  const char *__restrict__ drf,
+                                                  const int32_t *__restrict__ tokens,
+                                                  const float *__restrict__ unif, int K, int V,
+                                                  int nch, Scale sp, Scale sq,
+                                                  const float2 *__restrict__ part,
+                                                  int32_t *acc_len, int32_t *out_tokens,
+                                                  float *out_probs)
 {
+    extern __shared__ double dyn[];
+    __shared__ SeqInfo s_info;
     __shared__ int s_unit, s_fb;
     __shared__ double s_base, s_t;
-    __shared__ double s_units[NV_RESID][WAVES];
+    constexpr int CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
     const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int nu = nch * NV_RESID;
-    const double *ub = resid + (size_t)b * nu;
-    const SeqInfo si = seq[b];
+    accept_phase<DT, MODE>(tgt, drf, tokens, unif, b, K, V, nch, sp, sq, part,
+                           reinterpret_cast<float2 *>(dyn), acc_len, out_tokens, out_probs,
+                           &s_info);
+    __syncthreads();
+    const SeqInfo si = s_info;
     if (si.L < 0)
         return;
+    const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
+    const int nit = (V + CE - 1) / CE, nu = nit * NV_TAIL * TAIL_WAVES;
     const float u01 = unif[(size_t)b * (K + 1) + K];
     int32_t *out = out_tokens + (size_t)b * (K + 1) + si.L;
-    const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
-    if (t < 64) {
-        double base, tt;
-        int fb;
-        const int us = find_unit([&](int k) { return ub[k]; }, nu, u01, &base, &tt, &fb);
-        if (lane == 0) {
-            s_unit = us;
-            s_base = base;
-            s_t = tt;
-            s_fb = fb;
-        }
-    }
-    __syncthreads();
-    bool target_law = false;
-    if (s_unit < 0) {
-        // The residual is empty by rounding: draw from the target law p_L.  Its unit totals
-        // are computed here chunk by chunk, twice (the total, then the scan), in LDS only.
-        target_law = true;
-        double run = 0.0, tt = 0.0, last_base = 0.0;
-        int found = -1, last = -1;
-        for (int pass = 0; pass < 2 && found < 0; ++pass) {
-            run = 0.0;
-            for (int c = 0; c < nch && found < 0; ++c) {
-                float vs[NV_RESID];
-                uint4 a[NV_RESID], q[NV_RESID];
-                bool whole;
-                thread_vector_weights<DT, MODE, false>(r, c, V, true, si, sp, sq, vs, a, q, whole);
-                __syncthreads();  // s_units of the previous chunk have been read
-#pragma unroll
-                for (int i = 0; i < NV_RESID; ++i) {
-                    const double v = wave_sum((double)vs[i]);
-                    if (lane == 0)
-                        s_units[i][w] = v;
-                }
-                __syncthreads();
-                for (int i = 0; i < NV_RESID && found < 0; ++i) {  // every thread, same order
-                    const double ui =
-                        ((s_units[i][0] + s_units[i][1]) + s_units[i][2]) + s_units[i][3];
-                    if (pass == 1 && ui > 0.0) {
-                        if (run + ui > tt) {
-                            found = c * NV_RESID + i;
-                        } else {
-                            last = c * NV_RESID + i;
-                            last_base = run;
-                        }
-                    }
-                    if (found < 0)
-                        run += ui;
-                }
+    double *units = dyn;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool target_law = (pass == 1);
+        tail_unit_sums<DT, MODE>(r, V, nit, target_law, si, sp, sq, units);
+        __syncthreads();
+        if (w == 0) {
+            double base, tt;
+            int fb;
+            const int us = find_unit([&](int k) { return units[k]; }, nu, u01, &base, &tt, &fb);
+            if (lane == 0) {
+                s_unit = us;
+                s_base = base;
+                s_t = tt;
+                s_fb = fb;
             }
-            if (pass == 0)
-                tt = (double)u01 * run;
         }
-        const int us = (found >= 0) ? found : last;
-        if (us < 0) {
-            if (t == 0)
-                *out = -1;  // a row without finite logits: outside the contract
+        __syncthreads();
+        const int us = s_unit;
+        if (us >= 0) {
+            if (w == 0)
+                search_unit<DT, MODE>(r, si, V, us, s_base, s_t, s_fb != 0, target_law, sp, sq,
+                                      out);
             return;
         }
-        search_unit<DT, MODE>(r, si, V, us, (found >= 0) ? run : last_base, tt, found < 0, true,
-                              sp, sq, out);
-        return;
+        // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
     }
-    search_unit<DT, MODE>(r, si, V, s_unit, s_base, s_t, s_fb != 0, false, sp, sq, out);
+    if (t == 0)
+        *out = -1;  // a row without finite logits: outside the contract
 }
 
 // ------------------------------------------------------------------ greedy blockwise
@@ -914,14 +906,15 @@ struct Timer {
     int kind;
     Timer(const Launch &l, int k) : ln(l), kind(k)
     {
-        if (ln.ev)
+        if (on())
             (void)hipEventRecord(ln.ev[2 * kind], ln.stream);
     }
     ~Timer()
     {
-        if (ln.ev)
+        if (on())
             (void)hipEventRecord(ln.ev[2 * kind + 1], ln.stream);
     }
+    bool on() const { return ln.ev && ((ln.mask >> kind) & 1u); }
 };
 
 template <int DT, int MODE>
@@ -946,20 +939,10 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
         }
     }
     {
-        Timer tm(ln, KIND_ACCEPT);
-        hipLaunchKernelGGL((k_accept<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, tokens,
-                           unif, K, V, nch, sp, sq, ws.part, acc_len, out_tokens, out_probs, ws.seq);
-    }
-    const int ncr = num_chunks(NV_RESID, DT, V);
-    {
-        Timer tm(ln, KIND_RESID);
-        hipLaunchKernelGGL((k_resid<DT, MODE>), dim3((unsigned)((size_t)B * ncr)), dim3(WG), 0,
-                           ln.stream, t, d, K, V, ncr, sp, sq, ws.seq, ws.resid);
-    }
-    {
-        Timer tm(ln, KIND_DRAW);
-        hipLaunchKernelGGL((k_draw<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, unif, K, V,
-                           ncr, sp, sq, ws.seq, ws.resid, out_tokens);
+        Timer tm(ln, KIND_TAIL);
+        hipLaunchKernelGGL((k_tail<DT, MODE>), dim3(B), dim3(TAIL_WG),
+                           tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
+                           sp, sq, ws.part, acc_len, out_tokens, out_probs);
     }
     return hipGetLastError();
 }

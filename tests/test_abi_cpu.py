@@ -60,10 +60,22 @@ def test_null_context_is_rejected_on_the_host():
     assert lib.specverify_run_contrastive(None, None, 1, 1, 1, 8, 1.0, *([None] * 7)) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_run_greedy(None, None, 1, 1, 1, 8, None, None, None, None) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_destroy(None) == sv.SPECVERIFY_OK
-    assert lib.specverify_profile_begin(None, 4) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_begin(None, 4, 0) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_profile_end(None, None, None) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_workspace_bytes(None) == 0
     h = ctypes.c_void_p()
     assert lib.specverify_create(None, 0, 1, 1, 1) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_create(ctypes.byref(h), 0, 0, 1, 1) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_create(ctypes.byref(h), 0, 1, 64, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_create(ctypes.byref(h), 0, 1, 1, sv.SPECVERIFY_MAX_VOCAB + 1) == sv.SPECVERIFY_EINVAL
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (SPECVERIFY_\w+) (.+)", text))
+    assert eval(defs["SPECVERIFY_MAX_K"]) == sv.SPECVERIFY_MAX_K
+    assert eval(defs["SPECVERIFY_MAX_VOCAB"]) == sv.SPECVERIFY_MAX_VOCAB
+    assert eval(defs["SPECVERIFY_NUM_KERNELS"]) == sv.SPECVERIFY_NUM_KERNELS == len(sv.KERNEL_NAMES)
+    enums = dict((k, int(v)) for k, v in re.findall(r"\b(SPECVERIFY_[A-Z0-9]+) = (-?\d+)", text))
+    for k, v in enums.items():
+        assert getattr(sv, k) == v, k

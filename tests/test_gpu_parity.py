@@ -70,6 +70,9 @@ SMALL = [
     ("sampling", BF16, 9, 3, 16385),     # one bf16 chunk (16384 ids) and one id
     ("sampling", BF16, 6, 12, 50001),
     ("sampling", F32, 4, 7, 40000),
+    ("sampling", BF16, 5, 3, 65537),     # one tail-kernel pass over a bf16 row (65536 ids) and one id
+    ("sampling", F32, 4, 2, 32769),      # the same for f32 (32768 ids)
+    ("contrastive", F32, 3, 2, 65535),
     ("contrastive", BF16, 13, 3, 999),
     ("contrastive", F32, 5, 0, 8191),
     ("contrastive", BF16, 8, 4, 40003),
@@ -246,6 +249,7 @@ def test_host_side_errors(ctx):
     assert status(lambda: sv.specverify_run_greedy(ctx, None, BF16, 2, 4, 1000, t, None, acc, tok)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_create(0, 0, 4, 10)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_create(0, 4, 64, 10)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: sv.specverify_create(0, 4, 4, sv.SPECVERIFY_MAX_VOCAB + 1)) == sv.SPECVERIFY_EINVAL
     torch.cuda.synchronize()
     assert torch.all(tok == 9)  # nothing was written by any rejected call
 
@@ -256,7 +260,34 @@ def test_profile_api(ctx):
     for _ in range(3):
         run(ctx, w)
     ms, n = sv.specverify_profile_end(ctx)
-    assert n["row_stats"] == 3 and n["accept_scan"] == 3 and n["residual_sums"] == 3
-    assert n["draw"] == 3
+    assert n["row_stats"] == 3 and n["accept_draw"] == 3
     assert n["row_argmax"] == 0 and n["greedy_emit"] == 0
     assert all(v >= 0 for v in ms.values()) and ms["row_stats"] > 0
+    # a kinds mask times only the named kernels; calls past max_calls are not timed
+    sv.specverify_profile_begin(ctx, 2, ["row_stats"])
+    for _ in range(3):
+        run(ctx, w)
+    ms, n = sv.specverify_profile_end(ctx)
+    assert n["row_stats"] == 2 and n["accept_draw"] == 0 and ms["accept_draw"] == 0.0
+    lib = sv.load()
+    assert lib.specverify_profile_begin(ctx, 2, 1 << sv.SPECVERIFY_NUM_KERNELS) == sv.SPECVERIFY_EINVAL
+
+
+# ----------------------------------------------------------------- capacity limits
+
+@pytest.mark.parametrize("mode,dtype,B,K,V", [
+    ("sampling", BF16, 3, 63, 150000),    # 127 rows x 40 partials: read in place, not staged
+    ("contrastive", F32, 2, 63, 40000),
+    ("sampling", F32, 2, 2, 1 << 20),     # the largest vocabulary
+    ("sampling", BF16, 2, 3, 1 << 20),
+    ("greedy", BF16, 2, 63, 1 << 20),
+])
+def test_capacity_limits(mode, dtype, B, K, V):
+    h = sv.specverify_create(0, 4, 63, sv.SPECVERIFY_MAX_VOCAB)
+    try:
+        w = _small(mode, dtype, B, K, V, seed=9000 + K + V % 1000)
+        g = run(h, w)
+        rep = compare(w, g, oracle.run_workload(w))
+        _report("%s %s B=%d K=%d V=%d" % (mode, synth.DTYPE_NAMES[dtype], B, K, V), rep)
+    finally:
+        sv.specverify_destroy(h)
