@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark of the sampling verify-and-accept step on one MI355X.
+"""Benchmark of the batched verify-and-accept step on one MI355X.
 
-Workload: B=256 sequences, K=8 draft tokens, V=128256, bfloat16 logits, T=0.7 (target
-~N(0,4^2) plus +8 at 20 distinct ids per row, draft = target + N(0,1.5^2)), seeded and
-synthetic.  One step = one specverify_run_sampling call over the whole batch (row
-statistics, then accept + first-reject scan + residual/bonus draw).  Inputs sit in HBM
-before timing starts and alternate between two copies so that no step reads logits the
-previous one left in the 256 MB last-level cache.
+Default workload (the headline): sampling verify, B=256 sequences, K=8 draft tokens,
+V=128256, bfloat16 logits, T=0.7 (target ~N(0,4^2) plus +8 at 20 distinct ids per row,
+draft = target + N(0,1.5^2)), seeded and synthetic.  One step = one specverify_run_sampling
+call over the whole batch (row statistics, then accept + first-reject scan + residual/bonus
+draw).  Inputs sit in HBM before timing starts and alternate between two copies so that no
+step reads logits the previous one left in the 256 MB last-level cache.
 
-Prints one JSON line: verified draft positions/s (B*K per step), the row-statistics
-kernel's bytes/s against the 8 TB/s HBM peak (timed with HIP events on the call's stream),
-and the fp64 CPU oracle timed on a bounded sample of the same batch.
+Prints one JSON line: verified draft positions/s (B*K per step), the dominant kernel's
+bytes/s against the 8 TB/s HBM peak (timed with HIP events on the call's stream around that
+kernel only), and the fp64 CPU oracle timed on a bounded sample of the same batch.
+
+--workload names one of the other synthetic workloads (the tiny and mid-size sampling ones,
+greedy blockwise, contrastive) to measure its path the same way; the default is the one the
+headline metric is quoted on.
 """
 from __future__ import annotations
 
@@ -25,11 +29,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0
-B, K, V, T, SEED = 256, 8, 128256, 0.7, 1003
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_row_amd", "csrc", "sv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_bf16_B256_K8_V128256_traffic.md")
+
+# workload key -> (description, dominant kernel kind, its kernel name, traffic summary file)
+WORKLOADS = {
+    "c3": ("sampling verify B=256 K=8 V=128256 bf16 logits T=0.7", "row_stats",
+           "k_stats_sampling<bf16>", "row_stats_bf16_B256_K8_V128256_traffic.md"),
+    "c1": ("sampling verify B=1 K=4 V=1000 f32 logits T=1", "row_stats",
+           "k_stats_sampling<f32>", None),
+    "c2": ("sampling verify B=64 K=5 V=32000 f32 logits T=1", "row_stats",
+           "k_stats_sampling<f32>", None),
+    "c4": ("greedy blockwise verify B=512 K=8 V=32000 bf16 logits", "row_argmax",
+           "k_argmax<bf16>", "row_argmax_bf16_B512_K8_V32000_traffic.md"),
+    "c5": ("contrastive verify B=128 K=4 V=152064 bf16 logits tau=1", "row_stats",
+           "k_stats_contrastive<bf16>", "contrastive_stats_bf16_B128_K4_V152064_traffic.md"),
+}
+METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
 
 def log(msg):
@@ -41,13 +57,16 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the row-statistics kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(name):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, if there is one and it was taken on the current kernel source; else None."""
+    if not name:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         line = line.strip().lstrip("-* ")
         if ":" in line and line.startswith(("traffic_bytes_per_launch", "kernel_source_sha256")):
             k, v = line.split(":", 1)
@@ -80,6 +99,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work for the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -101,9 +121,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    log("generating the workload (seed %d)" % SEED)
-    w = synth.c3_sampling_large_vocab(B=B, seed=SEED)
-    log("uploading %.2f GB of logits x2" % (w.logit_bytes / 1e9))
+    desc, kind, kname, traffic_file = WORKLOADS[args.workload]
+    w = synth.CONFIGS[args.workload]()
+    B, K, V = w.B, w.K, w.V
+    log("generated %s (seed %d); uploading %.3f GB of logits x2"
+        % (desc, w.seed, w.logit_bytes / 1e9))
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -111,8 +133,9 @@ def main():
 
     copies = []
     for _ in range(2):
-        copies.append((up(w.target), up(w.draft)))
-    toks, unif = up(w.tokens), up(w.uniforms)
+        copies.append((up(w.target), up(w.draft) if w.draft is not None else None))
+    toks = up(w.tokens)
+    unif = up(w.uniforms) if w.uniforms is not None else None
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
     out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
     probs = torch.empty((B, K, 2), dtype=torch.float32, device="cuda")
@@ -121,16 +144,22 @@ def main():
 
     def step(i):
         tg, dr = copies[i & 1]
-        sv.specverify_run_sampling(ctx, stream, synth.BF16, B, K, V, w.temperature, tg, dr, toks,
-                                   unif, acc, out, probs)
+        if w.mode == synth.GREEDY:
+            sv.specverify_run_greedy(ctx, stream, w.dtype, B, K, V, tg, toks, acc, out)
+        elif w.mode == synth.CONTRASTIVE:
+            sv.specverify_run_contrastive(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
+                                          toks, unif, acc, out, probs)
+        else:
+            sv.specverify_run_sampling(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
+                                       toks, unif, acc, out, probs)
 
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
-    # HIP events around the row-statistics kernel only, on the call's stream
-    sv.specverify_profile_begin(ctx, args.steps, ["row_stats"])
+    # HIP events around the dominant kernel only, on the call's stream
+    sv.specverify_profile_begin(ctx, args.steps, [kind])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -157,12 +186,15 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     positions = B * K / (ms_step * 1e-3)
-    stats_ms = kms["row_stats"] / max(kn["row_stats"], 1)
+    kern_ms = kms[kind] / max(kn[kind], 1)
     logit_bytes = w.logit_bytes                      # one read of every logit row
-    call_bytes = logit_bytes + w.tokens.nbytes + w.uniforms.nbytes + acc.nbytes + out.nbytes
-    achieved = logit_bytes / (stats_ms * 1e-3) / 1e9
+    call_bytes = logit_bytes + w.tokens.nbytes + acc.nbytes + out.nbytes
+    if w.uniforms is not None:
+        call_bytes += w.uniforms.nbytes
+    achieved = logit_bytes / (kern_ms * 1e-3) / 1e9
     res = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "c3"
+        else "verified draft positions/s + HBM GB/s vs peak, " + desc,
         "value": positions,
         "unit": "verified draft positions/s",
         "n_gpus": 1,
@@ -174,15 +206,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "sampling verify B=256 K=8 V=128256 bf16 logits T=0.7",
-                   "B": B, "K": K, "V": V, "logits": "bf16", "temperature": T, "seed": SEED},
+        "config": {"workload": desc, "mode": w.mode, "B": B, "K": K, "V": V,
+                   "logits": synth.DTYPE_NAMES[w.dtype], "temperature": w.temperature,
+                   "seed": w.seed},
         "hbm_gbps_per_call": call_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac_of_peak_per_call": call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(),
-                     "kernel": "k_stats_sampling<bf16>", "algorithmic_bytes": logit_bytes,
-                     "avg_ms": stats_ms},
+                     "traffic": measured_traffic(traffic_file),
+                     "kernel": kname, "algorithmic_bytes": logit_bytes, "avg_ms": kern_ms},
         "kernels_ms_per_step": {k: bms[k] / bn[k] for k in bms if bn[k]},
         "mean_accepted_len": mean_L,
     }
