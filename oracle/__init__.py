@@ -61,6 +61,16 @@ def _load():
         lib.oracle_run_greedy.restype = ctypes.c_int
         lib.oracle_softmax.argtypes = [f64p, ctypes.c_int, f64p]
         lib.oracle_softmax.restype = None
+        lib.oracle_sample_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, vp, f32p, i32p, f64p, f64p, i32p]
+        lib.oracle_sample_rows.restype = ctypes.c_int
+        lib.oracle_run_greedy_heads.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, vp, i32p, i32p, i32p,
+                                                i32p]
+        lib.oracle_run_greedy_heads.restype = ctypes.c_int
+        lib.oracle_quantile_cut.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, f32p,
+                                            f32p, vp, i32p]
+        lib.oracle_quantile_cut.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -154,6 +164,76 @@ def run_greedy(dtype: int, B: int, K: int, V: int, target, proposals) -> Result:
     if rc != 0:
         raise ValueError("oracle_run_greedy failed: %d" % rc)
     return Result(L, tok)
+
+
+@dataclass
+class SampleResult:
+    tokens: np.ndarray        # int32 [N]
+    probs: np.ndarray         # float64 [N]: the drawn token's probability
+    margin: np.ndarray        # float64 [N]: distance of t to the drawn interval's nearer edge, / W
+    alt_token: np.ndarray     # int32 [N]: the id across that edge
+
+
+def sample_rows(dtype: int, N: int, V: int, T: float, logits, uniforms) -> SampleResult:
+    """One inverse-CDF draw per row from softmax(logits / T) (the draft-token sampler)."""
+    lib = _load()
+    logits = _logits(logits, dtype)
+    assert logits.size == N * V
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(N)
+    tok = np.empty(N, np.int32)
+    pr = np.empty(N, np.float64)
+    mg = np.empty(N, np.float64)
+    alt = np.empty(N, np.int32)
+    rc = lib.oracle_sample_rows(dtype, N, V, float(T), _ptr(logits), _ptr(u), _ptr(tok), _ptr(pr),
+                                _ptr(mg), _ptr(alt))
+    if rc != 0:
+        raise ValueError("oracle_sample_rows failed: %d" % rc)
+    return SampleResult(tok, pr, mg, alt)
+
+
+@dataclass
+class HeadsResult:
+    accepted_len: np.ndarray    # int32 [B]
+    out_tokens: np.ndarray      # int32 [B][K+1]
+    next_proposals: np.ndarray  # int32 [B][H-1]
+
+
+def run_greedy_heads(dtype: int, B: int, K: int, H: int, V: int, logits, proposals) -> HeadsResult:
+    """Greedy blockwise verify over [B][K+1][H][V] head logits, with the next block's
+    proposals from heads 1..H-1 at the emitted position."""
+    lib = _load()
+    logits = _logits(logits, dtype)
+    assert logits.size == B * (K + 1) * H * V
+    x = np.ascontiguousarray(proposals, dtype=np.int32).reshape(B, K)
+    L = np.empty(B, np.int32)
+    tok = np.empty((B, K + 1), np.int32)
+    nxt = np.empty((B, max(H - 1, 0)), np.int32)
+    rc = lib.oracle_run_greedy_heads(dtype, B, K, H, V, _ptr(logits), _ptr(x), _ptr(L), _ptr(tok),
+                                     _ptr(nxt))
+    if rc != 0:
+        raise ValueError("oracle_run_greedy_heads failed: %d" % rc)
+    return HeadsResult(L, tok, nxt)
+
+
+@dataclass
+class CutResult:
+    r_cut: np.ndarray   # float32 [P]
+    keep: np.ndarray    # bool [P][N]
+    n_keep: np.ndarray  # int32 [P]
+
+
+def quantile_cut(P: int, N: int, alpha: float, scores) -> CutResult:
+    """Per prompt: r_cut = the (min(floor(alpha N), N-1) + 1)-th smallest score; keep the
+    responses scoring >= r_cut."""
+    lib = _load()
+    s = np.ascontiguousarray(scores, dtype=np.float32).reshape(P, N)
+    cut = np.empty(P, np.float32)
+    keep = np.empty((P, N), np.uint8)
+    n = np.empty(P, np.int32)
+    rc = lib.oracle_quantile_cut(P, N, float(alpha), _ptr(s), _ptr(cut), _ptr(keep), _ptr(n))
+    if rc != 0:
+        raise ValueError("oracle_quantile_cut failed: %d" % rc)
+    return CutResult(cut, keep.astype(bool), n)
 
 
 def run_workload(w) -> Result:

@@ -361,3 +361,134 @@ int oracle_run_greedy(int dtype, int B, int K, int V, const void *target,
     }
     return OR_OK;
 }
+
+/*
+ * Draft-token sampler: one draw per row, x_n ~ softmax(l[n,:] / T) by the inverse CDF at
+ * u[n] (ascending id, strict ">"), the draft model proposing its next token ("推测性拒绝采样",
+ * step 1; Speculative Contrastive Decoding review, Ma drafting gamma tokens).
+ * logits [N][V] (dtype), uniforms [N].  Outputs out_tokens [N], out_probs [N] (the drawn
+ * token's probability, may be NULL), margin [N] (distance of t to the nearer edge of the
+ * drawn id's interval / W) and alt_token [N] (the id across that edge); both may be NULL.
+ */
+int oracle_sample_rows(int dtype, int N, int V, double T, const void *logits,
+                       const float *uniforms, int32_t *out_tokens, double *out_probs,
+                       double *margin, int32_t *alt_token)
+{
+    if (N < 0 || V < 1 || !(T > 0.0) || (dtype != OR_F32 && dtype != OR_BF16))
+        return OR_EINVAL;
+    double *z = malloc(sizeof(double) * (size_t)V);
+    double *p = malloc(sizeof(double) * (size_t)V);
+    if (!z || !p) {
+        free(z); free(p);
+        return OR_ENOMEM;
+    }
+    for (int n = 0; n < N; ++n) {
+        size_t off = (size_t)n * V;
+        for (int v = 0; v < V; ++v)
+            z[v] = logit_at(dtype, logits, off + v) / T;
+        oracle_softmax(z, V, p);
+        double mu;
+        int alt;
+        int y = inverse_cdf(p, V, (double)uniforms[n], &mu, &alt);
+        out_tokens[n] = y;
+        if (out_probs)
+            out_probs[n] = p[y];
+        if (margin)
+            margin[n] = mu;
+        if (alt_token)
+            alt_token[n] = alt;
+    }
+    free(z); free(p);
+    return OR_OK;
+}
+
+/*
+ * Greedy blockwise verify with the next block's proposals from the same pass ("Blockwise
+ * Parallel Decoding", section 3.6, Predict and Verify merged).  logits [B][K+1][H][V]: at
+ * position j (the prefix followed by proposals 0..j-1) head h scores the token h places
+ * after that position; head 0 is the base model.  g_j = first argmax of head 0 at position
+ * j; L = first j < K with proposal_j != g_j, else K; emits g_0..g_L then -1 (as
+ * oracle_run_greedy); next_proposals [B][H-1] = first argmaxes of heads 1..H-1 at position L,
+ * the heads that condition on the emitted prefix.  A proposal outside [0, V) marks the
+ * sequence bad (accepted_len -1, all tokens and next proposals -1).
+ */
+int oracle_run_greedy_heads(int dtype, int B, int K, int H, int V, const void *logits,
+                            const int32_t *proposals, int32_t *accepted_len, int32_t *out_tokens,
+                            int32_t *next_proposals)
+{
+    if (B < 0 || K < 0 || H < 1 || V < 1 || (dtype != OR_F32 && dtype != OR_BF16))
+        return OR_EINVAL;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *x = proposals + (size_t)b * K;
+        int32_t *tok = out_tokens + (size_t)b * (K + 1);
+        int32_t *nxt = next_proposals + (size_t)b * (H - 1);
+        if (!ids_ok(x, K, V)) {
+            margins_t mg;
+            mark_bad(K, accepted_len + b, tok, NULL, &mg);
+            for (int h = 1; h < H; ++h)
+                nxt[h - 1] = -1;
+            continue;
+        }
+        int L = K;
+        for (int j = 0; j <= K; ++j) {
+            size_t row = ((size_t)b * (K + 1) + j) * H;
+            int g = first_argmax(dtype, logits, row * V, V);
+            tok[j] = g;
+            if (j < K && x[j] != g) {
+                L = j;
+                break;
+            }
+        }
+        for (int j = L + 1; j <= K; ++j)
+            tok[j] = -1;
+        accepted_len[b] = L;
+        size_t rowL = ((size_t)b * (K + 1) + L) * H;
+        for (int h = 1; h < H; ++h)
+            nxt[h - 1] = first_argmax(dtype, logits, (rowL + h) * V, V);
+    }
+    return OR_OK;
+}
+
+static int cmp_float(const void *a, const void *b)
+{
+    float x = *(const float *)a, y = *(const float *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Speculative Rejection's cut ("Speculative Rejection" Best-of-N page, section 4.2: score the
+ * partial responses with the reward model, take the rejection threshold r_cut at the
+ * alpha-quantile of the scores, keep the responses that reach it).  For each of P prompts with
+ * N scores: r_cut = the (k+1)-th smallest score with k = min(floor(alpha * N), N - 1), so the
+ * floor(alpha * N) lowest-scoring responses fall below it; keep[i] = (score_i >= r_cut), so
+ * ties at r_cut are all kept and at least one response survives.  scores [P][N] (finite);
+ * outputs r_cut [P], keep [P][N] (0/1), n_keep [P].
+ */
+int oracle_quantile_cut(int P, int N, double alpha, const float *scores, float *r_cut,
+                        uint8_t *keep, int32_t *n_keep)
+{
+    if (P < 0 || N < 1 || !(alpha >= 0.0 && alpha <= 1.0))
+        return OR_EINVAL;
+    long k = (long)floor(alpha * (double)N);
+    if (k > N - 1)
+        k = N - 1;
+    float *s = malloc(sizeof(float) * (size_t)N);
+    if (!s)
+        return OR_ENOMEM;
+    for (int p = 0; p < P; ++p) {
+        const float *row = scores + (size_t)p * N;
+        memcpy(s, row, sizeof(float) * (size_t)N);
+        qsort(s, (size_t)N, sizeof(float), cmp_float);
+        float cut = s[k];
+        r_cut[p] = cut;
+        int32_t c = 0;
+        for (int i = 0; i < N; ++i) {
+            uint8_t kk = row[i] >= cut;
+            keep[(size_t)p * N + i] = kk;
+            c += kk;
+        }
+        n_keep[p] = c;
+    }
+    free(s);
+    return OR_OK;
+}

@@ -43,6 +43,19 @@ MUTANTS = [
      "z[v] = logit_at(dtype, amateur, off + v);", "z[v] = logit_at(dtype, amateur, off + v) / tau;"),
     ("greedy emits the proposal at the mismatch",
      "            tok[j] = g;\n", "            tok[j] = (j < K) ? x[j] : g;\n"),
+    ("next proposals from the last accepted position instead of L",
+     "size_t rowL = ((size_t)b * (K + 1) + L) * H;",
+     "size_t rowL = ((size_t)b * (K + 1) + (L > 0 ? L - 1 : 0)) * H;"),
+    ("next proposals from the head before",
+     "nxt[h - 1] = first_argmax(dtype, logits, (rowL + h) * V, V);",
+     "nxt[h - 1] = first_argmax(dtype, logits, (rowL + h - 1) * V, V);"),
+    ("sampler without the temperature",
+     "            z[v] = logit_at(dtype, logits, off + v) / T;\n        oracle_softmax(z, V, p);",
+     "            z[v] = logit_at(dtype, logits, off + v);\n        oracle_softmax(z, V, p);"),
+    ("quantile index rounded up", "long k = (long)floor(alpha * (double)N);",
+     "long k = (long)ceil(alpha * (double)N);"),
+    ("cut keeps only scores strictly above it", "uint8_t kk = row[i] >= cut;",
+     "uint8_t kk = row[i] > cut;"),
 ]
 
 # the quick pins (the z-tests at the larger sizes add nothing for these slips)
@@ -60,7 +73,8 @@ def _build(src_text, out):
 def _run_pins(lib):
     env = dict(os.environ, SPECVERIFY_ORACLE_LIB=lib)
     cmd = [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-           os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", PIN_SELECTION]
+           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+           os.path.join(ROOT, "tests", "test_oracle_pins_next.py"), "-k", PIN_SELECTION]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
 
 
