@@ -16,6 +16,12 @@
  *    Accept: longest prefix on which the target's argmax equals the proposals).
  *  - Contrastive-target verify: "Speculative Contrastive Decoding" review, sections on
  *    contrastive decoding (large-model minus small-model distribution) and SCD.
+ *  - Draft-token sampler: "推测性拒绝采样", step 1 (the draft model proposes its tokens one
+ *    at a time); SCD review (Ma drafts gamma tokens).
+ *  - Greedy verify with the next block's proposals: "Blockwise Parallel Decoding", section
+ *    3.6 (Predict and Verify merged into one pass of the heads).
+ *  - Alpha-quantile cut: "Speculative Rejection" Best-of-N page, section 4.2 (rejection
+ *    threshold r_cut at the alpha-quantile of the partial rewards).
  *
  * Conventions for every entry point below:
  *  - All array pointers are DEVICE pointers owned by the caller; arrays are row-major and
@@ -65,6 +71,9 @@ enum specverify_status {
 
 /* Largest vocabulary a context accepts (the draw keeps its per-slice weight sums on chip). */
 #define SPECVERIFY_MAX_VOCAB (1 << 20)
+
+/* Most scores per prompt the quantile cut accepts (they are selected on chip). */
+#define SPECVERIFY_MAX_CUT_N 8192
 
 /*
  * Create a context on HIP device `device` for calls with B <= max_batch, K <= max_k and
@@ -126,6 +135,47 @@ int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype,
                                const float *uniforms, int32_t *accepted_len,
                                int32_t *out_tokens, float *out_probs);
 
+/*
+ * Draft-token sampler: one draw per row, out_tokens[n] = the first id (ascending) whose
+ * inclusive prefix sum of p = softmax(logits[n,:] / T) exceeds uniforms[n] * sum(p).
+ * logits [N][V] (dtype), uniforms [N] float in [0,1]; out_tokens [N] int32; out_probs [N]
+ * float = p(out_tokens[n]) (fp64 from the row's statistics) or NULL.
+ * N is limited by the context's max_batch and V by its max_vocab (ECAPACITY); other errors
+ * as for specverify_run_sampling.  The same two kernels as sampling verify run, with no
+ * draft positions.
+ */
+int specverify_sample(specverify_ctx *ctx, void *hip_stream, int dtype, int N, int V,
+                      float temperature, const void *logits, const float *uniforms,
+                      int32_t *out_tokens, float *out_probs);
+
+/*
+ * Greedy blockwise verify whose verify pass also carries the next block's proposals.
+ * logits [B][K+1][H][V] (dtype): at position j (the prefix followed by proposals 0..j-1),
+ * head h scores the token h places after it; head 0 is the base model.  accepted_len and
+ * out_tokens are those of specverify_run_greedy on head 0 (L = longest prefix on which the
+ * proposals equal head 0's first argmax; g_0..g_L emitted).  next_proposals [B][H-1] =
+ * the first argmaxes of heads 1..H-1 at position L, the proposals for the positions after
+ * the emitted g_L (-1 for a sequence with bad ids); may be NULL when H = 1.
+ * Errors: EINVAL for H < 1 and as specverify_run_greedy; ECAPACITY for B, K or V above the
+ * context's capacity.
+ */
+int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
+                                int H, int V, const void *logits, const int32_t *proposals,
+                                int32_t *accepted_len, int32_t *out_tokens,
+                                int32_t *next_proposals);
+
+/*
+ * Alpha-quantile cut of P prompts' N partial-reward scores each (scores [P][N] float, finite):
+ * with k = min(floor(alpha * N), N - 1) (computed in double on the host), r_cut[p] = the
+ * (k+1)-th smallest score of prompt p, keep[p][i] = (scores[p][i] >= r_cut[p]) as 0/1 bytes,
+ * n_keep[p] = the number kept (>= N - k; ties at r_cut are all kept).  Exact: comparisons
+ * only.  Errors: EINVAL (NULL pointers, P < 0, N < 1, alpha outside [0, 1] or NaN),
+ * ECAPACITY (N > SPECVERIFY_MAX_CUT_N).  Needs no workspace: the context supplies the
+ * device and the timing.
+ */
+int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N, float alpha,
+                            const float *scores, float *r_cut, uint8_t *keep, int32_t *n_keep);
+
 /* Release the context and its workspace.  NULL-safe; returns SPECVERIFY_OK. */
 int specverify_destroy(specverify_ctx *ctx);
 
@@ -134,8 +184,9 @@ const char *specverify_strerror(int status);
 
 /*
  * Kernel timing.  Kernel kinds:
- *   0 row statistics (sampling, contrastive), 1 accept scan and draw (sampling,
- *   contrastive), 2 row argmax (greedy), 3 proposal compare and emit (greedy).
+ *   0 row statistics (sampling, contrastive, sampler), 1 accept scan and draw (sampling,
+ *   contrastive, sampler), 2 row argmax (greedy), 3 proposal compare and emit (greedy, with
+ *   the next proposals for the heads variant), 4 quantile cut.
  * specverify_profile_begin(ctx, max_calls, kinds) creates hipEvent pairs for up to
  * max_calls subsequent run_* calls and records one pair around every kernel they launch
  * whose kind k has bit (1 << k) set in `kinds` (0 = every kind), on the call's stream.
@@ -145,7 +196,7 @@ const char *specverify_strerror(int status);
  * Errors: EINVAL (NULL ctx, max_calls < 1, unknown kind bits, begin twice, end without
  * begin), EHIP.
  */
-#define SPECVERIFY_NUM_KERNELS 4
+#define SPECVERIFY_NUM_KERNELS 5
 int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds);
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
 

@@ -246,6 +246,10 @@ def run_workload(w) -> Result:
                                w.tokens, w.uniforms)
     if w.mode == "greedy":
         return run_greedy(w.dtype, w.B, w.K, w.V, w.target, w.tokens)
+    if w.mode == "sample":
+        return sample_rows(w.dtype, w.B, w.V, w.temperature, w.target, w.uniforms)
+    if w.mode == "greedy_heads":
+        return run_greedy_heads(w.dtype, w.B, w.K, w.meta["H"], w.V, w.target, w.tokens)
     raise ValueError(w.mode)
 
 

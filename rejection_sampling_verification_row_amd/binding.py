@@ -26,8 +26,9 @@ SPECVERIFY_ECAPACITY = -5
 
 SPECVERIFY_MAX_K = 63
 SPECVERIFY_MAX_VOCAB = 1 << 20
-SPECVERIFY_NUM_KERNELS = 4
-KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit")
+SPECVERIFY_MAX_CUT_N = 8192
+SPECVERIFY_NUM_KERNELS = 5
+KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit", "quantile_cut")
 
 _lib = None
 _lock = threading.Lock()
@@ -64,6 +65,12 @@ def load():
         lib.specverify_run_contrastive.restype = i
         lib.specverify_run_greedy.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
         lib.specverify_run_greedy.restype = i
+        lib.specverify_sample.argtypes = [vp, vp, i, i, i, f, vp, vp, vp, vp]
+        lib.specverify_sample.restype = i
+        lib.specverify_run_greedy_heads.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp]
+        lib.specverify_run_greedy_heads.restype = i
+        lib.specverify_quantile_cut.argtypes = [vp, vp, i, i, f, vp, vp, vp, vp]
+        lib.specverify_quantile_cut.restype = i
         lib.specverify_destroy.argtypes = [vp]
         lib.specverify_destroy.restype = i
         lib.specverify_strerror.argtypes = [i]
@@ -144,6 +151,27 @@ def specverify_run_greedy(ctx, stream, dtype, B, K, V, target_logits, proposals,
     _check(load().specverify_run_greedy(
         ctx, _stream(stream), dtype, B, K, V, _ptr(target_logits), _ptr(proposals),
         _ptr(accepted_len), _ptr(out_tokens)), "specverify_run_greedy")
+
+
+def specverify_sample(ctx, stream, dtype, N, V, temperature, logits, uniforms, out_tokens,
+                      out_probs=None) -> None:
+    _check(load().specverify_sample(
+        ctx, _stream(stream), dtype, N, V, float(temperature), _ptr(logits), _ptr(uniforms),
+        _ptr(out_tokens), _ptr(out_probs)), "specverify_sample")
+
+
+def specverify_run_greedy_heads(ctx, stream, dtype, B, K, H, V, logits, proposals, accepted_len,
+                                out_tokens, next_proposals=None) -> None:
+    _check(load().specverify_run_greedy_heads(
+        ctx, _stream(stream), dtype, B, K, H, V, _ptr(logits), _ptr(proposals),
+        _ptr(accepted_len), _ptr(out_tokens), _ptr(next_proposals)),
+        "specverify_run_greedy_heads")
+
+
+def specverify_quantile_cut(ctx, stream, P, N, alpha, scores, r_cut, keep, n_keep) -> None:
+    _check(load().specverify_quantile_cut(
+        ctx, _stream(stream), P, N, float(alpha), _ptr(scores), _ptr(r_cut), _ptr(keep),
+        _ptr(n_keep)), "specverify_quantile_cut")
 
 
 def specverify_destroy(ctx) -> None:

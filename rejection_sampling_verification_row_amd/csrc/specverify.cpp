@@ -29,6 +29,8 @@ namespace {
 
 constexpr int NK = SPECVERIFY_NUM_KERNELS;
 static_assert(NK == sv::NUM_KINDS, "kernel kinds out of step with the header");
+static_assert(SPECVERIFY_MAX_CUT_N == sv::MAX_CUT_N, "cut capacity out of step with the header");
+static_assert(SPECVERIFY_MAX_VOCAB == sv::MAX_VOCAB, "vocabulary cap out of step with the header");
 
 struct DeviceGuard {
     int prev = -1;
@@ -112,7 +114,7 @@ int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, in
     hipEvent_t *ev = next_events(ctx);
     sv::Launch ln{static_cast<hipStream_t>(stream), ev, ctx->prof_mask};
     hipError_t e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
-                                       unif, acc_len, out_tokens, out_probs);
+                                       unif, acc_len, out_tokens, out_probs, nullptr);
     note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_TAIL));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
@@ -205,6 +207,97 @@ int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int 
     hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
                                      accepted_len, out_tokens);
     note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_sample(specverify_ctx *ctx, void *hip_stream, int dtype, int N, int V,
+                      float temperature, const void *logits, const float *uniforms,
+                      int32_t *out_tokens, float *out_probs)
+{
+    int rc = check_common(ctx, dtype, N, 0, V);
+    if (rc != SPECVERIFY_OK)
+        return rc;
+    if (bad_temperature(temperature))
+        return SPECVERIFY_EINVAL;
+    if (N == 0)
+        return SPECVERIFY_OK;
+    if (!logits || !uniforms || !out_tokens)
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(logits, es) || !aligned_to(uniforms, 4) || !aligned_to(out_tokens, 4) ||
+        (out_probs && !aligned_to(out_probs, 4)))
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    const sv::Scale sp = sv::make_scale((double)temperature);
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
+    // K = 0: each row is its own "sequence" whose only row is drawn from, u[n] the draw
+    hipError_t e = sv::launch_sampling(ln, ctx->ws, sv::SAMPLING, dtype, N, 0, V, sp, sp, logits,
+                                       nullptr, nullptr, uniforms, nullptr, out_tokens, nullptr,
+                                       out_probs);
+    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_TAIL));
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
+                                int H, int V, const void *logits, const int32_t *proposals,
+                                int32_t *accepted_len, int32_t *out_tokens,
+                                int32_t *next_proposals)
+{
+    int rc = check_common(ctx, dtype, B, K, V);
+    if (rc != SPECVERIFY_OK)
+        return rc;
+    if (H < 1)
+        return SPECVERIFY_EINVAL;
+    if (B == 0)
+        return SPECVERIFY_OK;
+    if (!logits || !accepted_len || !out_tokens || (K > 0 && !proposals) ||
+        (H > 1 && !next_proposals))
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(logits, es) || (proposals && !aligned_to(proposals, 4)) ||
+        !aligned_to(accepted_len, 4) || !aligned_to(out_tokens, 4) ||
+        (next_proposals && !aligned_to(next_proposals, 4)))
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
+    hipError_t e = sv::launch_greedy_heads(ln, ctx->ws, dtype, B, K, H, V, logits, proposals,
+                                           accepted_len, out_tokens, next_proposals);
+    note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N, float alpha,
+                            const float *scores, float *r_cut, uint8_t *keep, int32_t *n_keep)
+{
+    if (!ctx)
+        return SPECVERIFY_EINVAL;
+    if (P < 0 || N < 1 || !(alpha >= 0.0f && alpha <= 1.0f))
+        return SPECVERIFY_EINVAL;
+    if (N > SPECVERIFY_MAX_CUT_N)
+        return SPECVERIFY_ECAPACITY;
+    if (P == 0)
+        return SPECVERIFY_OK;
+    if (!scores || !r_cut || !keep || !n_keep)
+        return SPECVERIFY_EINVAL;
+    if (!aligned_to(scores, 4) || !aligned_to(r_cut, 4) || !aligned_to(n_keep, 4))
+        return SPECVERIFY_EINVAL;
+    // the number of responses cut, floor(alpha * N), taken once in double on the host
+    long k = (long)floor((double)alpha * (double)N);
+    if (k > N - 1)
+        k = N - 1;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
+    hipError_t e = sv::launch_quantile_cut(ln, P, N, (int)k, scores, r_cut, keep, n_keep);
+    note_call(ctx, ev, 1u << sv::KIND_CUT);
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 

@@ -28,6 +28,7 @@ constexpr int TAIL_WAVES = TAIL_WG / 64;
 constexpr int NV_TAIL = 2;
 constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the accept phase
 constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
+constexpr int MAX_CUT_N = 8192;       // scores per prompt of the quantile cut (32 KiB of LDS)
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
@@ -69,7 +70,8 @@ struct SeqInfo {
     int L;           // first rejected position, K if none, -1 for bad ids
     float Rp, Rq;
     float isp, isq;
-    int pad[3];
+    float Mp;        // maximum and sum of the target row L, for the drawn id's probability
+    double Sp;
 };
 
 enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };
@@ -90,13 +92,28 @@ enum Kind {
     KIND_TAIL = 1,
     KIND_ARGMAX = 2,
     KIND_GREEDY_EMIT = 3,
-    NUM_KINDS = 4
+    KIND_CUT = 4,
+    NUM_KINDS = 5
 };
 
+// Sampling or contrastive verify (mode), or, with K = 0, acc_len = NULL and draw_probs set,
+// one draw per row (the draft-token sampler).  draw_probs [B]: the drawn token's probability
+// under the target law p_L (sampling mode only; may be NULL).
 hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,
                            int K, int V, const Scale &sp, const Scale &sq, const void *tgt,
                            const void *drf, const int32_t *tokens, const float *unif,
-                           int32_t *acc_len, int32_t *out_tokens, float *out_probs);
+                           int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                           float *draw_probs);
+
+// greedy verify over [B][K+1][H][V] head logits (head 0 verifies) plus next_props [B][H-1],
+// the first argmaxes of heads 1..H-1 at the emitted position
+hipError_t launch_greedy_heads(const Launch &ln, const Workspace &ws, int dtype, int B, int K,
+                               int H, int V, const void *logits, const int32_t *props,
+                               int32_t *acc_len, int32_t *out_tokens, int32_t *next_props);
+
+// per prompt of N scores: r_cut = the (k+1)-th smallest, keep = score >= r_cut, n_keep
+hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const float *scores,
+                               float *r_cut, uint8_t *keep, int32_t *n_keep);
 
 hipError_t launch_greedy(const Launch &ln, const Workspace &ws, int dtype, int B, int K, int V,
                          const void *tgt, const int32_t *props, int32_t *acc_len,

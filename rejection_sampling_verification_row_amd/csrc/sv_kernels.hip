@@ -381,7 +381,8 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
             out_probs[((size_t)b * K + lane) * 2 + 1] = NAN;
         }
         if (lane == 0) {
-            acc_len[b] = -1;
+            if (acc_len)
+                acc_len[b] = -1;
             SeqInfo si = {};
             si.L = -1;
             *info = si;
@@ -405,10 +406,13 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
     else if (lane > L && lane <= K)
         ot[lane] = -1;
     if (lane == 0) {
-        acc_len[b] = L;
+        if (acc_len)
+            acc_len[b] = L;
         SeqInfo si = {};
         si.L = L;
         const float Mp = sM[L];
+        si.Mp = Mp;
+        si.Sp = sS[L];
         si.Rp = Mp * sp.hi;
         const float ep = __builtin_fmaf(Mp, sp.lo, __builtin_fmaf(Mp, sp.hi, -si.Rp));
         si.isp = (float)(exp2(-(double)ep) / sS[L]);
@@ -716,7 +720,8 @@ __device__ inline int find_unit(F unit, int nu, float u01, double *base, double 
 template <int DT, int MODE>
 __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si, int V, int unit,
                                             double base, double tt, bool fb, bool target_law,
-                                            const Scale &sp, const Scale &sq, int32_t *out)
+                                            const Scale &sp, const Scale &sq, int32_t *out,
+                                            float *out_prob)
 {
     constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
     const int lane = threadIdx.x & 63;
@@ -740,8 +745,11 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
     const unsigned long long hit = __ballot(!fb && vsum > 0.0f && bt + (double)vsum > tt);
     const unsigned long long pos = __ballot(vsum > 0.0f);
     if (pos == 0) {  // the unit's total is a sum of these vector sums, so this is not reached
-        if (lane == 0)
+        if (lane == 0) {
             *out = -1;
+            if (out_prob)
+                *out_prob = NAN;
+        }
         return;
     }
     const bool fb2 = fb || hit == 0;
@@ -760,7 +768,12 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
         }
     }
     // rounding may put t past this vector's ids: then its last id of positive weight
-    *out = (y >= 0) ? y : lastpos;
+    const int id = (y >= 0) ? y : lastpos;
+    *out = id;
+    if (MODE == SAMPLING && out_prob)  // p_L(id) in fp64 from the row's merged statistics
+        *out_prob = (float)(exp(((double)Elt<DT>::one(r.p0, (size_t)id) - (double)si.Mp) *
+                                sp.inv_t) /
+                            si.Sp);
 }
 
 // One 1024-thread workgroup per sequence, after the row statistics: the accept phase
@@ -776,7 +789,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
                                                   int nch, Scale sp, Scale sq,
                                                   const float2 *__restrict__ part,
                                                   int32_t *acc_len, int32_t *out_tokens,
-                                                  float *out_probs)
+                                                  float *out_probs, float *draw_probs)
 {
     extern __shared__ double dyn[];
     __shared__ SeqInfo s_info;
@@ -795,6 +808,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
     const int nit = (V + CE - 1) / CE, nu = nit * NV_TAIL * TAIL_WAVES;
     const float u01 = unif[(size_t)b * (K + 1) + K];
     int32_t *out = out_tokens + (size_t)b * (K + 1) + si.L;
+    float *out_prob = draw_probs ? draw_probs + b : nullptr;
     double *units = dyn;
     for (int pass = 0; pass < 2; ++pass) {
         const bool target_law = (pass == 1);
@@ -816,25 +830,29 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
         if (us >= 0) {
             if (w == 0)
                 search_unit<DT, MODE>(r, si, V, us, s_base, s_t, s_fb != 0, target_law, sp, sq,
-                                      out);
+                                      out, out_prob);
             return;
         }
         // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
     }
-    if (t == 0)
-        *out = -1;  // a row without finite logits: outside the contract
+    if (t == 0) {  // a row without finite logits: outside the contract
+        *out = -1;
+        if (out_prob)
+            *out_prob = NAN;
+    }
 }
 
 // ------------------------------------------------------------------ greedy blockwise
 
-// per chunk of a row: (max, first id of the max) per wave
+// per chunk of a row: (max, first id of the max) per wave.  Logical row r is stored at row
+// r * row_stride of the input (1 for [B][K+1][V]; H to take head 0 of [B][K+1][H][V]).
 template <int DT>
 __global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int V, int nch,
-                                               float2 *part)
+                                               int row_stride, float2 *part)
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
     const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
-    const char *rp = tgt + (size_t)row * (size_t)V * BY;
+    const char *rp = tgt + (size_t)row * row_stride * (size_t)V * BY;
     const int cbase = c * WG * NV_ARGMAX * E;
     float x[NV_ARGMAX][E];
     load_chunk<DT, NV_ARGMAX>(rp, aligned16(rp), cbase, V, x);
@@ -897,6 +915,211 @@ __global__ __launch_bounds__(WG) void k_greedy_final(const int32_t *__restrict__
         acc_len[b] = L;
 }
 
+// (max, first id) of one whole row, across the workgroup: thread t takes vectors t,
+// t + TAIL_WG, ... (ascending ids per thread, so a strict '>' keeps the first maximum), then
+// the waves and the workgroup merge by value, then lowest id.  Every thread returns the row's
+// first argmax.  An all -inf row gives id 0.
+template <int DT>
+__device__ inline int block_row_argmax(const char *rp, int V)
+{
+    constexpr int E = Elt<DT>::EPV;
+    __shared__ float s_v[TAIL_WAVES];
+    __shared__ int s_i[TAIL_WAVES];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const bool al = aligned16(rp);
+    float bv = -INFINITY;
+    int bi = (t * E < V) ? t * E : INT_MAX;
+#pragma unroll 4
+    for (int e0 = t * E; e0 < V; e0 += TAIL_WG * E) {
+        float x[E];
+        load_elems<DT>(rp, al, e0, V, -INFINITY, x);
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if (x[k] > bv) {
+                bv = x[k];
+                bi = e0 + k;
+            }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+        s_v[w] = bv;
+        s_i[w] = bi;
+    }
+    __syncthreads();
+    float v = s_v[0];
+    int id = s_i[0];
+    for (int k = 1; k < TAIL_WAVES; ++k)
+        take_better(v, id, s_v[k], s_i[k]);
+    __syncthreads();  // s_v / s_i may be reused by the next call
+    return id;
+}
+
+// Greedy blockwise verify with the next block's proposals (one 1024-thread workgroup per
+// sequence): head 0's row argmaxes g_j from k_argmax's partials, the longest matching prefix
+// L, the emitted g_0..g_L, then the first argmax of each of heads 1..H-1 at position L (rows
+// ((b*(K+1) + L)*H + h) of the input), the next block's proposals.
+template <int DT>
+__global__ __launch_bounds__(TAIL_WG) void k_greedy_heads(const char *__restrict__ logits,
+                                                          const int32_t *__restrict__ props,
+                                                          int K, int H, int V, int nch,
+                                                          const float2 *__restrict__ part,
+                                                          int32_t *acc_len, int32_t *out_tokens,
+                                                          int32_t *next_props)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    __shared__ int sg[64];
+    __shared__ int s_L;
+    const int b = blockIdx.x, P = K + 1;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, np = nch * WAVES;
+    for (int j = w; j < P; j += TAIL_WAVES) {
+        const float2 *pr = part + ((size_t)b * P + j) * np;
+        float v = -INFINITY;
+        int id = INT_MAX;
+        for (int i = lane; i < np; i += 64) {
+            const float2 e = pr[i];
+            take_better(v, id, e.x, __float_as_int(e.y));
+        }
+        wave_argmax(v, id);
+        if (lane == 0)
+            sg[j] = id;
+    }
+    __syncthreads();
+    if (w == 0) {
+        const int32_t xp = (lane < K) ? props[(size_t)b * K + lane] : 0;
+        const bool bad = (lane < K) && (xp < 0 || xp >= V);
+        int32_t *ot = out_tokens + (size_t)b * (K + 1);
+        if (__ballot(bad) != 0) {
+            if (lane <= K)
+                ot[lane] = -1;
+            if (lane == 0) {
+                acc_len[b] = -1;
+                s_L = -1;
+            }
+        } else {
+            const unsigned long long mm = __ballot(lane < K && xp != sg[lane]);
+            const int L = mm ? __builtin_ctzll(mm) : K;
+            if (lane <= K)
+                ot[lane] = (lane <= L) ? sg[lane] : -1;
+            if (lane == 0) {
+                acc_len[b] = L;
+                s_L = L;
+            }
+        }
+    }
+    __syncthreads();
+    const int L = s_L;
+    if (H < 2)
+        return;
+    int32_t *nx = next_props + (size_t)b * (H - 1);
+    if (L < 0) {
+        for (int h = t + 1; h < H; h += TAIL_WG)
+            nx[h - 1] = -1;
+        return;
+    }
+    for (int h = 1; h < H; ++h) {
+        const char *rp = logits + (((size_t)b * P + L) * H + h) * (size_t)V * BY;
+        const int id = block_row_argmax<DT>(rp, V);
+        if (t == 0)
+            nx[h - 1] = id;
+    }
+}
+
+// ------------------------------------------------------------------ alpha-quantile cut
+
+// float -> uint32 with the same order (negative floats flipped, positive ones offset)
+__device__ inline uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float key_to_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// One 1024-thread workgroup per prompt: r_cut = the (k+1)-th smallest of its N scores
+// (radix selection on order keys in LDS, one byte per pass from the top), keep[i] =
+// (score_i >= r_cut), n_keep = the count.  Comparisons only, so exact.
+__global__ __launch_bounds__(TAIL_WG) void k_quantile_cut(const float *__restrict__ scores, int N,
+                                                          int k, float *r_cut, uint8_t *keep,
+                                                          int32_t *n_keep)
+{
+    extern __shared__ uint32_t keys[];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_prefix, s_rank;
+    __shared__ int s_cnt[TAIL_WAVES];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const float *row = scores + (size_t)blockIdx.x * N;
+    for (int i = t; i < N; i += TAIL_WG)
+        keys[i] = order_key(row[i]);
+    uint32_t prefix = 0, mask = 0, rank = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (t < 256)
+            hist[t] = 0;
+        __syncthreads();
+        for (int i = t; i < N; i += TAIL_WG) {
+            const uint32_t key = keys[i];
+            if ((key & mask) == prefix)
+                atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (w == 0) {  // lane l owns bins 4l..4l+3: find the bin holding the rank-th key
+            uint32_t c[4], sum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[4 * lane + q];
+                sum += c[q];
+            }
+            uint32_t inc = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t n = __shfl_up(inc, o);
+                if (lane >= o)
+                    inc += n;
+            }
+            const uint32_t exc = inc - sum;
+            const unsigned long long hit = __ballot(inc > rank);
+            const int l = __builtin_ctzll(hit);  // the keys left hold rank, so some lane hits
+            if (lane == l) {
+                uint32_t below = exc;
+                int q = 0;
+                while (q < 3 && below + c[q] <= rank) {
+                    below += c[q];
+                    ++q;
+                }
+                s_rank = rank - below;
+                s_prefix = prefix | ((uint32_t)(4 * l + q) << shift);
+            }
+        }
+        __syncthreads();
+        rank = s_rank;
+        prefix = s_prefix;
+        mask |= 0xffu << shift;
+        __syncthreads();  // everyone has read s_rank / s_prefix before the next pass
+    }
+    const float cut = key_to_float(prefix);
+    int cnt = 0;
+    for (int i = t; i < N; i += TAIL_WG) {
+        const bool kk = row[i] >= cut;
+        keep[(size_t)blockIdx.x * N + i] = kk ? 1 : 0;
+        cnt += kk;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        cnt += __shfl_xor(cnt, o);
+    if (lane == 0)
+        s_cnt[w] = cnt;
+    __syncthreads();
+    if (t == 0) {
+        int total = 0;
+        for (int q = 0; q < TAIL_WAVES; ++q)
+            total += s_cnt[q];
+        n_keep[blockIdx.x] = total;
+        r_cut[blockIdx.x] = cut;
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 namespace {
@@ -921,7 +1144,7 @@ template <int DT, int MODE>
 hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, int V,
                          const Scale &sp, const Scale &sq, const void *tgt, const void *drf,
                          const int32_t *tokens, const float *unif, int32_t *acc_len,
-                         int32_t *out_tokens, float *out_probs)
+                         int32_t *out_tokens, float *out_probs, float *draw_probs)
 {
     const char *t = static_cast<const char *>(tgt);
     const char *d = static_cast<const char *>(drf);
@@ -942,7 +1165,7 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
         Timer tm(ln, KIND_TAIL);
         hipLaunchKernelGGL((k_tail<DT, MODE>), dim3(B), dim3(TAIL_WG),
                            tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
-                           sp, sq, ws.part, acc_len, out_tokens, out_probs);
+                           sp, sq, ws.part, acc_len, out_tokens, out_probs, draw_probs);
     }
     return hipGetLastError();
 }
@@ -956,7 +1179,7 @@ hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int 
         Timer tm(ln, KIND_ARGMAX);
         const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
         hipLaunchKernelGGL(k_argmax<DT>, dim3(grid), dim3(WG), 0, ln.stream,
-                           static_cast<const char *>(tgt), V, nch, ws.part);
+                           static_cast<const char *>(tgt), V, nch, 1, ws.part);
     }
     {
         Timer tm(ln, KIND_GREEDY_EMIT);
@@ -966,22 +1189,57 @@ hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int 
     return hipGetLastError();
 }
 
+template <int DT>
+hipError_t greedy_heads_impl(const Launch &ln, const Workspace &ws, int B, int K, int H, int V,
+                             const void *logits, const int32_t *props, int32_t *acc_len,
+                             int32_t *out_tokens, int32_t *next_props)
+{
+    const int nch = num_chunks(NV_ARGMAX, DT, V);
+    const char *lg = static_cast<const char *>(logits);
+    {
+        Timer tm(ln, KIND_ARGMAX);
+        const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
+        hipLaunchKernelGGL(k_argmax<DT>, dim3(grid), dim3(WG), 0, ln.stream, lg, V, nch, H,
+                           ws.part);
+    }
+    {
+        Timer tm(ln, KIND_GREEDY_EMIT);
+        hipLaunchKernelGGL(k_greedy_heads<DT>, dim3(B), dim3(TAIL_WG), 0, ln.stream, lg, props, K,
+                           H, V, nch, ws.part, acc_len, out_tokens, next_props);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_greedy_heads(const Launch &ln, const Workspace &ws, int dtype, int B, int K,
+                               int H, int V, const void *logits, const int32_t *props,
+                               int32_t *acc_len, int32_t *out_tokens, int32_t *next_props)
+{
+    auto f = dtype == 1 ? greedy_heads_impl<1> : greedy_heads_impl<0>;
+    return f(ln, ws, B, K, H, V, logits, props, acc_len, out_tokens, next_props);
+}
+
+hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const float *scores,
+                               float *r_cut, uint8_t *keep, int32_t *n_keep)
+{
+    Timer tm(ln, KIND_CUT);
+    hipLaunchKernelGGL(k_quantile_cut, dim3(P), dim3(TAIL_WG), (size_t)N * sizeof(uint32_t),
+                       ln.stream, scores, N, k, r_cut, keep, n_keep);
+    return hipGetLastError();
+}
 
 hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,
                            int K, int V, const Scale &sp, const Scale &sq, const void *tgt,
                            const void *drf, const int32_t *tokens, const float *unif,
-                           int32_t *acc_len, int32_t *out_tokens, float *out_probs)
+                           int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                           float *draw_probs)
 {
-    if (mode == SAMPLING)
-        return dtype == 1 ? sampling_impl<1, SAMPLING>(ln, ws, B, K, V, sp, sq, tgt, drf, tokens,
-                                                       unif, acc_len, out_tokens, out_probs)
-                          : sampling_impl<0, SAMPLING>(ln, ws, B, K, V, sp, sq, tgt, drf, tokens,
-                                                       unif, acc_len, out_tokens, out_probs);
-    return dtype == 1 ? sampling_impl<1, CONTRASTIVE>(ln, ws, B, K, V, sp, sq, tgt, drf, tokens,
-                                                      unif, acc_len, out_tokens, out_probs)
-                      : sampling_impl<0, CONTRASTIVE>(ln, ws, B, K, V, sp, sq, tgt, drf, tokens,
-                                                      unif, acc_len, out_tokens, out_probs);
+    auto f = (mode == SAMPLING) ? (dtype == 1 ? sampling_impl<1, SAMPLING> : sampling_impl<0, SAMPLING>)
+                                : (dtype == 1 ? sampling_impl<1, CONTRASTIVE>
+                                              : sampling_impl<0, CONTRASTIVE>);
+    return f(ln, ws, B, K, V, sp, sq, tgt, drf, tokens, unif, acc_len, out_tokens, out_probs,
+             draw_probs);
 }
 
 hipError_t launch_greedy(const Launch &ln, const Workspace &ws, int dtype, int B, int K, int V,

@@ -38,6 +38,8 @@ DTYPE_NAMES = {F32: "f32", BF16: "bf16"}
 SAMPLING = "sampling"
 GREEDY = "greedy"
 CONTRASTIVE = "contrastive"
+SAMPLE = "sample"              # draft-token sampler: one draw per row
+GREEDY_HEADS = "greedy_heads"  # greedy verify over [B][K+1][H][V] head logits
 
 _U_BITS = 23
 _U_SCALE = 2.0 ** -_U_BITS
@@ -288,6 +290,68 @@ def make_contrastive(B: int, K: int, V: int, dtype: int, tau: float, seed: int, 
                     tokens=np.ascontiguousarray(tokens.reshape(B, K)), uniforms=uniforms, seed=seed)
 
 
+def make_sampler(N: int, V: int, dtype: int, temperature: float, seed: int, *,
+                 sigma: float = 4.0, n_peaks: int = 0, peak_height: float = 8.0,
+                 name: str = "sample") -> Workload:
+    """Draft-token sampler workload: N rows l ~ N(0, sigma^2) plus ``peak_height`` at
+    ``n_peaks`` distinct positions per row, one lattice uniform per row.  Stored as a
+    Workload with K = 0 (``target`` holds the rows, ``uniforms`` is [N][1])."""
+    s_logits, _s_noise, s_peaks, _s_tokens, s_unif = _streams(seed)
+    t = normal_rows(s_logits, N, V, sigma)
+    if n_peaks:
+        rng = np.random.Generator(np.random.PCG64(s_peaks))
+        pos = _distinct_positions(rng, N, n_peaks, V)
+        t[np.repeat(np.arange(N), n_peaks), pos.reshape(-1)] += np.float32(peak_height)
+    logits = _store(t, dtype)
+    del t
+    uniforms = lattice_uniforms(np.random.Generator(np.random.PCG64(s_unif)), (N, 1))
+    return Workload(name=name, mode=SAMPLE, dtype=dtype, B=N, K=0, V=V,
+                    temperature=_f32(temperature), target=logits, draft=None,
+                    tokens=np.zeros((N, 0), np.int32), uniforms=uniforms, seed=seed)
+
+
+def make_greedy_heads(B: int, K: int, H: int, V: int, dtype: int, seed: int, *,
+                      sigma: float = 4.0, match_prob: float = 0.7,
+                      name: str = "greedy_heads") -> Workload:
+    """Greedy verify with H heads: logits [B][K+1][H][V] ~ N(0, sigma^2); proposal j equals
+    head 0's first maximum at position j with probability ``match_prob``, else a uniformly
+    chosen other id.  ``meta["H"]`` holds H."""
+    s_logits, _s_noise, _s_peaks, s_tokens, _s_unif = _streams(seed)
+    t = normal_rows(s_logits, B * (K + 1) * H, V, sigma).reshape(B, K + 1, H, V)
+    logits = _store(t, dtype)
+    del t
+    top = np.argmax(decode(logits[:, :K, 0, :], dtype), axis=2)  # first occurrence
+    rng = np.random.Generator(np.random.PCG64(s_tokens))
+    match = rng.random((B, K)) < match_prob
+    r = rng.integers(0, max(V - 1, 1), size=(B, K), dtype=np.int64)
+    other = top if V == 1 else r + (r >= top)
+    props = np.where(match, top, other).astype(np.int32)
+    return Workload(name=name, mode=GREEDY_HEADS, dtype=dtype, B=B, K=K, V=V, temperature=1.0,
+                    target=logits, draft=None, tokens=np.ascontiguousarray(props),
+                    uniforms=None, seed=seed, meta={"H": H})
+
+
+@dataclass
+class CutWorkload:
+    """P prompts with N partial-reward scores each, and the cut fraction alpha."""
+    name: str
+    P: int
+    N: int
+    alpha: float
+    scores: np.ndarray  # float32 [P][N]
+    seed: int = 0
+
+
+def make_cut(P: int, N: int, alpha: float, seed: int, *, grid: float = 2.0 ** -8,
+             name: str = "cut") -> CutWorkload:
+    """Scores ~ N(0, 1) rounded to multiples of ``grid`` (reward scores with ties)."""
+    s_scores = _streams(seed)[0]
+    x = np.random.Generator(np.random.PCG64(s_scores)).standard_normal((P, N))
+    scores = (np.round(x / grid) * grid).astype(np.float32)
+    return CutWorkload(name=name, P=P, N=N, alpha=float(np.float32(alpha)), scores=scores,
+                       seed=seed)
+
+
 # The five named workloads. Each takes an optional batch override so that tests can
 # run the same distributions at a smaller B; the default is the full size.
 def c1_sampling_tiny(B: int = 1, seed: int = 1001) -> Workload:
@@ -328,4 +392,31 @@ CONFIGS = {
     "c3": c3_sampling_large_vocab,
     "c4": c4_greedy_blockwise,
     "c5": c5_contrastive,
+}
+
+
+# Workloads of the operations next to the verify step, at the shapes of their neighbours.
+def sampler_draft_rows(N: int = 256, seed: int = 1006) -> Workload:
+    """One drafting step of 256 sequences: N=256 rows, V=128256 bf16, T=0.7, rows shaped
+    like the large-vocabulary target rows (N(0,4^2) + 8 at 20 positions)."""
+    return make_sampler(N, 128256, BF16, 0.7, seed, sigma=4.0, n_peaks=20,
+                        name="sampler N=%d V=128256 bf16 T=0.7" % N)
+
+
+def greedy_heads_blockwise(B: int = 512, seed: int = 1007) -> Workload:
+    """Blockwise decoding with merged predict/verify: B=512, K=4 proposals, H=4 heads,
+    V=32000 bf16, l ~N(0,4^2), proposals match head 0's argmax w.p. 0.7."""
+    return make_greedy_heads(B, 4, 4, 32000, BF16, seed, sigma=4.0, match_prob=0.7,
+                             name="greedy-heads B=%d K=4 H=4 V=32000 bf16" % B)
+
+
+def cut_best_of_n(P: int = 128, seed: int = 1008) -> CutWorkload:
+    """P=128 prompts with N=1000 partial-reward scores each, alpha=0.5."""
+    return make_cut(P, 1000, 0.5, seed, name="cut P=%d N=1000 alpha=0.5" % P)
+
+
+NEXT_CONFIGS = {
+    "sample": sampler_draft_rows,
+    "heads": greedy_heads_blockwise,
+    "cut": cut_best_of_n,
 }

@@ -129,3 +129,59 @@ def compare(w, g: GpuOut, o: oracle.Result, seqs=None) -> Report:
             tol = PROB_RTOL * np.maximum(np.abs(gp), np.abs(op)) + 1e-30
             assert np.all(np.abs(gp - op) <= tol), (b, gp, op)
     return rep
+
+
+# ----------------------------------------------------------------- the operations next to it
+
+def run_sample(ctx: int, w, misalign: int = 0, with_probs: bool = True):
+    put = (lambda a: dev_offset(a, misalign)) if misalign else dev
+    N = w.B
+    tok = torch.full((N,), -7, dtype=torch.int32, device="cuda")
+    pr = torch.full((N,), -7.0, dtype=torch.float32, device="cuda") if with_probs else None
+    sv.specverify_sample(ctx, None, w.dtype, N, w.V, w.temperature, put(w.target),
+                         dev(w.uniforms.reshape(N)), tok, pr)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), None if pr is None else pr.cpu().numpy()
+
+
+def compare_sample(w, tok, pr, o) -> Report:
+    """Sampler parity: ids bit-exact where the oracle's draw margin is >= 1e-6, else the
+    oracle's id or the one across the near edge; probabilities to 1e-5 relative."""
+    rep = Report(n=w.B)
+    for n in range(w.B):
+        if o.margin[n] >= LOW:
+            assert tok[n] == o.tokens[n], (n, tok[n], o.tokens[n], o.margin[n])
+            rep.exact += 1
+        else:
+            rep.low_draw += 1
+            assert tok[n] in (o.tokens[n], o.alt_token[n]), (n, tok[n], o.tokens[n], o.alt_token[n])
+            rep.low_draw_same += int(tok[n] == o.tokens[n])
+    if pr is not None:
+        # the probability of the id actually drawn
+        for n in range(w.B):
+            if tok[n] == o.tokens[n]:
+                a, b = float(pr[n]), float(o.probs[n])
+                assert abs(a - b) <= PROB_RTOL * max(abs(a), abs(b)) + 1e-30, (n, a, b)
+    return rep
+
+
+def run_heads(ctx: int, w, misalign: int = 0):
+    put = (lambda a: dev_offset(a, misalign)) if misalign else dev
+    B, K, H = w.B, w.K, w.meta["H"]
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    tok = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+    nxt = torch.full((B, max(H - 1, 1)), -7, dtype=torch.int32, device="cuda")
+    sv.specverify_run_greedy_heads(ctx, None, w.dtype, B, K, H, w.V, put(w.target), dev(w.tokens),
+                                   acc, tok, nxt if H > 1 else None)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), tok.cpu().numpy(), nxt.cpu().numpy()[:, :H - 1]
+
+
+def run_cut(ctx: int, P: int, N: int, alpha: float, scores: np.ndarray, misalign: int = 0):
+    s = dev_offset(scores, misalign) if misalign else dev(scores)
+    cut = torch.full((P,), -7.0, dtype=torch.float32, device="cuda")
+    keep = torch.full((P, N), 7, dtype=torch.uint8, device="cuda")
+    n = torch.full((P,), -7, dtype=torch.int32, device="cuda")
+    sv.specverify_quantile_cut(ctx, None, P, N, alpha, s, cut, keep, n)
+    torch.cuda.synchronize()
+    return cut.cpu().numpy(), keep.cpu().numpy().astype(bool), n.cpu().numpy()
