@@ -13,8 +13,9 @@ bytes/s against the 8 TB/s HBM peak (timed with HIP events on the call's stream 
 kernel only), and the fp64 CPU oracle timed on a bounded sample of the same batch.
 
 --workload names one of the other synthetic workloads (the tiny and mid-size sampling ones,
-greedy blockwise, contrastive) to measure its path the same way; the default is the one the
-headline metric is quoted on.
+greedy blockwise, contrastive, and the operations next to the verify step: the draft-token
+sampler, greedy verify with the next block's proposals, the alpha-quantile cut) to measure
+its path the same way; the default is the one the headline metric is quoted on.
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_row_amd", "csrc", "sv_kernels.hip")
 
-# workload key -> (description, dominant kernel kind, its kernel name, traffic summary file)
+# workload key -> (description, timed kernel kind, its kernel name, traffic summary file)
 WORKLOADS = {
     "c3": ("sampling verify B=256 K=8 V=128256 bf16 logits T=0.7", "row_stats",
            "k_stats_sampling<bf16>", "row_stats_bf16_B256_K8_V128256_traffic.md"),
@@ -44,6 +45,12 @@ WORKLOADS = {
            "k_argmax<bf16>", "row_argmax_bf16_B512_K8_V32000_traffic.md"),
     "c5": ("contrastive verify B=128 K=4 V=152064 bf16 logits tau=1", "row_stats",
            "k_stats_contrastive<bf16>", "contrastive_stats_bf16_B128_K4_V152064_traffic.md"),
+    "sample": ("draft-token sampler N=256 V=128256 bf16 logits T=0.7", "accept_draw",
+               "k_tail<bf16> (draw: one re-read of every row)", None),
+    "heads": ("greedy verify with next-block proposals B=512 K=4 H=4 V=32000 bf16 logits",
+              "row_argmax", "k_argmax<bf16> (head 0 rows)", None),
+    "cut": ("alpha-quantile cut P=128 N=1000 alpha=0.5 f32 scores", "quantile_cut",
+            "k_quantile_cut", None),
 }
 METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
@@ -88,10 +95,13 @@ def cpu_baseline(w, seconds: float):
         oracle.run_workload(w.subset([done]))
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": done * w.K / dt, "unit": "verified draft positions/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "first %d of the %d sequences of the same batch, one at a time, %.1f s "
-                      "single-threaded fp64 C" % (done, w.B, dt)}
+    if w.mode == "sample":
+        value, unit, what = done / dt, "sampled tokens/s", "rows"
+    else:
+        value, unit, what = done * w.K / dt, "verified draft positions/s", "sequences"
+    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": "first %d of the %d %s of the same batch, one at a time, %.1f s "
+                      "single-threaded fp64 C" % (done, w.B, what, dt)}
 
 
 def main():
@@ -122,7 +132,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     desc, kind, kname, traffic_file = WORKLOADS[args.workload]
-    w = synth.CONFIGS[args.workload]()
+    if args.workload == "cut":
+        return bench_cut(args, desc, kind, kname)
+    w = (synth.CONFIGS.get(args.workload) or synth.NEXT_CONFIGS[args.workload])()
     B, K, V = w.B, w.K, w.V
     log("generated %s (seed %d); uploading %.3f GB of logits x2"
         % (desc, w.seed, w.logit_bytes / 1e9))
@@ -139,12 +151,20 @@ def main():
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
     out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
     probs = torch.empty((B, K, 2), dtype=torch.float32, device="cuda")
+    H = w.meta.get("H", 1)
+    nxt = torch.empty((B, max(H - 1, 1)), dtype=torch.int32, device="cuda")
+    draw_p = torch.empty(B, dtype=torch.float32, device="cuda")
     ctx = sv.specverify_create(0, B, K, V)
     stream = torch.cuda.current_stream()
 
     def step(i):
         tg, dr = copies[i & 1]
-        if w.mode == synth.GREEDY:
+        if w.mode == synth.SAMPLE:
+            sv.specverify_sample(ctx, stream, w.dtype, B, V, w.temperature, tg, unif, out, draw_p)
+        elif w.mode == synth.GREEDY_HEADS:
+            sv.specverify_run_greedy_heads(ctx, stream, w.dtype, B, K, H, V, tg, toks, acc, out,
+                                           nxt)
+        elif w.mode == synth.GREEDY:
             sv.specverify_run_greedy(ctx, stream, w.dtype, B, K, V, tg, toks, acc, out)
         elif w.mode == synth.CONTRASTIVE:
             sv.specverify_run_contrastive(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
@@ -185,18 +205,29 @@ def main():
     sv.specverify_destroy(ctx)
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    positions = B * K / (ms_step * 1e-3)
     kern_ms = kms[kind] / max(kn[kind], 1)
     logit_bytes = w.logit_bytes                      # one read of every logit row
+    if w.mode == synth.SAMPLE:
+        positions = B / (ms_step * 1e-3)             # tokens drawn per second
+        unit = "sampled tokens/s"
+        kern_bytes = logit_bytes                     # the draw re-reads every row once
+    elif w.mode == synth.GREEDY_HEADS:
+        positions = B * K / (ms_step * 1e-3)
+        unit = "verified draft positions/s"
+        kern_bytes = logit_bytes // H                # head 0's rows
+    else:
+        positions = B * K / (ms_step * 1e-3)
+        unit = "verified draft positions/s"
+        kern_bytes = logit_bytes
     call_bytes = logit_bytes + w.tokens.nbytes + acc.nbytes + out.nbytes
     if w.uniforms is not None:
         call_bytes += w.uniforms.nbytes
-    achieved = logit_bytes / (kern_ms * 1e-3) / 1e9
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC if args.workload == "c3"
-        else "verified draft positions/s + HBM GB/s vs peak, " + desc,
+        else "%s + HBM GB/s vs peak, %s" % (unit, desc),
         "value": positions,
-        "unit": "verified draft positions/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -214,13 +245,78 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(traffic_file),
-                     "kernel": kname, "algorithmic_bytes": logit_bytes, "avg_ms": kern_ms},
+                     "kernel": kname, "algorithmic_bytes": kern_bytes, "avg_ms": kern_ms},
         "kernels_ms_per_step": {k: bms[k] / bn[k] for k in bms if bn[k]},
-        "mean_accepted_len": mean_L,
+        "mean_accepted_len": mean_L if w.mode != synth.SAMPLE else None,
     }
     if args.cpu_seconds > 0:
         log("CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def bench_cut(args, desc, kind, kname):
+    """The alpha-quantile cut: P prompts x N scores per call; value = prompts cut per second."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verification_row_amd import binding as sv
+    from rejection_sampling_verification_row_amd import synth
+
+    w = synth.NEXT_CONFIGS["cut"]()
+    P, N = w.P, w.N
+    s = [torch.from_numpy(w.scores).to("cuda") for _ in range(2)]
+    cut = torch.empty(P, dtype=torch.float32, device="cuda")
+    keep = torch.empty((P, N), dtype=torch.uint8, device="cuda")
+    n = torch.empty(P, dtype=torch.int32, device="cuda")
+    ctx = sv.specverify_create(0, 1, 0, 1)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        sv.specverify_quantile_cut(ctx, stream, P, N, w.alpha, s[i & 1], cut, keep, n)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sv.specverify_profile_begin(ctx, args.steps, [kind])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms, kn = sv.specverify_profile_end(ctx)
+    sv.specverify_destroy(ctx)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = kms[kind] / max(kn[kind], 1)
+    nbytes = P * N * 4 + P * N + P * 8               # scores in; keep bytes, cut and count out
+    res = {
+        "metric": "prompts cut/s, " + desc, "value": P / (ms_step * 1e-3),
+        "unit": "prompts/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": desc, "P": P, "N": N, "alpha": w.alpha, "seed": w.seed},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": kname, "algorithmic_bytes": nbytes, "avg_ms": kern_ms,
+                     "note": "latency-bound: one workgroup per prompt, four selection passes"},
+        "mean_kept": float(n.float().mean().item()),
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.build(force=False)
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.cpu_seconds and done < 1000:
+            oracle.quantile_cut(P, N, w.alpha, w.scores)
+            done += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done * P / dt, "unit": "prompts/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "the whole batch %d times, %.1f s single-threaded C"
+                                         % (done, dt)}
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -20,9 +20,10 @@ constexpr int NV_ARGMAX = 8;          // greedy argmax
 constexpr int MAX_ROWS = 2 * 63 + 1;  // rows per sequence at the largest K
 
 // The per-sequence tail (accept scan + draw) runs one 1024-thread workgroup per sequence;
-// its pass over row L loads NV_TAIL vectors per thread per row and iteration (64 KiB per
-// iteration when both rows are read, the next iteration's loads in flight while the current
-// one is weighed) and keeps one fp64 weight sum per wave and vector slot ("unit") in LDS.
+// its pass over row L loads NV_TAIL vectors per thread per row and iteration when the draft
+// row L is read too, 2 * NV_TAIL when only the target row is (64 KiB per iteration either
+// way, the next iteration's loads in flight while the current one is weighed), and keeps one
+// fp64 weight sum per wave and vector slot ("unit") in LDS.
 constexpr int TAIL_WG = 1024;
 constexpr int TAIL_WAVES = TAIL_WG / 64;
 constexpr int NV_TAIL = 2;
@@ -38,10 +39,17 @@ inline int num_chunks(int nv, int dtype, int V)
 }
 // the most chunks any pass needs for a row of V ids (float32 pairs have the smallest chunks)
 inline int max_chunks(int V) { return num_chunks(NV_PAIR, 0, V); }
+// unit sums of one row pass: NV_TAIL vectors per thread and iteration when two rows are read,
+// 2 * NV_TAIL when one is; the LDS holds the larger count
 inline int tail_units(int dtype, int V)
 {
-    const int ce = TAIL_WG * NV_TAIL * elems_per_vec(dtype);
-    return (V + ce - 1) / ce * NV_TAIL * TAIL_WAVES;
+    int most = 0;
+    for (int nv = NV_TAIL; nv <= 2 * NV_TAIL; nv += NV_TAIL) {
+        const int ce = TAIL_WG * nv * elems_per_vec(dtype);
+        const int n = (V + ce - 1) / ce * nv * TAIL_WAVES;
+        most = n > most ? n : most;
+    }
+    return most;
 }
 // dynamic LDS of the tail kernel: the staged partials, then (reusing it) the unit sums
 inline size_t tail_lds_bytes(int dtype, int K, int V, int nch)

@@ -561,8 +561,9 @@ __device__ inline void vec_weights_masked(const DrawRows &r, int e0, int V, bool
     }
 }
 
-// Weights of one whole 16-byte vector from its raw words.
-template <int DT, int MODE>
+// Weights of one whole 16-byte vector from its raw words; TWO: a draft-side vector q is
+// read too (the residual, or the contrastive target's amateur half), else the target law p.
+template <int DT, int MODE, bool TWO>
 __device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint4 &q,
                                    bool target_law, const SeqInfo &si, const Scale &sp,
                                    const Scale &sq, float (&wv)[Elt<DT>::EPV])
@@ -570,40 +571,48 @@ __device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint
     constexpr int E = Elt<DT>::EPV;
     float pv[E], qv[E];
     Elt<DT>::unpack(a, pv);
-    if (r.two)
+    if constexpr (TWO) {
         Elt<DT>::unpack(q, qv);
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-        if (MODE == CONTRASTIVE)
-            pv[k] = pv[k] - qv[k];
-        wv[k] = draw_weight(pv[k], qv[k], r.resid, target_law, si, sp, sq);
+        for (int k = 0; k < E; ++k) {
+            if (MODE == CONTRASTIVE)
+                pv[k] = pv[k] - qv[k];
+            wv[k] = draw_weight(pv[k], qv[k], r.resid, target_law, si, sp, sq);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            wv[k] = draw_weight(pv[k], 0.0f, false, true, si, sp, sq);
     }
 }
 
-// One k_tail iteration covers CE = TAIL_WG * NV_TAIL * E contiguous ids; thread t holds the
-// NV_TAIL vectors base + i*TAIL_WG*E + [0, E), base = the iteration's first id + t*E, so a
-// wave's loads are 1 KiB contiguous.  In an aligned row every vector wholly below V is one
-// streamed 16-byte load per row read (vectors at or past V load nothing).
-template <int DT>
-__device__ inline void tail_load(const DrawRows &r, int base, int V, uint4 (&a)[NV_TAIL],
-                                 uint4 (&q)[NV_TAIL])
+// A k_tail iteration with NV vectors per thread covers CE = TAIL_WG * NV * E contiguous ids;
+// thread t holds the NV vectors base + i*TAIL_WG*E + [0, E), base = the iteration's first id
+// + t*E, so a wave's loads are 1 KiB contiguous.  NV = NV_TAIL when a draft-side row is read
+// as well (TWO), 2 * NV_TAIL when only the target row is: the same bytes in flight either
+// way.  In an aligned row every vector wholly below V is one streamed 16-byte load per row
+// read (vectors at or past V load nothing).
+template <int DT, int NV, bool TWO>
+__device__ inline void tail_load(const DrawRows &r, int base, int V, uint4 (&a)[NV],
+                                 uint4 (&q)[NV])
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = TAIL_WG * Elt<DT>::EPV;
     if (!r.al)
         return;
 #pragma unroll
-    for (int i = 0; i < NV_TAIL; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int e0 = base + i * STRIDE;
         if (e0 + E <= V)
             a[i] = load_stream(r.p0 + (size_t)e0 * BY);
     }
-    if (r.two)
+    if constexpr (TWO) {
 #pragma unroll
-        for (int i = 0; i < NV_TAIL; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const int e0 = base + i * STRIDE;
             if (e0 + E <= V)
                 q[i] = load_stream(r.p1 + (size_t)e0 * BY);
         }
+    }
 }
 
 // The draw-weight sums of this thread's vectors from tail_load (fp32 tree over each vector's
@@ -611,19 +620,18 @@ __device__ inline void tail_load(const DrawRows &r, int base, int V, uint4 (&a)[
 // width), and every vector of an unaligned row, is weighed element by element through
 // vec_weights_masked, which the unit search also uses: every id gets the same weight, bit
 // for bit, in both places.
-template <int DT, int MODE>
+template <int DT, int MODE, int NV, bool TWO>
 __device__ inline void tail_weigh(const DrawRows &r, int base, int V, bool target_law,
                                   const SeqInfo &si, const Scale &sp, const Scale &sq,
-                                  const uint4 (&a)[NV_TAIL], const uint4 (&q)[NV_TAIL],
-                                  float (&vs)[NV_TAIL])
+                                  const uint4 (&a)[NV], const uint4 (&q)[NV], float (&vs)[NV])
 {
     constexpr int E = Elt<DT>::EPV, STRIDE = TAIL_WG * Elt<DT>::EPV;
 #pragma unroll
-    for (int i = 0; i < NV_TAIL; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int e0 = base + i * STRIDE;
         float wv[E];
         if (r.al && e0 + E <= V) {
-            raw_weights<DT, MODE>(r, a[i], q[i], target_law, si, sp, sq, wv);
+            raw_weights<DT, MODE, TWO>(r, a[i], q[i], target_law, si, sp, sq, wv);
             vs[i] = tree_sum<E>(wv);
         } else if (e0 < V) {
             vec_weights_masked<DT, MODE>(r, e0, V, target_law, si, sp, sq, wv);
@@ -634,44 +642,44 @@ __device__ inline void tail_weigh(const DrawRows &r, int base, int V, bool targe
     }
 }
 
-template <int DT, int MODE>
-__device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV_TAIL],
-                                                 double *units)
+template <int NV>
+__device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV], double *units)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NV_TAIL; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const double s = wave_sum((double)vs[i]);
         if (lane == 0)
-            units[(it * NV_TAIL + i) * TAIL_WAVES + w] = s;
+            units[(it * NV + i) * TAIL_WAVES + w] = s;
     }
 }
 
-// One pass over row L (and the draft row L): unit u = (it*NV_TAIL + i)*TAIL_WAVES + w holds
-// the fp64 sum of wave w's draw weights at vector slot i of iteration it, i.e. the 64*E
-// contiguous ids it*CE + i*TAIL_WG*E + w*64*E + [0, 64*E); unit order is id order.  Two
+// One pass over row L (and the draft row L when TWO): unit u = (it*NV + i)*TAIL_WAVES + w
+// holds the fp64 sum of wave w's draw weights at vector slot i of iteration it, i.e. the
+// 64*E contiguous ids it*CE + i*TAIL_WG*E + w*64*E + [0, 64*E); unit order is id order.  Two
 // register buffers alternate so that the next iteration's loads are in flight while the
 // current one is weighed.
-template <int DT, int MODE>
+template <int DT, int MODE, int NV, bool TWO>
 __device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit, bool target_law,
                                                const SeqInfo &si, const Scale &sp,
                                                const Scale &sq, double *units)
 {
-    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
+    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV * Elt<DT>::EPV;
     const int t0 = threadIdx.x * E;
-    uint4 a0[NV_TAIL], q0[NV_TAIL], a1[NV_TAIL], q1[NV_TAIL];
-    float vs[NV_TAIL];
-    tail_load<DT>(r, t0, V, a0, q0);
+    uint4 a0[NV], q0[NV], a1[NV], q1[NV];
+    float vs[NV];
+    tail_load<DT, NV, TWO>(r, t0, V, a0, q0);
     for (int it = 0; it < nit; it += 2) {
         if (it + 1 < nit)
-            tail_load<DT>(r, (it + 1) * CE + t0, V, a1, q1);
-        tail_weigh<DT, MODE>(r, it * CE + t0, V, target_law, si, sp, sq, a0, q0, vs);
-        tail_store_units<DT, MODE>(it, vs, units);
+            tail_load<DT, NV, TWO>(r, (it + 1) * CE + t0, V, a1, q1);
+        tail_weigh<DT, MODE, NV, TWO>(r, it * CE + t0, V, target_law, si, sp, sq, a0, q0, vs);
+        tail_store_units<NV>(it, vs, units);
         if (it + 1 < nit) {
             if (it + 2 < nit)
-                tail_load<DT>(r, (it + 2) * CE + t0, V, a0, q0);
-            tail_weigh<DT, MODE>(r, (it + 1) * CE + t0, V, target_law, si, sp, sq, a1, q1, vs);
-            tail_store_units<DT, MODE>(it + 1, vs, units);
+                tail_load<DT, NV, TWO>(r, (it + 2) * CE + t0, V, a0, q0);
+            tail_weigh<DT, MODE, NV, TWO>(r, (it + 1) * CE + t0, V, target_law, si, sp, sq, a1,
+                                          q1, vs);
+            tail_store_units<NV>(it + 1, vs, units);
         }
     }
 }
@@ -718,16 +726,16 @@ __device__ inline int find_unit(F unit, int nu, float u01, double *base, double 
 // the unit pass, a wave scan of the vector sums from `base` finds the vector, and its lane
 // emits the first id whose running weight exceeds tt (fb: the last id of positive weight).
 template <int DT, int MODE>
-__device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si, int V, int unit,
-                                            double base, double tt, bool fb, bool target_law,
-                                            const Scale &sp, const Scale &sq, int32_t *out,
-                                            float *out_prob)
+__device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si, int V, int nv,
+                                            int unit, double base, double tt, bool fb,
+                                            bool target_law, const Scale &sp, const Scale &sq,
+                                            int32_t *out, float *out_prob)
 {
-    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
+    constexpr int E = Elt<DT>::EPV;
     const int lane = threadIdx.x & 63;
-    const int it = unit / (NV_TAIL * TAIL_WAVES), rem = unit - it * (NV_TAIL * TAIL_WAVES);
+    const int it = unit / (nv * TAIL_WAVES), rem = unit - it * (nv * TAIL_WAVES);
     const int i = rem / TAIL_WAVES, ww = rem - i * TAIL_WAVES;
-    const int e0 = it * CE + i * TAIL_WG * E + (ww * 64 + lane) * E;
+    const int e0 = it * (TAIL_WG * nv * E) + i * TAIL_WG * E + (ww * 64 + lane) * E;
     float wv[E];
     if (e0 < V) {
         vec_weights_masked<DT, MODE>(r, e0, V, target_law, si, sp, sq, wv);
@@ -795,7 +803,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
     __shared__ SeqInfo s_info;
     __shared__ int s_unit, s_fb;
     __shared__ double s_base, s_t;
-    constexpr int CE = TAIL_WG * NV_TAIL * Elt<DT>::EPV;
+    constexpr int E = Elt<DT>::EPV;
     const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
     accept_phase<DT, MODE>(tgt, drf, tokens, unif, b, K, V, nch, sp, sq, part,
                            reinterpret_cast<float2 *>(dyn), acc_len, out_tokens, out_probs,
@@ -805,14 +813,21 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
     if (si.L < 0)
         return;
     const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
-    const int nit = (V + CE - 1) / CE, nu = nit * NV_TAIL * TAIL_WAVES;
+    // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
+    const bool two = (MODE == CONTRASTIVE) || r.two;
+    const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
+    const int nit = (V + ce - 1) / ce, nu = nit * nv * TAIL_WAVES;
     const float u01 = unif[(size_t)b * (K + 1) + K];
     int32_t *out = out_tokens + (size_t)b * (K + 1) + si.L;
     float *out_prob = draw_probs ? draw_probs + b : nullptr;
     double *units = dyn;
     for (int pass = 0; pass < 2; ++pass) {
         const bool target_law = (pass == 1);
-        tail_unit_sums<DT, MODE>(r, V, nit, target_law, si, sp, sq, units);
+        if (two)
+            tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, target_law, si, sp, sq, units);
+        else if constexpr (MODE == SAMPLING)
+            tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, target_law, si, sp, sq,
+                                                         units);
         __syncthreads();
         if (w == 0) {
             double base, tt;
@@ -829,8 +844,8 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
         const int us = s_unit;
         if (us >= 0) {
             if (w == 0)
-                search_unit<DT, MODE>(r, si, V, us, s_base, s_t, s_fb != 0, target_law, sp, sq,
-                                      out, out_prob);
+                search_unit<DT, MODE>(r, si, V, nv, us, s_base, s_t, s_fb != 0, target_law, sp,
+                                      sq, out, out_prob);
             return;
         }
         // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
