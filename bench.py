@@ -51,6 +51,8 @@ WORKLOADS = {
               "row_argmax", "k_argmax<bf16> (head 0 rows)", None),
     "cut": ("alpha-quantile cut P=128 N=1000 alpha=0.5 f32 scores", "quantile_cut",
             "k_quantile_cut", None),
+    "early": ("sampling verify with early exit B=256 K=8 V=128256 bf16 logits T=0.7",
+              "row_stats", "k_stats_prefix<bf16> (positions 0-1 of every sequence)", None),
 }
 METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
@@ -134,7 +136,9 @@ def main():
     desc, kind, kname, traffic_file = WORKLOADS[args.workload]
     if args.workload == "cut":
         return bench_cut(args, desc, kind, kname)
-    w = (synth.CONFIGS.get(args.workload) or synth.NEXT_CONFIGS[args.workload])()
+    early = args.workload == "early"
+    w = (synth.CONFIGS.get("c3" if early else args.workload)
+         or synth.NEXT_CONFIGS[args.workload])()
     B, K, V = w.B, w.K, w.V
     log("generated %s (seed %d); uploading %.3f GB of logits x2"
         % (desc, w.seed, w.logit_bytes / 1e9))
@@ -166,6 +170,9 @@ def main():
                                            nxt)
         elif w.mode == synth.GREEDY:
             sv.specverify_run_greedy(ctx, stream, w.dtype, B, K, V, tg, toks, acc, out)
+        elif early:
+            sv.specverify_run_sampling_early_exit(ctx, stream, w.dtype, B, K, V, w.temperature, tg,
+                                                  dr, toks, unif, acc, out, probs)
         elif w.mode == synth.CONTRASTIVE:
             sv.specverify_run_contrastive(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
                                           toks, unif, acc, out, probs)
@@ -215,6 +222,10 @@ def main():
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"
         kern_bytes = logit_bytes // H                # head 0's rows
+    elif early:
+        positions = B * K / (ms_step * 1e-3)
+        unit = "verified draft positions/s"
+        kern_bytes = 4 * B * V * w.target.itemsize   # target and draft rows 0 and 1
     else:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"

@@ -6,7 +6,7 @@
  * returns, per sequence, how many draft tokens are accepted and the tokens to emit.
  *
  * Operations and where they are defined (page title, section):
- *  - Sampling verify: "推测性拒绝采样" (speculative rejection sampling), steps 2-4
+ *  - Sampling verify (also with early exit): "推测性拒绝采样" (speculative rejection sampling), steps 2-4
  *    (parallel verification, probability-ratio acceptance, truncation at the first
  *    rejection, replacement drawn at that position) and its "key guarantee" section
  *    (output distribution identical to the target's), which fixes the replacement law
@@ -113,6 +113,21 @@ int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, in
                             float *out_probs);
 
 /*
+ * Sampling verify with early exit: accepted_len and out_tokens exactly as
+ * specverify_run_sampling (same arithmetic, same decisions), but a sequence's rows after its
+ * first rejection are not read, since the tokens after that rejection are discarded
+ * ("推测性拒绝采样", step 3).  Every sequence's first two positions (target and draft rows) are
+ * read, then the remaining rows of the sequences that accepted both, then the draw.
+ * out_probs [B][K][2] holds (p_j(x_j), q_j(x_j)) for j <= L only and NaN for j > L.
+ * Same arguments, layouts and errors as specverify_run_sampling.
+ */
+int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                      int K, int V, float temperature, const void *target_logits,
+                                      const void *draft_logits, const int32_t *draft_tokens,
+                                      const float *uniforms, int32_t *accepted_len,
+                                      int32_t *out_tokens, float *out_probs);
+
+/*
  * Greedy blockwise verify.  g_j = the lowest id among the maxima of l_target[b,j,:]
  * (raw value comparison) for j in [0, K]; L = the first j < K with proposals[b,j] != g_j,
  * else K.  target_logits [B][K+1][V] (dtype), proposals [B][K] int32.
@@ -186,7 +201,8 @@ const char *specverify_strerror(int status);
  * Kernel timing.  Kernel kinds:
  *   0 row statistics (sampling, contrastive, sampler), 1 accept scan and draw (sampling,
  *   contrastive, sampler), 2 row argmax (greedy), 3 proposal compare and emit (greedy, with
- *   the next proposals for the heads variant), 4 quantile cut.
+ *   the next proposals for the heads variant), 4 quantile cut, 5 early-exit accept tests on
+ *   the first positions, 6 early-exit statistics of the remaining rows.
  * specverify_profile_begin(ctx, max_calls, kinds) creates hipEvent pairs for up to
  * max_calls subsequent run_* calls and records one pair around every kernel they launch
  * whose kind k has bit (1 << k) set in `kinds` (0 = every kind), on the call's stream.
@@ -196,7 +212,7 @@ const char *specverify_strerror(int status);
  * Errors: EINVAL (NULL ctx, max_calls < 1, unknown kind bits, begin twice, end without
  * begin), EHIP.
  */
-#define SPECVERIFY_NUM_KERNELS 5
+#define SPECVERIFY_NUM_KERNELS 7
 int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds);
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
 

@@ -27,8 +27,9 @@ SPECVERIFY_ECAPACITY = -5
 SPECVERIFY_MAX_K = 63
 SPECVERIFY_MAX_VOCAB = 1 << 20
 SPECVERIFY_MAX_CUT_N = 8192
-SPECVERIFY_NUM_KERNELS = 5
-KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit", "quantile_cut")
+SPECVERIFY_NUM_KERNELS = 7
+KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit", "quantile_cut",
+                "early_accept", "early_rest_stats")
 
 _lib = None
 _lock = threading.Lock()
@@ -60,6 +61,8 @@ def load():
         lib.specverify_workspace_bytes.restype = i64
         lib.specverify_run_sampling.argtypes = [vp, vp, i, i, i, i, f, vp, vp, vp, vp, vp, vp, vp]
         lib.specverify_run_sampling.restype = i
+        lib.specverify_run_sampling_early_exit.argtypes = lib.specverify_run_sampling.argtypes
+        lib.specverify_run_sampling_early_exit.restype = i
         lib.specverify_run_contrastive.argtypes = [vp, vp, i, i, i, i, f, vp, vp, vp, vp, vp, vp,
                                                    vp]
         lib.specverify_run_contrastive.restype = i
@@ -135,6 +138,15 @@ def specverify_run_sampling(ctx, stream, dtype, B, K, V, temperature, target_log
         ctx, _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
         _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
         _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling")
+
+
+def specverify_run_sampling_early_exit(ctx, stream, dtype, B, K, V, temperature, target_logits,
+                                       draft_logits, draft_tokens, uniforms, accepted_len,
+                                       out_tokens, out_probs=None) -> None:
+    _check(load().specverify_run_sampling_early_exit(
+        ctx, _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
+        _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling_early_exit")
 
 
 def specverify_run_contrastive(ctx, stream, dtype, B, K, V, tau, expert_logits, amateur_logits,

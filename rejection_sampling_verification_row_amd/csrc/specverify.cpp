@@ -14,6 +14,7 @@
 struct specverify_ctx {
     int device;
     int max_batch, max_k, max_vocab, max_nch;
+    int num_cus;                          // compute units of the device
     void *mem;
     size_t bytes;
     sv::Workspace ws;
@@ -138,7 +139,13 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
 
     const size_t nch = (size_t)sv::max_chunks(max_vocab);
     const size_t rows = (size_t)max_batch * (2 * (size_t)max_k + 1);
-    const size_t total = align_up(rows * nch * sv::WAVES * sizeof(float2));
+    const size_t b_part = align_up(rows * nch * sv::WAVES * sizeof(float2));
+    const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
+    const size_t total = b_part + 2 * b_seq + align_up(sizeof(int));
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cus < 1)
+        return SPECVERIFY_EHIP;
 
     specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
     if (!ctx)
@@ -147,7 +154,12 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
         delete ctx;
         return SPECVERIFY_ENOMEM;
     }
-    ctx->ws.part = static_cast<float2 *>(ctx->mem);
+    char *p = static_cast<char *>(ctx->mem);
+    ctx->ws.part = reinterpret_cast<float2 *>(p);
+    ctx->ws.alive = reinterpret_cast<int *>(p + b_part);
+    ctx->ws.list = reinterpret_cast<int *>(p + b_part + b_seq);
+    ctx->ws.count = reinterpret_cast<int *>(p + b_part + 2 * b_seq);
+    ctx->num_cus = cus;
     ctx->device = device;
     ctx->max_batch = max_batch;
     ctx->max_k = max_k;
@@ -207,6 +219,44 @@ int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int 
     hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
                                      accepted_len, out_tokens);
     note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                      int K, int V, float temperature, const void *target_logits,
+                                      const void *draft_logits, const int32_t *draft_tokens,
+                                      const float *uniforms, int32_t *accepted_len,
+                                      int32_t *out_tokens, float *out_probs)
+{
+    int rc = check_common(ctx, dtype, B, K, V);
+    if (rc != SPECVERIFY_OK)
+        return rc;
+    if (bad_temperature(temperature))
+        return SPECVERIFY_EINVAL;
+    if (B == 0)
+        return SPECVERIFY_OK;
+    if (!target_logits || !uniforms || !accepted_len || !out_tokens ||
+        (K > 0 && (!draft_logits || !draft_tokens)))
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(target_logits, es) || (draft_logits && !aligned_to(draft_logits, es)) ||
+        (draft_tokens && !aligned_to(draft_tokens, 4)) || !aligned_to(uniforms, 4) ||
+        !aligned_to(accepted_len, 4) || !aligned_to(out_tokens, 4) ||
+        (out_probs && !aligned_to(out_probs, 4)))
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    const sv::Scale sp = sv::make_scale((double)temperature);
+    hipEvent_t *ev = next_events(ctx);
+    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
+    // the rest of the alive rows: about six 256-thread workgroups per compute unit
+    hipError_t e = sv::launch_sampling_early_exit(ln, ctx->ws, dtype, B, K, V, sp, target_logits,
+                                                  draft_logits, draft_tokens, uniforms,
+                                                  accepted_len, out_tokens, out_probs,
+                                                  6 * ctx->num_cus);
+    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_EARLY_ACCEPT) |
+                           (1u << sv::KIND_EARLY_REST) | (1u << sv::KIND_TAIL));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 

@@ -30,6 +30,7 @@ constexpr int NV_TAIL = 2;
 constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the accept phase
 constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
 constexpr int MAX_CUT_N = 8192;       // scores per prompt of the quantile cut (32 KiB of LDS)
+constexpr int EARLY_PREFIX = 2;       // positions every sequence reads before early exit
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
@@ -86,6 +87,9 @@ enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };
 
 struct Workspace {
     float2 *part;       // [rows][nch][WAVES] per-wave (max, sum of exp2) or (max, id) partials
+    int *alive;         // [B] early exit: 1 if the sequence accepted its first positions
+    int *list;          // [B] early exit: the alive sequences, in no particular order
+    int *count;         // early exit: the number of alive sequences
 };
 
 struct Launch {
@@ -101,7 +105,9 @@ enum Kind {
     KIND_ARGMAX = 2,
     KIND_GREEDY_EMIT = 3,
     KIND_CUT = 4,
-    NUM_KINDS = 5
+    KIND_EARLY_ACCEPT = 5,
+    KIND_EARLY_REST = 6,
+    NUM_KINDS = 7
 };
 
 // Sampling or contrastive verify (mode), or, with K = 0, acc_len = NULL and draw_probs set,
@@ -112,6 +118,16 @@ hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int 
                            const void *drf, const int32_t *tokens, const float *unif,
                            int32_t *acc_len, int32_t *out_tokens, float *out_probs,
                            float *draw_probs);
+
+// Sampling verify reading rows only up to each sequence's first rejection: the first
+// EARLY_PREFIX positions of every sequence, then the rest of the sequences that accepted
+// them (k_stats_rest runs rest_grid workgroups over that work).  Tokens and accepted_len as
+// launch_sampling; out_probs for j <= L only (NaN after).
+hipError_t launch_sampling_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B,
+                                      int K, int V, const Scale &sp, const void *tgt,
+                                      const void *drf, const int32_t *tokens, const float *unif,
+                                      int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                                      int rest_grid);
 
 // greedy verify over [B][K+1][H][V] head logits (head 0 verifies) plus next_props [B][H-1],
 // the first argmaxes of heads 1..H-1 at the emitted position

@@ -291,65 +291,76 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
     }
 }
 
-// Sequence b after its rows' statistics (the first phase of k_tail): merge the per-wave
-// partials of its 2K+1 rows (fp64), then wave 0 runs the accept tests and the
-// first-rejection scan, one lane per draft position, writes accepted_len, the kept tokens,
-// -1 padding and out_probs, and leaves in *info what the draw needs (L = -1 for bad ids).
-// The draft tokens and their logits are fetched first and the partials are staged in LDS
-// in one coalesced pass when they fit, so the merge waits on memory once.
-template <int DT, int MODE>
-__device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
-                                             const int32_t *tokens, const float *unif, int b,
-                                             int K, int V, int nch, const Scale &sp,
-                                             const Scale &sq, const float2 *part, float2 *stage,
-                                             int32_t *acc_len, int32_t *out_tokens,
-                                             float *out_probs, SeqInfo *info)
-{
-    __shared__ float sM[MAX_ROWS];
-    __shared__ double sS[MAX_ROWS];
-    const int R = 2 * K + 1, np = nch * WAVES, total = R * np;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+// Per-lane inputs of the accept tests of sequence b (wave 0, lane j < K): draft token x_j,
+// uniform u_j and the gathered logits (the contrastive target value l_e - l_a in fp32); bad:
+// x_j outside [0, V).
+struct Draft {
+    int32_t x;
+    float lp, lq, u;
+    bool bad;
+};
 
-    int32_t x = 0;
-    float lp = 0.0f, lq = 0.0f, u = 0.0f;
-    bool bad = false;
-    if (w == 0 && lane < K) {
-        x = tokens[(size_t)b * K + lane];
-        u = unif[(size_t)b * (K + 1) + lane];
-        bad = (x < 0 || x >= V);
-        if (!bad) {
-            const size_t it = ((size_t)b * (K + 1) + lane) * (size_t)V + x;
+template <int DT, int MODE>
+__device__ __forceinline__ Draft gather_draft(const char *tgt, const char *drf,
+                                              const int32_t *tokens, const float *unif, int b,
+                                              int K, int V, int lane)
+{
+    Draft d = {0, 0.0f, 0.0f, 0.0f, false};
+    if (lane < K) {
+        d.x = tokens[(size_t)b * K + lane];
+        d.u = unif[(size_t)b * (K + 1) + lane];
+        d.bad = (d.x < 0 || d.x >= V);
+        if (!d.bad) {
+            const size_t it = ((size_t)b * (K + 1) + lane) * (size_t)V + d.x;
             if (MODE == SAMPLING) {
-                lp = Elt<DT>::one(tgt, it);
-                lq = Elt<DT>::one(drf, ((size_t)b * K + lane) * (size_t)V + x);
+                d.lp = Elt<DT>::one(tgt, it);
+                d.lq = Elt<DT>::one(drf, ((size_t)b * K + lane) * (size_t)V + d.x);
             } else {
                 const float le = Elt<DT>::one(tgt, it), la = Elt<DT>::one(drf, it);
-                lp = le - la;
-                lq = la;
+                d.lp = le - la;
+                d.lq = la;
             }
         }
     }
+    return d;
+}
 
+// Merge the per-wave partials of the rows of sequence b whose position is below npos
+// (target row j and draft row j of position j) into (M, S) in fp64: M = max, S = sum of
+// s * 2^((m - M) log2(e)/T).  The NT threads stage the partials in LDS in one coalesced pass
+// when they fit; one wave merges each row, always with the same instructions, so every
+// kernel that merges a row gets the same bits.
+template <int NT>
+__device__ __forceinline__ void merge_rows(const float2 *part, int b, int K, int nch, int npos,
+                                           const Scale &sp, const Scale &sq, float2 *stage,
+                                           float *sM, double *sS)
+{
+    constexpr int NW = NT / 64;
+    const int R = 2 * K + 1, np = nch * WAVES, total = R * np;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float2 *pb = part + (size_t)b * total;
     const bool staged = total <= ACCEPT_STAGE;
     if (staged) {
-        for (int i0 = 0; i0 < total; i0 += 4 * TAIL_WG) {
+        for (int i0 = 0; i0 < total; i0 += 4 * NT) {
             float2 v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int i = i0 + k * TAIL_WG + t;
+                const int i = i0 + k * NT + t;
                 v[k] = (i < total) ? pb[i] : make_float2(0.0f, 0.0f);
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int i = i0 + k * TAIL_WG + t;
+                const int i = i0 + k * NT + t;
                 if (i < total)
                     stage[i] = v[k];
             }
         }
         __syncthreads();
     }
-    for (int r = w; r < R; r += TAIL_WAVES) {
+    for (int r = w; r < R; r += NW) {
+        const int pos = (r <= K) ? r : r - K - 1;
+        if (pos >= npos)
+            continue;  // not read by this call
         const int r0 = r * np;
         const double cc = (r <= K) ? sp.c : sq.c;
         float ml = -INFINITY;
@@ -369,11 +380,46 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         }
     }
     __syncthreads();
+}
+
+// p_j(x_j), q_j(x_j) in fp64 from the merged statistics and the accept test: kept iff
+// P > 0 and u * Q <= P.
+__device__ __forceinline__ bool accept_test(const Draft &d, int j, int K, const float *sM,
+                                            const double *sS, const Scale &sp, const Scale &sq,
+                                            double &P, double &Q)
+{
+    P = exp(((double)d.lp - (double)sM[j]) * sp.inv_t) / sS[j];
+    Q = exp(((double)d.lq - (double)sM[K + 1 + j]) * sq.inv_t) / sS[K + 1 + j];
+    return (P > 0.0) && ((double)d.u * Q <= P);
+}
+
+// Sequence b after its rows' statistics (the first phase of k_tail): merge the rows of the
+// positions below npos (K+1: all of them), then wave 0 runs the accept tests, one lane per
+// draft position, finds the first rejection L, writes accepted_len, the kept tokens, -1
+// padding and out_probs, and leaves in *info what the draw needs (L = -1 for bad ids).
+// Positions at or past npos are only reached by a sequence that rejects before them.
+// mask_probs: out_probs only for j <= L, NaN after (the rows after L may not have been read).
+template <int DT, int MODE>
+__device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
+                                             const int32_t *tokens, const float *unif, int b,
+                                             int K, int V, int nch, int npos, bool mask_probs,
+                                             const Scale &sp, const Scale &sq, const float2 *part,
+                                             float2 *stage, int32_t *acc_len,
+                                             int32_t *out_tokens, float *out_probs,
+                                             SeqInfo *info)
+{
+    __shared__ float sM[MAX_ROWS];
+    __shared__ double sS[MAX_ROWS];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    Draft d = {0, 0.0f, 0.0f, 0.0f, false};
+    if (w == 0)  // the token and logit loads go out before the merge waits on memory
+        d = gather_draft<DT, MODE>(tgt, drf, tokens, unif, b, K, V, lane);
+    merge_rows<TAIL_WG>(part, b, K, nch, npos, sp, sq, stage, sM, sS);
     if (w != 0)
         return;
 
     int32_t *ot = out_tokens + (size_t)b * (K + 1);
-    if (__ballot(bad) != 0) {
+    if (__ballot(d.bad) != 0) {
         if (lane <= K)
             ot[lane] = -1;
         if (lane < K && out_probs) {
@@ -389,20 +435,19 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         }
         return;
     }
-    bool acc = false;
-    if (lane < K) {
-        const double P = exp(((double)lp - (double)sM[lane]) * sp.inv_t) / sS[lane];
-        const double Q = exp(((double)lq - (double)sM[K + 1 + lane]) * sq.inv_t) / sS[K + 1 + lane];
-        if (out_probs) {
-            out_probs[((size_t)b * K + lane) * 2] = (float)P;
-            out_probs[((size_t)b * K + lane) * 2 + 1] = (float)Q;
-        }
-        acc = (P > 0.0) && ((double)u * Q <= P);
-    }
+    bool acc = lane < K;  // lanes >= K never accept; positions >= npos are never reached
+    double P = NAN, Q = NAN;
+    if (lane < K && lane < npos)
+        acc = accept_test(d, lane, K, sM, sS, sp, sq, P, Q);
     const unsigned long long am = __ballot(acc);
-    const int L = __builtin_ctzll(~am);  // lanes >= K never accept, so L <= K
+    const int L = __builtin_ctzll(~am);  // L <= K
+    if (lane < K && out_probs) {
+        const bool show = !mask_probs || lane <= L;
+        out_probs[((size_t)b * K + lane) * 2] = show ? (float)P : NAN;
+        out_probs[((size_t)b * K + lane) * 2 + 1] = show ? (float)Q : NAN;
+    }
     if (lane < L)
-        ot[lane] = x;
+        ot[lane] = d.x;
     else if (lane > L && lane <= K)
         ot[lane] = -1;
     if (lane == 0) {
@@ -784,7 +829,8 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
                             si.Sp);
 }
 
-// One 1024-thread workgroup per sequence, after the row statistics: the accept phase
+// One 1024-thread workgroup per sequence, after the row statistics (with early exit: alive[b]
+// says whether all rows were read, else only the first `prefix` positions): the accept phase
 // (merge, gather, accept tests, L), then one pass over row L (and draft row L) into unit sums
 // in LDS, then the unit holding t = u_K * W and the id inside it.  If rounding left the
 // residual empty, the pass is repeated with the target law p_L (essentially never taken).
@@ -797,7 +843,8 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
                                                   int nch, Scale sp, Scale sq,
                                                   const float2 *__restrict__ part,
                                                   int32_t *acc_len, int32_t *out_tokens,
-                                                  float *out_probs, float *draw_probs)
+                                                  float *out_probs, float *draw_probs,
+                                                  const int *alive, int prefix, int mask_probs)
 {
     extern __shared__ double dyn[];
     __shared__ SeqInfo s_info;
@@ -805,8 +852,11 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
     __shared__ double s_base, s_t;
     constexpr int E = Elt<DT>::EPV;
     const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-    accept_phase<DT, MODE>(tgt, drf, tokens, unif, b, K, V, nch, sp, sq, part,
-                           reinterpret_cast<float2 *>(dyn), acc_len, out_tokens, out_probs,
+    // rows read by this call: every position, or with early exit the first `prefix` ones for
+    // a sequence that was not alive after them
+    const int npos = (alive == nullptr || alive[b]) ? K + 1 : prefix;
+    accept_phase<DT, MODE>(tgt, drf, tokens, unif, b, K, V, nch, npos, mask_probs != 0, sp, sq,
+                           part, reinterpret_cast<float2 *>(dyn), acc_len, out_tokens, out_probs,
                            &s_info);
     __syncthreads();
     const SeqInfo si = s_info;
@@ -854,6 +904,114 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
         *out = -1;
         if (out_prob)
             *out_prob = NAN;
+    }
+}
+
+// ------------------------------------------------------------------ early-exit verify
+//
+// Rows after a sequence's first rejection are not needed for its tokens.  Early exit reads
+// the first `prefix` positions of every sequence (k_stats_prefix), runs their accept tests
+// (k_alive: the sequences that accept all of them are listed), reads the remaining rows of
+// the listed sequences only (k_stats_rest), and k_tail finishes every sequence from the rows
+// it has.  The statistics and the accept tests are the same instructions as the full pass,
+// so the decisions are the same.
+
+// the partials of one chunk of one row, as k_stats_sampling computes them
+template <int DT>
+__device__ __forceinline__ void row_chunk_stats(const char *rp, int V, int c, const Scale &sc,
+                                                float2 *dst)
+{
+    constexpr int E = Elt<DT>::EPV;
+    float x[NV_STATS][E];
+    load_chunk<DT, NV_STATS>(rp, aligned16(rp), c * WG * NV_STATS * E, V, x);
+    float m, s;
+    thread_stats<E, NV_STATS>(x, sc, m, s);
+    store_wave_partials(wave_stats(m, s, sc), dst);
+}
+
+// target rows 0..prefix-1 and draft rows 0..prefix-1 of every sequence (prefix <= K); workgroup
+// 0 also clears the survivor count for k_alive
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats_prefix(const char *__restrict__ tgt,
+                                                     const char *__restrict__ drf, int K, int V,
+                                                     int nch, int prefix, Scale sc, float2 *part,
+                                                     int *count)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    const int per = 2 * prefix * nch;
+    const int b = blockIdx.x / per, rem = blockIdx.x - b * per;
+    const int lr = rem / nch, c = rem - lr * nch;
+    const bool draft = lr >= prefix;
+    const int j = draft ? lr - prefix : lr;
+    const char *rp = draft ? drf + ((size_t)b * K + j) * (size_t)V * BY
+                           : tgt + ((size_t)b * (K + 1) + j) * (size_t)V * BY;
+    const int r = draft ? K + 1 + j : j;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *count = 0;
+    row_chunk_stats<DT>(rp, V, c, sc, part + (((size_t)b * (2 * K + 1) + r) * nch + c) * WAVES);
+}
+
+// One 256-thread workgroup per sequence: the accept tests at positions 0..prefix-1 on the same
+// merged statistics as k_tail.  A sequence with valid ids that accepts all of them is alive:
+// alive[b] = 1 and it is appended to list (count = list length); else alive[b] = 0.
+template <int DT>
+__global__ __launch_bounds__(WG) void k_alive(const char *__restrict__ tgt,
+                                              const char *__restrict__ drf,
+                                              const int32_t *__restrict__ tokens,
+                                              const float *__restrict__ unif, int K, int V,
+                                              int nch, int prefix, Scale sp, Scale sq,
+                                              const float2 *__restrict__ part, int *alive,
+                                              int *list, int *count)
+{
+    __shared__ float2 stage[ACCEPT_STAGE];
+    __shared__ float sM[MAX_ROWS];
+    __shared__ double sS[MAX_ROWS];
+    const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    Draft d = {0, 0.0f, 0.0f, 0.0f, false};
+    if (w == 0)
+        d = gather_draft<DT, SAMPLING>(tgt, drf, tokens, unif, b, K, V, lane);
+    merge_rows<WG>(part, b, K, nch, prefix, sp, sq, stage, sM, sS);
+    if (w != 0)
+        return;
+    bool acc = true;
+    if (lane < prefix) {
+        double P, Q;
+        acc = accept_test(d, lane, K, sM, sS, sp, sq, P, Q);
+    }
+    const bool live = __ballot(d.bad) == 0 && __ballot(!acc) == 0;
+    if (lane == 0) {
+        alive[b] = live ? 1 : 0;
+        if (live)
+            list[atomicAdd(count, 1)] = b;
+    }
+}
+
+// The rows of positions prefix..K of the listed sequences: item i of count * rows * nch
+// (rows = 2K + 1 - 2 prefix per sequence: target rows prefix..K, draft rows prefix..K-1) is one
+// chunk of one row, taken by workgroup i mod gridDim in turn; the loop bound is read from the
+// count k_alive left, so every workgroup ends.
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats_rest(const char *__restrict__ tgt,
+                                                   const char *__restrict__ drf, int K, int V,
+                                                   int nch, int prefix, Scale sc, float2 *part,
+                                                   const int *__restrict__ list,
+                                                   const int *__restrict__ count)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    const int nt = K + 1 - prefix;                       // target rows per sequence
+    const int per = (2 * K + 1 - 2 * prefix) * nch;
+    const long total = (long)(*count) * per;
+    for (long item = blockIdx.x; item < total; item += gridDim.x) {
+        const int a = (int)(item / per), rem = (int)(item - (long)a * per);
+        const int lr = rem / nch, c = rem - lr * nch;
+        const int b = list[a];
+        const bool draft = lr >= nt;
+        const int j = prefix + (draft ? lr - nt : lr);
+        const char *rp = draft ? drf + ((size_t)b * K + j) * (size_t)V * BY
+                               : tgt + ((size_t)b * (K + 1) + j) * (size_t)V * BY;
+        const int r = draft ? K + 1 + j : j;
+        row_chunk_stats<DT>(rp, V, c, sc, part + (((size_t)b * (2 * K + 1) + r) * nch + c) * WAVES);
+        __syncthreads();  // the LDS of store_wave_partials is reused by the next item
     }
 }
 
@@ -1180,7 +1338,8 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
         Timer tm(ln, KIND_TAIL);
         hipLaunchKernelGGL((k_tail<DT, MODE>), dim3(B), dim3(TAIL_WG),
                            tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
-                           sp, sq, ws.part, acc_len, out_tokens, out_probs, draw_probs);
+                           sp, sq, ws.part, acc_len, out_tokens, out_probs, draw_probs, nullptr,
+                           K + 1, 0);
     }
     return hipGetLastError();
 }
@@ -1200,6 +1359,52 @@ hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int 
         Timer tm(ln, KIND_GREEDY_EMIT);
         hipLaunchKernelGGL(k_greedy_final, dim3(B), dim3(WG), 0, ln.stream, props, K, V, nch,
                            ws.part, acc_len, out_tokens);
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, int V,
+                           const Scale &sp, const void *tgt, const void *drf,
+                           const int32_t *tokens, const float *unif, int32_t *acc_len,
+                           int32_t *out_tokens, float *out_probs, int rest_grid)
+{
+    const char *t = static_cast<const char *>(tgt);
+    const char *d = static_cast<const char *>(drf);
+    const int nch = num_chunks(NV_STATS, DT, V);
+    const int prefix = EARLY_PREFIX < K + 1 ? EARLY_PREFIX : K + 1;
+    const int *alive = nullptr;
+    if (prefix == K + 1) {  // every position is in the prefix: one full pass
+        Timer tm(ln, KIND_STATS);
+        hipLaunchKernelGGL(k_stats_sampling<DT>, dim3((unsigned)((size_t)B * (2 * K + 1) * nch)),
+                           dim3(WG), 0, ln.stream, t, d, K, V, nch, sp, ws.part);
+    } else {
+        {
+            Timer tm(ln, KIND_STATS);
+            hipLaunchKernelGGL(k_stats_prefix<DT>,
+                               dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0,
+                               ln.stream, t, d, K, V, nch, prefix, sp, ws.part, ws.count);
+        }
+        {
+            Timer tm(ln, KIND_EARLY_ACCEPT);
+            hipLaunchKernelGGL(k_alive<DT>, dim3(B), dim3(WG), 0, ln.stream, t, d, tokens, unif,
+                               K, V, nch, prefix, sp, sp, ws.part, ws.alive, ws.list, ws.count);
+        }
+        {
+            Timer tm(ln, KIND_EARLY_REST);
+            const size_t items = (size_t)B * (2 * K + 1 - 2 * prefix) * nch;
+            const unsigned grid = (unsigned)(items < (size_t)rest_grid ? items : rest_grid);
+            hipLaunchKernelGGL(k_stats_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K, V,
+                               nch, prefix, sp, ws.part, ws.list, ws.count);
+        }
+        alive = ws.alive;
+    }
+    {
+        Timer tm(ln, KIND_TAIL);
+        hipLaunchKernelGGL((k_tail<DT, SAMPLING>), dim3(B), dim3(TAIL_WG),
+                           tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
+                           sp, sp, ws.part, acc_len, out_tokens, out_probs, nullptr, alive,
+                           prefix, 1);
     }
     return hipGetLastError();
 }
@@ -1226,6 +1431,17 @@ hipError_t greedy_heads_impl(const Launch &ln, const Workspace &ws, int B, int K
 }
 
 }  // namespace
+
+hipError_t launch_sampling_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B,
+                                      int K, int V, const Scale &sp, const void *tgt,
+                                      const void *drf, const int32_t *tokens, const float *unif,
+                                      int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                                      int rest_grid)
+{
+    auto f = dtype == 1 ? early_exit_impl<1> : early_exit_impl<0>;
+    return f(ln, ws, B, K, V, sp, tgt, drf, tokens, unif, acc_len, out_tokens, out_probs,
+             rest_grid);
+}
 
 hipError_t launch_greedy_heads(const Launch &ln, const Workspace &ws, int dtype, int B, int K,
                                int H, int V, const void *logits, const int32_t *props,

@@ -185,3 +185,35 @@ def run_cut(ctx: int, P: int, N: int, alpha: float, scores: np.ndarray, misalign
     sv.specverify_quantile_cut(ctx, None, P, N, alpha, s, cut, keep, n)
     torch.cuda.synchronize()
     return cut.cpu().numpy(), keep.cpu().numpy().astype(bool), n.cpu().numpy()
+
+
+def run_early(ctx: int, w, misalign: int = 0, with_probs: bool = True) -> GpuOut:
+    """specverify_run_sampling_early_exit on a sampling workload."""
+    put = (lambda a: dev_offset(a, misalign)) if misalign else dev
+    B, K = w.B, w.K
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    tok = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+    probs = torch.full((B, K, 2), -7.0, dtype=torch.float32, device="cuda") if with_probs else None
+    drf = put(w.draft) if w.draft is not None and w.draft.size else None
+    sv.specverify_run_sampling_early_exit(ctx, None, w.dtype, B, K, w.V, w.temperature,
+                                          put(w.target), drf, dev(w.tokens), dev(w.uniforms),
+                                          acc, tok, probs)
+    torch.cuda.synchronize()
+    return GpuOut(acc.cpu().numpy(), tok.cpu().numpy(),
+                  None if probs is None else probs.cpu().numpy())
+
+
+def compare_early(w, g: GpuOut, o: oracle.Result, seqs=None) -> Report:
+    """Early exit: out_probs must be NaN after the accepted length and, up to it, agree with
+    the oracle as in compare(); everything else is compare()."""
+    if g.out_probs is not None:
+        seqs_l = list(range(w.B)) if seqs is None else list(seqs)
+        probs = g.out_probs.copy()
+        for i, b in enumerate(seqs_l):
+            L = int(g.accepted_len[b])
+            if L < 0:
+                continue
+            assert np.all(np.isnan(probs[b, L + 1:])), (b, L, probs[b])
+            probs[b, L + 1:] = o.out_probs[i, L + 1:]
+        g = GpuOut(g.accepted_len, g.out_tokens, probs)
+    return compare(w, g, o, seqs)

@@ -1,0 +1,87 @@
+"""GPU parity of sampling verify with early exit (needs an MI355X): the same tokens and
+accepted lengths as the oracle and as the full-read entry point, out_probs up to L."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_support import compare_early, run, run_early
+from rejection_sampling_verification_row_amd import binding as sv
+from rejection_sampling_verification_row_amd import synth
+from rejection_sampling_verification_row_amd.synth import BF16, F32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    h = sv.specverify_create(0, 1024, 16, 160000)
+    yield h
+    sv.specverify_destroy(h)
+
+
+def _same_as_full(ctx, w, g):
+    f = run(ctx, w)
+    assert np.array_equal(g.accepted_len, f.accepted_len)
+    assert np.array_equal(g.out_tokens, f.out_tokens)
+    for b in range(w.B):
+        L = int(f.accepted_len[b])
+        if L >= 0:
+            assert np.array_equal(g.out_probs[b, :L + 1], f.out_probs[b, :L + 1])
+
+
+@pytest.mark.parametrize("cfg,sample", [("c1", None), ("c2", None), ("c3", 48)])
+def test_early_exit_full_size(ctx, cfg, sample):
+    w = synth.CONFIGS[cfg]()
+    g = run_early(ctx, w)
+    if sample is None:
+        seqs, o = None, oracle.run_workload(w)
+    else:
+        seqs = sorted(np.random.default_rng(78).choice(w.B, sample, replace=False).tolist())
+        o = oracle.run_workload(w.subset(seqs))
+    rep = compare_early(w, g, o, seqs)
+    print("\n[early exit %s] %s" % (w.name, rep), flush=True)
+    _same_as_full(ctx, w, g)
+
+
+@pytest.mark.parametrize("dtype,B,K,V", [(F32, 6, 0, 100), (BF16, 7, 1, 300), (F32, 9, 2, 1001),
+                                         (BF16, 11, 3, 16385), (BF16, 5, 12, 50001),
+                                         (F32, 4, 7, 40000)])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_early_exit_small_shapes(ctx, dtype, B, K, V, misalign):
+    w = synth.make_sampling(B, K, V, dtype, 0.85, seed=700 + B + K + V, target_sigma=2.5,
+                            draft_sigma=1.0)
+    g = run_early(ctx, w, misalign=misalign)
+    compare_early(w, g, oracle.run_workload(w))
+    _same_as_full(ctx, w, g)
+
+
+@pytest.mark.parametrize("draft_sigma", [0.0, 6.0])
+def test_early_exit_all_alive_and_none_alive(ctx, draft_sigma):
+    """An identical draft accepts everything (every sequence reads every row); a far draft
+    rejects almost at once (nothing left after the first positions)."""
+    w = synth.make_sampling(24, 6, 3000, BF16, 1.0, seed=5, target_sigma=2.0,
+                            draft_sigma=draft_sigma)
+    g = run_early(ctx, w)
+    compare_early(w, g, oracle.run_workload(w))
+    _same_as_full(ctx, w, g)
+    if draft_sigma == 0.0:
+        assert np.all(g.accepted_len == 6)
+
+
+def test_early_exit_bad_id_after_an_early_rejection(ctx):
+    """A bad id anywhere marks the sequence, even past the rows early exit reads."""
+    w = synth.make_sampling(6, 5, 500, F32, 1.0, seed=8, target_sigma=2.0, draft_sigma=4.0)
+    w.tokens[3, 4] = 500
+    g = run_early(ctx, w)
+    assert g.accepted_len[3] == -1 and np.all(g.out_tokens[3] == -1)
+    assert np.all(np.isnan(g.out_probs[3]))
+    compare_early(w, g, oracle.run_workload(w))
+
+
+def test_early_exit_is_deterministic(ctx):
+    w = synth.make_sampling(64, 6, 20000, BF16, 0.8, seed=12, target_sigma=3.0, draft_sigma=1.2)
+    a, b = run_early(ctx, w), run_early(ctx, w)
+    assert np.array_equal(a.out_tokens, b.out_tokens)
+    assert np.array_equal(a.out_probs, b.out_probs, equal_nan=True)
