@@ -250,11 +250,12 @@ int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, in
     const sv::Scale sp = sv::make_scale((double)temperature);
     hipEvent_t *ev = next_events(ctx);
     sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
-    // the rest of the alive rows: about six 256-thread workgroups per compute unit
+    // the rest of the alive rows: 24 256-thread workgroups per compute unit, most of which
+    // take one or two items (fewer left the last items to a few workgroups)
     hipError_t e = sv::launch_sampling_early_exit(ln, ctx->ws, dtype, B, K, V, sp, target_logits,
                                                   draft_logits, draft_tokens, uniforms,
                                                   accepted_len, out_tokens, out_probs,
-                                                  6 * ctx->num_cus);
+                                                  24 * ctx->num_cus);
     note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_EARLY_ACCEPT) |
                            (1u << sv::KIND_EARLY_REST) | (1u << sv::KIND_TAIL));
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
