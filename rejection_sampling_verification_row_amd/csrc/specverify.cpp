@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -139,13 +140,18 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
 
     const size_t nch = (size_t)sv::max_chunks(max_vocab);
     const size_t rows = (size_t)max_batch * (2 * (size_t)max_k + 1);
-    const size_t b_part = align_up(rows * nch * sv::WAVES * sizeof(float2));
-    const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
-    const size_t total = b_part + 2 * b_seq + align_up(sizeof(int));
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
         cus < 1)
         return SPECVERIFY_EHIP;
+    // a sequence's draw is shared by several workgroups only when B <= cus / 2
+    const int split_batch = std::min(max_batch, cus / 2);
+    const int nu_stride = std::max(sv::tail_units(0, max_vocab), sv::tail_units(1, max_vocab));
+    const size_t b_part = align_up(rows * nch * sv::WAVES * sizeof(float2));
+    const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
+    const size_t b_gu = align_up((size_t)split_batch * nu_stride * sizeof(double));
+    const size_t b_gc = align_up((size_t)split_batch * sizeof(int));
+    const size_t total = b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu + b_gc;
 
     specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
     if (!ctx)
@@ -159,6 +165,19 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     ctx->ws.alive = reinterpret_cast<int *>(p + b_part);
     ctx->ws.list = reinterpret_cast<int *>(p + b_part + b_seq);
     ctx->ws.count = reinterpret_cast<int *>(p + b_part + 2 * b_seq);
+    ctx->ws.gunits = reinterpret_cast<double *>(p + b_part + 2 * b_seq + align_up(sizeof(int)));
+    ctx->ws.gcount = reinterpret_cast<int *>(p + b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu);
+    ctx->ws.split_batch = split_batch;
+    ctx->ws.nu_stride = nu_stride;
+    ctx->ws.num_cus = cus;
+    // the arrival counts start at 0; every call leaves them at 0
+    if (split_batch > 0 &&
+        (hipMemset(ctx->ws.gcount, 0, (size_t)split_batch * sizeof(int)) != hipSuccess ||
+         hipDeviceSynchronize() != hipSuccess)) {
+        (void)hipFree(ctx->mem);
+        delete ctx;
+        return SPECVERIFY_EHIP;
+    }
     ctx->num_cus = cus;
     ctx->device = device;
     ctx->max_batch = max_batch;

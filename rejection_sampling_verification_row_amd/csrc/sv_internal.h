@@ -31,6 +31,7 @@ constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the ac
 constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
 constexpr int MAX_CUT_N = 8192;       // scores per prompt of the quantile cut (32 KiB of LDS)
 constexpr int EARLY_PREFIX = 2;       // positions every sequence reads before early exit
+constexpr int TAIL_MAX_SPLIT = 8;     // most workgroups that share one sequence's draw
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
@@ -90,6 +91,11 @@ struct Workspace {
     int *alive;         // [B] early exit: 1 if the sequence accepted its first positions
     int *list;          // [B] early exit: the alive sequences, in no particular order
     int *count;         // early exit: the number of alive sequences
+    double *gunits;     // [split_batch][nu_stride] unit sums of a draw shared by workgroups
+    int *gcount;        // [split_batch] arrival counts of those workgroups, 0 between calls
+    int split_batch;    // largest batch whose draws may be shared (0: never)
+    int nu_stride;      // unit sums per sequence in gunits
+    int num_cus;        // compute units of the device
 };
 
 struct Launch {

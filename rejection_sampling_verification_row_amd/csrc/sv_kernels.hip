@@ -399,14 +399,15 @@ __device__ __forceinline__ bool accept_test(const Draft &d, int j, int K, const 
 // padding and out_probs, and leaves in *info what the draw needs (L = -1 for bad ids).
 // Positions at or past npos are only reached by a sequence that rejects before them.
 // mask_probs: out_probs only for j <= L, NaN after (the rows after L may not have been read).
+// write: whether this workgroup writes the outputs (one of the workgroups of a split draw).
 template <int DT, int MODE>
 __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
                                              const int32_t *tokens, const float *unif, int b,
                                              int K, int V, int nch, int npos, bool mask_probs,
-                                             const Scale &sp, const Scale &sq, const float2 *part,
-                                             float2 *stage, int32_t *acc_len,
-                                             int32_t *out_tokens, float *out_probs,
-                                             SeqInfo *info)
+                                             bool write, const Scale &sp, const Scale &sq,
+                                             const float2 *part, float2 *stage,
+                                             int32_t *acc_len, int32_t *out_tokens,
+                                             float *out_probs, SeqInfo *info)
 {
     __shared__ float sM[MAX_ROWS];
     __shared__ double sS[MAX_ROWS];
@@ -419,8 +420,12 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         return;
 
     int32_t *ot = out_tokens + (size_t)b * (K + 1);
+    if (!write) {
+        acc_len = nullptr;
+        out_probs = nullptr;
+    }
     if (__ballot(d.bad) != 0) {
-        if (lane <= K)
+        if (write && lane <= K)
             ot[lane] = -1;
         if (lane < K && out_probs) {
             out_probs[((size_t)b * K + lane) * 2] = NAN;
@@ -446,9 +451,9 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         out_probs[((size_t)b * K + lane) * 2] = show ? (float)P : NAN;
         out_probs[((size_t)b * K + lane) * 2 + 1] = show ? (float)Q : NAN;
     }
-    if (lane < L)
+    if (write && lane < L)
         ot[lane] = d.x;
-    else if (lane > L && lane <= K)
+    else if (write && lane > L && lane <= K)
         ot[lane] = -1;
     if (lane == 0) {
         if (acc_len)
@@ -699,32 +704,35 @@ __device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV], 
     }
 }
 
-// One pass over row L (and the draft row L when TWO): unit u = (it*NV + i)*TAIL_WAVES + w
-// holds the fp64 sum of wave w's draw weights at vector slot i of iteration it, i.e. the
-// 64*E contiguous ids it*CE + i*TAIL_WG*E + w*64*E + [0, 64*E); unit order is id order.  Two
-// register buffers alternate so that the next iteration's loads are in flight while the
-// current one is weighed.
+// A pass over row L (and the draft row L when TWO) for the iterations first, first + step, ...
+// below nit: unit u = (it*NV + i)*TAIL_WAVES + w holds the fp64 sum of wave w's draw weights
+// at vector slot i of iteration it, i.e. the 64*E contiguous ids it*CE + i*TAIL_WG*E + w*64*E
+// + [0, 64*E); unit order is id order.  Two register buffers alternate so that the next
+// iteration's loads are in flight while the current one is weighed.
 template <int DT, int MODE, int NV, bool TWO>
-__device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit, bool target_law,
-                                               const SeqInfo &si, const Scale &sp,
-                                               const Scale &sq, double *units)
+__device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit, int first,
+                                               int step, bool target_law, const SeqInfo &si,
+                                               const Scale &sp, const Scale &sq, double *units)
 {
     constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV * Elt<DT>::EPV;
     const int t0 = threadIdx.x * E;
     uint4 a0[NV], q0[NV], a1[NV], q1[NV];
     float vs[NV];
-    tail_load<DT, NV, TWO>(r, t0, V, a0, q0);
-    for (int it = 0; it < nit; it += 2) {
-        if (it + 1 < nit)
-            tail_load<DT, NV, TWO>(r, (it + 1) * CE + t0, V, a1, q1);
+    if (first >= nit)
+        return;
+    tail_load<DT, NV, TWO>(r, first * CE + t0, V, a0, q0);
+    for (int it = first; it < nit; it += 2 * step) {
+        const int it1 = it + step;
+        if (it1 < nit)
+            tail_load<DT, NV, TWO>(r, it1 * CE + t0, V, a1, q1);
         tail_weigh<DT, MODE, NV, TWO>(r, it * CE + t0, V, target_law, si, sp, sq, a0, q0, vs);
         tail_store_units<NV>(it, vs, units);
-        if (it + 1 < nit) {
-            if (it + 2 < nit)
-                tail_load<DT, NV, TWO>(r, (it + 2) * CE + t0, V, a0, q0);
-            tail_weigh<DT, MODE, NV, TWO>(r, (it + 1) * CE + t0, V, target_law, si, sp, sq, a1,
-                                          q1, vs);
-            tail_store_units<NV>(it + 1, vs, units);
+        if (it1 < nit) {
+            if (it1 + step < nit)
+                tail_load<DT, NV, TWO>(r, (it1 + step) * CE + t0, V, a0, q0);
+            tail_weigh<DT, MODE, NV, TWO>(r, it1 * CE + t0, V, target_law, si, sp, sq, a1, q1,
+                                          vs);
+            tail_store_units<NV>(it1, vs, units);
         }
     }
 }
@@ -829,56 +837,105 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
                             si.Sp);
 }
 
-// One 1024-thread workgroup per sequence, after the row statistics (with early exit: alive[b]
-// says whether all rows were read, else only the first `prefix` positions): the accept phase
-// (merge, gather, accept tests, L), then one pass over row L (and draft row L) into unit sums
-// in LDS, then the unit holding t = u_K * W and the id inside it.  If rounding left the
-// residual empty, the pass is repeated with the target law p_L (essentially never taken).
-// Dynamic LDS: the staged partials during the accept phase, the unit sums afterwards.
-template <int DT, int MODE>
-__global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
-                                                  const char *__restrict__ drf,
-                                                  const int32_t *__restrict__ tokens,
-                                                  const float *__restrict__ unif, int K, int V,
-                                                  int nch, Scale sp, Scale sq,
-                                                  const float2 *__restrict__ part,
-                                                  int32_t *acc_len, int32_t *out_tokens,
-                                                  float *out_probs, float *draw_probs,
-                                                  const int *alive, int prefix, int mask_probs)
+// Arguments of k_tail.
+struct TailArgs {
+    const char *tgt, *drf;
+    const int32_t *tokens;
+    const float *unif;
+    const float2 *part;
+    int32_t *acc_len, *out_tokens;
+    float *out_probs, *draw_probs;
+    const int *alive;   // early exit: alive[b] = 1 if every row was read, else the first
+                        // `prefix` positions were; NULL: every row was read
+    double *gunits;     // split > 1: [B][nu_stride] the unit sums of each sequence's row pass
+    int *gcount;        // split > 1: [B] workgroups done with their share; 0 between calls
+    Scale sp, sq;
+    int K, V, nch, prefix, mask_probs, split, nu_stride;
+};
+
+// `split` workgroups of 1024 threads per sequence, after the row statistics.  Each runs the
+// accept phase (merge, gather, accept tests, L: the same decisions in every one; the first
+// writes the outputs), then weighs its share of the pass over row L (and the draft row L),
+// iterations g, g + split, ..., into unit sums in LDS.  With one workgroup it then finds the
+// unit holding t = u_K * W and the id inside it.  With several, each copies its unit sums to
+// the workspace (device-coherent stores, waited for) and counts itself in; the last to arrive
+// reads the others' sums (device-coherent loads), resets the count and draws.  If rounding left the residual
+// empty, that workgroup repeats the whole pass with the target law p_L (essentially never
+// taken).  Dynamic LDS: the staged partials during the accept phase, the unit sums afterwards.
+template <int DT, int MODE, bool SPLIT>
+__global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
 {
     extern __shared__ double dyn[];
     __shared__ SeqInfo s_info;
-    __shared__ int s_unit, s_fb;
+    __shared__ int s_unit, s_fb, s_last;
     __shared__ double s_base, s_t;
     constexpr int E = Elt<DT>::EPV;
-    const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // SPLIT: a.split workgroups share each sequence; else one, and this compiles to the plain
+    // single-workgroup pass
+    const int G = SPLIT ? a.split : 1, K = a.K, V = a.V;
+    const int b = SPLIT ? blockIdx.x / G : blockIdx.x, g = SPLIT ? blockIdx.x - b * G : 0;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     // rows read by this call: every position, or with early exit the first `prefix` ones for
     // a sequence that was not alive after them
-    const int npos = (alive == nullptr || alive[b]) ? K + 1 : prefix;
-    accept_phase<DT, MODE>(tgt, drf, tokens, unif, b, K, V, nch, npos, mask_probs != 0, sp, sq,
-                           part, reinterpret_cast<float2 *>(dyn), acc_len, out_tokens, out_probs,
+    const int npos = (a.alive == nullptr || a.alive[b]) ? K + 1 : a.prefix;
+    accept_phase<DT, MODE>(a.tgt, a.drf, a.tokens, a.unif, b, K, V, a.nch, npos,
+                           a.mask_probs != 0, g == 0, a.sp, a.sq, a.part,
+                           reinterpret_cast<float2 *>(dyn), a.acc_len, a.out_tokens, a.out_probs,
                            &s_info);
     __syncthreads();
     const SeqInfo si = s_info;
     if (si.L < 0)
         return;
-    const DrawRows r = draw_rows<DT, MODE>(tgt, drf, b, K, V, si.L);
+    const DrawRows r = draw_rows<DT, MODE>(a.tgt, a.drf, b, K, V, si.L);
     // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
     const bool two = (MODE == CONTRASTIVE) || r.two;
     const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
-    const int nit = (V + ce - 1) / ce, nu = nit * nv * TAIL_WAVES;
-    const float u01 = unif[(size_t)b * (K + 1) + K];
-    int32_t *out = out_tokens + (size_t)b * (K + 1) + si.L;
-    float *out_prob = draw_probs ? draw_probs + b : nullptr;
+    const int nit = (V + ce - 1) / ce, per_it = nv * TAIL_WAVES, nu = nit * per_it;
+    const float u01 = a.unif[(size_t)b * (K + 1) + K];
+    int32_t *out = a.out_tokens + (size_t)b * (K + 1) + si.L;
+    float *out_prob = a.draw_probs ? a.draw_probs + b : nullptr;
     double *units = dyn;
     for (int pass = 0; pass < 2; ++pass) {
         const bool target_law = (pass == 1);
+        // the first pass is shared by the sequence's workgroups; a repeat is done by one alone
+        const int first = (pass == 0) ? g : 0, step = (pass == 0) ? G : 1;
         if (two)
-            tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, target_law, si, sp, sq, units);
+            tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, first, step, target_law, si, a.sp,
+                                                    a.sq, units);
         else if constexpr (MODE == SAMPLING)
-            tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, target_law, si, sp, sq,
-                                                         units);
+            tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, first, step, target_law, si,
+                                                         a.sp, a.sq, units);
         __syncthreads();
+        if (SPLIT && pass == 0) {
+            double *gu = a.gunits + (size_t)b * a.nu_stride;
+            if (w == 0) {
+                // The sums go out as device-coherent stores, and the wave waits until they
+                // are acknowledged before it counts in, so a workgroup that sees the count
+                // complete reads every share with device-coherent loads.  (A device fence
+                // would also write back the whole L2, which costs more than the draw.)
+                for (int it = g; it < nit; it += G)
+                    for (int k = lane; k < per_it; k += 64)
+                        __hip_atomic_store(gu + it * per_it + k, units[it * per_it + k],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                int last = 0;
+                if (lane == 0)
+                    last = (__hip_atomic_fetch_add(a.gcount + b, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == G - 1);
+                last = __shfl(last, 0);
+                if (last && lane == 0)  // every share is in: ready for the next call
+                    __hip_atomic_store(a.gcount + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0)
+                    s_last = last;
+            }
+            __syncthreads();
+            if (!s_last)
+                return;
+            for (int k = t; k < nu; k += TAIL_WG)
+                if ((k / per_it) % G != g)
+                    units[k] = __hip_atomic_load(gu + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+        }
         if (w == 0) {
             double base, tt;
             int fb;
@@ -894,11 +951,12 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const char *__restrict__ tgt,
         const int us = s_unit;
         if (us >= 0) {
             if (w == 0)
-                search_unit<DT, MODE>(r, si, V, nv, us, s_base, s_t, s_fb != 0, target_law, sp,
-                                      sq, out, out_prob);
+                search_unit<DT, MODE>(r, si, V, nv, us, s_base, s_t, s_fb != 0, target_law, a.sp,
+                                      a.sq, out, out_prob);
             return;
         }
         // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
+        __syncthreads();  // find_unit has read the units the repeat overwrites
     }
     if (t == 0) {  // a row without finite logits: outside the contract
         *out = -1;
@@ -1297,6 +1355,62 @@ __global__ __launch_bounds__(TAIL_WG) void k_quantile_cut(const float *__restric
 
 namespace {
 
+// Workgroups per sequence for the tail: enough to give every compute unit a share of the
+// draws when the batch is small (at most TAIL_MAX_SPLIT, at most one per pass iteration, and
+// only for batches the workspace's unit-sum buffer holds).
+int tail_split(const Workspace &ws, int dtype, int B, int V)
+{
+    if (B < 1 || B > ws.split_batch)
+        return 1;
+    const int ce = TAIL_WG * NV_TAIL * elems_per_vec(dtype);
+    const int nit = (V + ce - 1) / ce;
+    int g = ws.num_cus / B;
+    g = g < TAIL_MAX_SPLIT ? g : TAIL_MAX_SPLIT;
+    g = g < nit ? g : nit;
+    return g > 1 ? g : 1;
+}
+
+TailArgs tail_args(const Workspace &ws, int dtype, int B, int K, int V, int nch, const Scale &sp,
+                   const Scale &sq, const void *tgt, const void *drf, const int32_t *tokens,
+                   const float *unif, int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                   float *draw_probs, const int *alive, int prefix, int mask_probs)
+{
+    TailArgs a;
+    a.tgt = static_cast<const char *>(tgt);
+    a.drf = static_cast<const char *>(drf);
+    a.tokens = tokens;
+    a.unif = unif;
+    a.part = ws.part;
+    a.acc_len = acc_len;
+    a.out_tokens = out_tokens;
+    a.out_probs = out_probs;
+    a.draw_probs = draw_probs;
+    a.alive = alive;
+    a.gunits = ws.gunits;
+    a.gcount = ws.gcount;
+    a.sp = sp;
+    a.sq = sq;
+    a.K = K;
+    a.V = V;
+    a.nch = nch;
+    a.prefix = prefix;
+    a.mask_probs = mask_probs;
+    a.split = tail_split(ws, dtype, B, V);
+    a.nu_stride = ws.nu_stride;
+    return a;
+}
+
+template <int DT, int MODE>
+void launch_tail(const TailArgs &a, int B, size_t lds, hipStream_t stream)
+{
+    if (a.split > 1)
+        hipLaunchKernelGGL((k_tail<DT, MODE, true>), dim3((unsigned)(B * a.split)),
+                           dim3(TAIL_WG), lds, stream, a);
+    else
+        hipLaunchKernelGGL((k_tail<DT, MODE, false>), dim3((unsigned)B), dim3(TAIL_WG), lds,
+                           stream, a);
+}
+
 struct Timer {
     const Launch &ln;
     int kind;
@@ -1336,10 +1450,9 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
     }
     {
         Timer tm(ln, KIND_TAIL);
-        hipLaunchKernelGGL((k_tail<DT, MODE>), dim3(B), dim3(TAIL_WG),
-                           tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
-                           sp, sq, ws.part, acc_len, out_tokens, out_probs, draw_probs, nullptr,
-                           K + 1, 0);
+        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
+                                     out_tokens, out_probs, draw_probs, nullptr, K + 1, 0);
+        launch_tail<DT, MODE>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
     }
     return hipGetLastError();
 }
@@ -1401,10 +1514,9 @@ hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, 
     }
     {
         Timer tm(ln, KIND_TAIL);
-        hipLaunchKernelGGL((k_tail<DT, SAMPLING>), dim3(B), dim3(TAIL_WG),
-                           tail_lds_bytes(DT, K, V, nch), ln.stream, t, d, tokens, unif, K, V, nch,
-                           sp, sp, ws.part, acc_len, out_tokens, out_probs, nullptr, alive,
-                           prefix, 1);
+        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sp, tgt, drf, tokens, unif, acc_len,
+                                     out_tokens, out_probs, nullptr, alive, prefix, 1);
+        launch_tail<DT, SAMPLING>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
     }
     return hipGetLastError();
 }

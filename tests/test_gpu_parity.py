@@ -291,3 +291,17 @@ def test_capacity_limits(mode, dtype, B, K, V):
         _report("%s %s B=%d K=%d V=%d" % (mode, synth.DTYPE_NAMES[dtype], B, K, V), rep)
     finally:
         sv.specverify_destroy(h)
+
+
+def test_split_draw_matches_single_workgroup_draw(ctx):
+    """A batch above half the CU count draws each sequence with one workgroup; a small batch
+    shares each draw among several.  The same sequences must come out bit for bit the same,
+    call after call (the arrival counts return to zero)."""
+    w = synth.make_sampling(160, 6, 70000, BF16, 0.8, seed=44, target_sigma=3.0, draft_sigma=1.3)
+    full = run(ctx, w)
+    for rep in range(3):
+        for idx in ([0, 1, 2, 3], list(range(16)), [5, 17, 99]):
+            g = run(ctx, w.subset(idx))
+            assert np.array_equal(g.accepted_len, full.accepted_len[idx]), (rep, idx)
+            assert np.array_equal(g.out_tokens, full.out_tokens[idx]), (rep, idx)
+            assert np.array_equal(g.out_probs, full.out_probs[idx]), (rep, idx)
