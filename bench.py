@@ -53,6 +53,8 @@ WORKLOADS = {
             "k_quantile_cut", None),
     "early": ("sampling verify with early exit B=256 K=8 V=128256 bf16 logits T=0.7",
               "row_stats", "k_stats_prefix<bf16> (positions 0-1 of every sequence)", None),
+    "early_c5": ("contrastive verify with early exit B=128 K=4 V=152064 bf16 logits tau=1",
+                 "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)", None),
 }
 METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
@@ -136,9 +138,9 @@ def main():
     desc, kind, kname, traffic_file = WORKLOADS[args.workload]
     if args.workload == "cut":
         return bench_cut(args, desc, kind, kname)
-    early = args.workload == "early"
-    w = (synth.CONFIGS.get("c3" if early else args.workload)
-         or synth.NEXT_CONFIGS[args.workload])()
+    early = args.workload in ("early", "early_c5")
+    base = {"early": "c3", "early_c5": "c5"}.get(args.workload, args.workload)
+    w = (synth.CONFIGS.get(base) or synth.NEXT_CONFIGS[base])()
     B, K, V = w.B, w.K, w.V
     log("generated %s (seed %d); uploading %.3f GB of logits x2"
         % (desc, w.seed, w.logit_bytes / 1e9))
@@ -171,8 +173,9 @@ def main():
         elif w.mode == synth.GREEDY:
             sv.specverify_run_greedy(ctx, stream, w.dtype, B, K, V, tg, toks, acc, out)
         elif early:
-            sv.specverify_run_sampling_early_exit(ctx, stream, w.dtype, B, K, V, w.temperature, tg,
-                                                  dr, toks, unif, acc, out, probs)
+            fn = (sv.specverify_run_sampling_early_exit if w.mode == synth.SAMPLING
+                  else sv.specverify_run_contrastive_early_exit)
+            fn(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr, toks, unif, acc, out, probs)
         elif w.mode == synth.CONTRASTIVE:
             sv.specverify_run_contrastive(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
                                           toks, unif, acc, out, probs)
@@ -225,7 +228,8 @@ def main():
     elif early:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"
-        kern_bytes = 4 * B * V * w.target.itemsize   # target and draft rows 0 and 1
+        # positions 0 and 1: target and draft rows (sampling) or expert and amateur rows
+        kern_bytes = 4 * B * V * w.target.itemsize
     else:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"

@@ -128,6 +128,18 @@ int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, in
                                       int32_t *out_tokens, float *out_probs);
 
 /*
+ * Contrastive-target verify with early exit: accepted_len and out_tokens exactly as
+ * specverify_run_contrastive, reading each sequence's row pairs only up to its first
+ * rejection (as specverify_run_sampling_early_exit).  out_probs for j <= L, NaN after.
+ * Same arguments, layouts and errors as specverify_run_contrastive.
+ */
+int specverify_run_contrastive_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                         int K, int V, float tau, const void *expert_logits,
+                                         const void *amateur_logits, const int32_t *draft_tokens,
+                                         const float *uniforms, int32_t *accepted_len,
+                                         int32_t *out_tokens, float *out_probs);
+
+/*
  * Greedy blockwise verify.  g_j = the lowest id among the maxima of l_target[b,j,:]
  * (raw value comparison) for j in [0, K]; L = the first j < K with proposals[b,j] != g_j,
  * else K.  target_logits [B][K+1][V] (dtype), proposals [B][K] int32.

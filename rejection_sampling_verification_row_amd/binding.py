@@ -66,6 +66,8 @@ def load():
         lib.specverify_run_contrastive.argtypes = [vp, vp, i, i, i, i, f, vp, vp, vp, vp, vp, vp,
                                                    vp]
         lib.specverify_run_contrastive.restype = i
+        lib.specverify_run_contrastive_early_exit.argtypes = lib.specverify_run_contrastive.argtypes
+        lib.specverify_run_contrastive_early_exit.restype = i
         lib.specverify_run_greedy.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
         lib.specverify_run_greedy.restype = i
         lib.specverify_sample.argtypes = [vp, vp, i, i, i, f, vp, vp, vp, vp]
@@ -156,6 +158,15 @@ def specverify_run_contrastive(ctx, stream, dtype, B, K, V, tau, expert_logits, 
         ctx, _stream(stream), dtype, B, K, V, float(tau), _ptr(expert_logits),
         _ptr(amateur_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
         _ptr(out_tokens), _ptr(out_probs)), "specverify_run_contrastive")
+
+
+def specverify_run_contrastive_early_exit(ctx, stream, dtype, B, K, V, tau, expert_logits,
+                                          amateur_logits, draft_tokens, uniforms, accepted_len,
+                                          out_tokens, out_probs=None) -> None:
+    _check(load().specverify_run_contrastive_early_exit(
+        ctx, _stream(stream), dtype, B, K, V, float(tau), _ptr(expert_logits),
+        _ptr(amateur_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_contrastive_early_exit")
 
 
 def specverify_run_greedy(ctx, stream, dtype, B, K, V, target_logits, proposals, accepted_len,

@@ -88,9 +88,12 @@ void note_call(specverify_ctx *ctx, hipEvent_t *ev, unsigned kinds)
     }
 }
 
+// sampling or contrastive verify, reading every row or (early_exit) only up to each
+// sequence's first rejection
 int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, int B, int K, int V,
                       float temperature, const void *tgt, const void *drf, const int32_t *tokens,
-                      const float *unif, int32_t *acc_len, int32_t *out_tokens, float *out_probs)
+                      const float *unif, int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                      bool early_exit)
 {
     int rc = check_common(ctx, dtype, B, K, V);
     if (rc != SPECVERIFY_OK)
@@ -115,9 +118,19 @@ int run_sampling_like(specverify_ctx *ctx, void *stream, int mode, int dtype, in
     const sv::Scale sq = (mode == sv::CONTRASTIVE) ? sv::make_scale(1.0) : sp;
     hipEvent_t *ev = next_events(ctx);
     sv::Launch ln{static_cast<hipStream_t>(stream), ev, ctx->prof_mask};
-    hipError_t e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
-                                       unif, acc_len, out_tokens, out_probs, nullptr);
-    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_TAIL));
+    hipError_t e;
+    unsigned kinds = (1u << sv::KIND_STATS) | (1u << sv::KIND_TAIL);
+    if (early_exit) {
+        // the survivors' rows: 24 256-thread workgroups per compute unit, most of which take
+        // one or two items (fewer left the last items to a few workgroups)
+        e = sv::launch_early_exit(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens,
+                                  unif, acc_len, out_tokens, out_probs, 24 * ctx->num_cus);
+        kinds |= (1u << sv::KIND_EARLY_ACCEPT) | (1u << sv::KIND_EARLY_REST);
+    } else {
+        e = sv::launch_sampling(ln, ctx->ws, mode, dtype, B, K, V, sp, sq, tgt, drf, tokens, unif,
+                                acc_len, out_tokens, out_probs, nullptr);
+    }
+    note_call(ctx, ev, kinds);
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 
@@ -201,7 +214,7 @@ int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, in
 {
     return run_sampling_like(ctx, hip_stream, sv::SAMPLING, dtype, B, K, V, temperature,
                              target_logits, draft_logits, draft_tokens, uniforms, accepted_len,
-                             out_tokens, out_probs);
+                             out_tokens, out_probs, false);
 }
 
 int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
@@ -212,7 +225,7 @@ int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype,
 {
     return run_sampling_like(ctx, hip_stream, sv::CONTRASTIVE, dtype, B, K, V, tau, expert_logits,
                              amateur_logits, draft_tokens, uniforms, accepted_len, out_tokens,
-                             out_probs);
+                             out_probs, false);
 }
 
 int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
@@ -247,37 +260,20 @@ int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, in
                                       const float *uniforms, int32_t *accepted_len,
                                       int32_t *out_tokens, float *out_probs)
 {
-    int rc = check_common(ctx, dtype, B, K, V);
-    if (rc != SPECVERIFY_OK)
-        return rc;
-    if (bad_temperature(temperature))
-        return SPECVERIFY_EINVAL;
-    if (B == 0)
-        return SPECVERIFY_OK;
-    if (!target_logits || !uniforms || !accepted_len || !out_tokens ||
-        (K > 0 && (!draft_logits || !draft_tokens)))
-        return SPECVERIFY_EINVAL;
-    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
-    if (!aligned_to(target_logits, es) || (draft_logits && !aligned_to(draft_logits, es)) ||
-        (draft_tokens && !aligned_to(draft_tokens, 4)) || !aligned_to(uniforms, 4) ||
-        !aligned_to(accepted_len, 4) || !aligned_to(out_tokens, 4) ||
-        (out_probs && !aligned_to(out_probs, 4)))
-        return SPECVERIFY_EINVAL;
-    DeviceGuard g(ctx->device);
-    if (g.err != hipSuccess)
-        return SPECVERIFY_EHIP;
-    const sv::Scale sp = sv::make_scale((double)temperature);
-    hipEvent_t *ev = next_events(ctx);
-    sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
-    // the rest of the alive rows: 24 256-thread workgroups per compute unit, most of which
-    // take one or two items (fewer left the last items to a few workgroups)
-    hipError_t e = sv::launch_sampling_early_exit(ln, ctx->ws, dtype, B, K, V, sp, target_logits,
-                                                  draft_logits, draft_tokens, uniforms,
-                                                  accepted_len, out_tokens, out_probs,
-                                                  24 * ctx->num_cus);
-    note_call(ctx, ev, (1u << sv::KIND_STATS) | (1u << sv::KIND_EARLY_ACCEPT) |
-                           (1u << sv::KIND_EARLY_REST) | (1u << sv::KIND_TAIL));
-    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+    return run_sampling_like(ctx, hip_stream, sv::SAMPLING, dtype, B, K, V, temperature,
+                             target_logits, draft_logits, draft_tokens, uniforms, accepted_len,
+                             out_tokens, out_probs, true);
+}
+
+int specverify_run_contrastive_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                         int K, int V, float tau, const void *expert_logits,
+                                         const void *amateur_logits, const int32_t *draft_tokens,
+                                         const float *uniforms, int32_t *accepted_len,
+                                         int32_t *out_tokens, float *out_probs)
+{
+    return run_sampling_like(ctx, hip_stream, sv::CONTRASTIVE, dtype, B, K, V, tau, expert_logits,
+                             amateur_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                             out_probs, true);
 }
 
 int specverify_sample(specverify_ctx *ctx, void *hip_stream, int dtype, int N, int V,

@@ -125,15 +125,15 @@ hipError_t launch_sampling(const Launch &ln, const Workspace &ws, int mode, int 
                            int32_t *acc_len, int32_t *out_tokens, float *out_probs,
                            float *draw_probs);
 
-// Sampling verify reading rows only up to each sequence's first rejection: the first
-// EARLY_PREFIX positions of every sequence, then the rest of the sequences that accepted
-// them (k_stats_rest runs rest_grid workgroups over that work).  Tokens and accepted_len as
-// launch_sampling; out_probs for j <= L only (NaN after).
-hipError_t launch_sampling_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B,
-                                      int K, int V, const Scale &sp, const void *tgt,
-                                      const void *drf, const int32_t *tokens, const float *unif,
-                                      int32_t *acc_len, int32_t *out_tokens, float *out_probs,
-                                      int rest_grid);
+// Sampling or contrastive verify (mode) reading rows only up to each sequence's first
+// rejection: the first EARLY_PREFIX positions of every sequence, then the rest of the
+// sequences that accepted them (the rest pass runs rest_grid workgroups over that work).
+// Tokens and accepted_len as launch_sampling; out_probs for j <= L only (NaN after).
+hipError_t launch_early_exit(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,
+                             int K, int V, const Scale &sp, const Scale &sq, const void *tgt,
+                             const void *drf, const int32_t *tokens, const float *unif,
+                             int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                             int rest_grid);
 
 // greedy verify over [B][K+1][H][V] head logits (head 0 verifies) plus next_props [B][H-1],
 // the first argmaxes of heads 1..H-1 at the emitted position

@@ -496,18 +496,16 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
     store_wave_partials(wave_stats(m, s, sc), part + (size_t)blockIdx.x * WAVES);
 }
 
-// one workgroup per (row pair (b, j), chunk): target values l_e - l_a (fp32), draft values l_a;
-// the pair's expert row gives p_j's partials (row j of the sequence), its amateur row q_j's
-// (row K+1+j, j < K)
+// One chunk of the row pair (b, j): target values l_e - l_a (fp32), draft values l_a.  The
+// pair's expert row gives p_j's partials (row j of the sequence), its amateur row q_j's (row
+// K+1+j, j < K).
 template <int DT>
-__global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
-                                                          const char *__restrict__ am, int K, int V,
-                                                          int nch, Scale sp, Scale sq, float2 *part)
+__device__ __forceinline__ void pair_chunk_stats(const char *ex, const char *am, int b, int j,
+                                                 int c, int K, int V, int nch, const Scale &sp,
+                                                 const Scale &sq, float2 *part)
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
     const int P = K + 1, R = 2 * K + 1;
-    const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
-    const int b = pr / P, j = pr - b * P;
     const size_t off = ((size_t)b * P + j) * (size_t)V * BY;
     const char *re = ex + off, *ra = am + off;
     const int cbase = c * WG * NV_PAIR * E;
@@ -539,6 +537,17 @@ __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict
         store_wave_partials(wave_stats(m, s, sq),
                             part + (((size_t)b * R + K + 1 + j) * nch + c) * WAVES);
     }
+}
+
+// one workgroup per (row pair (b, j), chunk)
+template <int DT>
+__global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
+                                                          const char *__restrict__ am, int K, int V,
+                                                          int nch, Scale sp, Scale sq, float2 *part)
+{
+    const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
+    const int b = pr / (K + 1), j = pr - b * (K + 1);
+    pair_chunk_stats<DT>(ex, am, b, j, c, K, V, nch, sp, sq, part);
 }
 
 // ------------------------------------------------------------------ residual / bonus draw
@@ -1012,7 +1021,7 @@ __global__ __launch_bounds__(WG) void k_stats_prefix(const char *__restrict__ tg
 // One 256-thread workgroup per sequence: the accept tests at positions 0..prefix-1 on the same
 // merged statistics as k_tail.  A sequence with valid ids that accepts all of them is alive:
 // alive[b] = 1 and it is appended to list (count = list length); else alive[b] = 0.
-template <int DT>
+template <int DT, int MODE>
 __global__ __launch_bounds__(WG) void k_alive(const char *__restrict__ tgt,
                                               const char *__restrict__ drf,
                                               const int32_t *__restrict__ tokens,
@@ -1027,7 +1036,7 @@ __global__ __launch_bounds__(WG) void k_alive(const char *__restrict__ tgt,
     const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     Draft d = {0, 0.0f, 0.0f, 0.0f, false};
     if (w == 0)
-        d = gather_draft<DT, SAMPLING>(tgt, drf, tokens, unif, b, K, V, lane);
+        d = gather_draft<DT, MODE>(tgt, drf, tokens, unif, b, K, V, lane);
     merge_rows<WG>(part, b, K, nch, prefix, sp, sq, stage, sM, sS);
     if (w != 0)
         return;
@@ -1069,6 +1078,40 @@ __global__ __launch_bounds__(WG) void k_stats_rest(const char *__restrict__ tgt,
                                : tgt + ((size_t)b * (K + 1) + j) * (size_t)V * BY;
         const int r = draft ? K + 1 + j : j;
         row_chunk_stats<DT>(rp, V, c, sc, part + (((size_t)b * (2 * K + 1) + r) * nch + c) * WAVES);
+        __syncthreads();  // the LDS of store_wave_partials is reused by the next item
+    }
+}
+
+// contrastive: the row pairs of positions 0..prefix-1 of every sequence (prefix <= K);
+// workgroup 0 also clears the survivor count for k_alive
+template <int DT>
+__global__ __launch_bounds__(WG) void k_pairs_prefix(const char *__restrict__ ex,
+                                                     const char *__restrict__ am, int K, int V,
+                                                     int nch, int prefix, Scale sp, Scale sq,
+                                                     float2 *part, int *count)
+{
+    const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
+    const int b = pr / prefix, j = pr - b * prefix;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *count = 0;
+    pair_chunk_stats<DT>(ex, am, b, j, c, K, V, nch, sp, sq, part);
+}
+
+// contrastive: the row pairs of positions prefix..K of the listed sequences, item i of
+// count * (K+1-prefix) * nch taken by workgroup i mod gridDim (as k_stats_rest)
+template <int DT>
+__global__ __launch_bounds__(WG) void k_pairs_rest(const char *__restrict__ ex,
+                                                   const char *__restrict__ am, int K, int V,
+                                                   int nch, int prefix, Scale sp, Scale sq,
+                                                   float2 *part, const int *__restrict__ list,
+                                                   const int *__restrict__ count)
+{
+    const int per = (K + 1 - prefix) * nch;
+    const long total = (long)(*count) * per;
+    for (long item = blockIdx.x; item < total; item += gridDim.x) {
+        const int a = (int)(item / per), rem = (int)(item - (long)a * per);
+        const int lr = rem / nch, c = rem - lr * nch;
+        pair_chunk_stats<DT>(ex, am, list[a], prefix + lr, c, K, V, nch, sp, sq, part);
         __syncthreads();  // the LDS of store_wave_partials is reused by the next item
     }
 }
@@ -1476,47 +1519,64 @@ hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int 
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int MODE>
 hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, int V,
-                           const Scale &sp, const void *tgt, const void *drf,
+                           const Scale &sp, const Scale &sq, const void *tgt, const void *drf,
                            const int32_t *tokens, const float *unif, int32_t *acc_len,
                            int32_t *out_tokens, float *out_probs, int rest_grid)
 {
     const char *t = static_cast<const char *>(tgt);
     const char *d = static_cast<const char *>(drf);
-    const int nch = num_chunks(NV_STATS, DT, V);
+    const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
     const int prefix = EARLY_PREFIX < K + 1 ? EARLY_PREFIX : K + 1;
     const int *alive = nullptr;
     if (prefix == K + 1) {  // every position is in the prefix: one full pass
         Timer tm(ln, KIND_STATS);
-        hipLaunchKernelGGL(k_stats_sampling<DT>, dim3((unsigned)((size_t)B * (2 * K + 1) * nch)),
-                           dim3(WG), 0, ln.stream, t, d, K, V, nch, sp, ws.part);
+        if (MODE == SAMPLING)
+            hipLaunchKernelGGL(k_stats_sampling<DT>,
+                               dim3((unsigned)((size_t)B * (2 * K + 1) * nch)), dim3(WG), 0,
+                               ln.stream, t, d, K, V, nch, sp, ws.part);
+        else
+            hipLaunchKernelGGL(k_stats_contrastive<DT>, dim3((unsigned)((size_t)B * (K + 1) * nch)),
+                               dim3(WG), 0, ln.stream, t, d, K, V, nch, sp, sq, ws.part);
     } else {
         {
             Timer tm(ln, KIND_STATS);
-            hipLaunchKernelGGL(k_stats_prefix<DT>,
-                               dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0,
-                               ln.stream, t, d, K, V, nch, prefix, sp, ws.part, ws.count);
+            if (MODE == SAMPLING)
+                hipLaunchKernelGGL(k_stats_prefix<DT>,
+                                   dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0,
+                                   ln.stream, t, d, K, V, nch, prefix, sp, ws.part, ws.count);
+            else
+                hipLaunchKernelGGL(k_pairs_prefix<DT>, dim3((unsigned)((size_t)B * prefix * nch)),
+                                   dim3(WG), 0, ln.stream, t, d, K, V, nch, prefix, sp, sq,
+                                   ws.part, ws.count);
         }
         {
             Timer tm(ln, KIND_EARLY_ACCEPT);
-            hipLaunchKernelGGL(k_alive<DT>, dim3(B), dim3(WG), 0, ln.stream, t, d, tokens, unif,
-                               K, V, nch, prefix, sp, sp, ws.part, ws.alive, ws.list, ws.count);
+            hipLaunchKernelGGL((k_alive<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, tokens,
+                               unif, K, V, nch, prefix, sp, sq, ws.part, ws.alive, ws.list,
+                               ws.count);
         }
         {
             Timer tm(ln, KIND_EARLY_REST);
-            const size_t items = (size_t)B * (2 * K + 1 - 2 * prefix) * nch;
+            const size_t rows = (MODE == SAMPLING) ? (size_t)(2 * K + 1 - 2 * prefix)
+                                                   : (size_t)(K + 1 - prefix);
+            const size_t items = (size_t)B * rows * nch;
             const unsigned grid = (unsigned)(items < (size_t)rest_grid ? items : rest_grid);
-            hipLaunchKernelGGL(k_stats_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K, V,
-                               nch, prefix, sp, ws.part, ws.list, ws.count);
+            if (MODE == SAMPLING)
+                hipLaunchKernelGGL(k_stats_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
+                                   V, nch, prefix, sp, ws.part, ws.list, ws.count);
+            else
+                hipLaunchKernelGGL(k_pairs_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
+                                   V, nch, prefix, sp, sq, ws.part, ws.list, ws.count);
         }
         alive = ws.alive;
     }
     {
         Timer tm(ln, KIND_TAIL);
-        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sp, tgt, drf, tokens, unif, acc_len,
+        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
                                      out_tokens, out_probs, nullptr, alive, prefix, 1);
-        launch_tail<DT, SAMPLING>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
+        launch_tail<DT, MODE>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
     }
     return hipGetLastError();
 }
@@ -1544,14 +1604,16 @@ hipError_t greedy_heads_impl(const Launch &ln, const Workspace &ws, int B, int K
 
 }  // namespace
 
-hipError_t launch_sampling_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B,
-                                      int K, int V, const Scale &sp, const void *tgt,
-                                      const void *drf, const int32_t *tokens, const float *unif,
-                                      int32_t *acc_len, int32_t *out_tokens, float *out_probs,
-                                      int rest_grid)
+hipError_t launch_early_exit(const Launch &ln, const Workspace &ws, int mode, int dtype, int B,
+                             int K, int V, const Scale &sp, const Scale &sq, const void *tgt,
+                             const void *drf, const int32_t *tokens, const float *unif,
+                             int32_t *acc_len, int32_t *out_tokens, float *out_probs,
+                             int rest_grid)
 {
-    auto f = dtype == 1 ? early_exit_impl<1> : early_exit_impl<0>;
-    return f(ln, ws, B, K, V, sp, tgt, drf, tokens, unif, acc_len, out_tokens, out_probs,
+    auto f = (mode == SAMPLING)
+                 ? (dtype == 1 ? early_exit_impl<1, SAMPLING> : early_exit_impl<0, SAMPLING>)
+                 : (dtype == 1 ? early_exit_impl<1, CONTRASTIVE> : early_exit_impl<0, CONTRASTIVE>);
+    return f(ln, ws, B, K, V, sp, sq, tgt, drf, tokens, unif, acc_len, out_tokens, out_probs,
              rest_grid);
 }
 

@@ -1,5 +1,6 @@
-"""GPU parity of sampling verify with early exit (needs an MI355X): the same tokens and
-accepted lengths as the oracle and as the full-read entry point, out_probs up to L."""
+"""GPU parity of sampling and contrastive verify with early exit (needs an MI355X): the same
+tokens and accepted lengths as the oracle and as the full-read entry points, out_probs up
+to L."""
 import numpy as np
 import pytest
 import torch
@@ -31,7 +32,7 @@ def _same_as_full(ctx, w, g):
             assert np.array_equal(g.out_probs[b, :L + 1], f.out_probs[b, :L + 1])
 
 
-@pytest.mark.parametrize("cfg,sample", [("c1", None), ("c2", None), ("c3", 48)])
+@pytest.mark.parametrize("cfg,sample", [("c1", None), ("c2", None), ("c3", 48), ("c5", 40)])
 def test_early_exit_full_size(ctx, cfg, sample):
     w = synth.CONFIGS[cfg]()
     g = run_early(ctx, w)
@@ -85,3 +86,24 @@ def test_early_exit_is_deterministic(ctx):
     a, b = run_early(ctx, w), run_early(ctx, w)
     assert np.array_equal(a.out_tokens, b.out_tokens)
     assert np.array_equal(a.out_probs, b.out_probs, equal_nan=True)
+
+
+@pytest.mark.parametrize("dtype,B,K,V", [(BF16, 5, 0, 999), (F32, 6, 1, 3000), (BF16, 13, 3, 40003),
+                                         (F32, 4, 6, 20001)])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_contrastive_early_exit_small_shapes(ctx, dtype, B, K, V, misalign):
+    w = synth.make_contrastive(B, K, V, dtype, 1.3, seed=900 + B + K + V)
+    g = run_early(ctx, w, misalign=misalign)
+    compare_early(w, g, oracle.run_workload(w))
+    _same_as_full(ctx, w, g)
+
+
+def test_contrastive_early_exit_with_survivors(ctx):
+    """With l_a close to l_e / 2 and tau = 1 the contrastive target is close to the amateur's
+    law, so most sequences stay alive past the prefix and the rest pass runs too."""
+    w = synth.make_contrastive(20, 6, 5000, BF16, 1.0, seed=31, amateur_scale=0.5,
+                               amateur_sigma=0.1)
+    g = run_early(ctx, w)
+    compare_early(w, g, oracle.run_workload(w))
+    _same_as_full(ctx, w, g)
+    assert np.mean(g.accepted_len >= 2) > 0.5
