@@ -1189,51 +1189,92 @@ __global__ __launch_bounds__(WG) void k_greedy_final(const int32_t *__restrict__
         acc_len[b] = L;
 }
 
-// (max, first id) of one whole row, across the workgroup: thread t takes vectors t,
-// t + TAIL_WG, ... (ascending ids per thread, so a strict '>' keeps the first maximum), then
-// the waves and the workgroup merge by value, then lowest id.  Every thread returns the row's
-// first argmax.  An all -inf row gives id 0.
+// First argmaxes of up to HG rows at once across the workgroup: row h starts at
+// rp + h * stride (bytes).  Per round thread t loads vectors t + v*HEADS_WG (v < HV) of every row
+// (all loads issued before any compare), so a thread's ids ascend and a strict '>' keeps the
+// first maximum; then the waves and the workgroup merge by value, then lowest id.  ids[h]
+// receives row h's first argmax (0 for an all -inf row).
+constexpr int HG = 4;          // rows per group
+constexpr int HV = 2;          // vectors per thread per row and round
+constexpr int HEADS_WG = 512;  // threads per sequence: all of a large batch resident at once
+constexpr int HEADS_WAVES = HEADS_WG / 64;
+
 template <int DT>
-__device__ inline int block_row_argmax(const char *rp, int V)
+__device__ inline void block_rows_argmax(const char *rp, size_t stride, int nrows, int V, int *ids)
 {
-    constexpr int E = Elt<DT>::EPV;
-    __shared__ float s_v[TAIL_WAVES];
-    __shared__ int s_i[TAIL_WAVES];
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    __shared__ float s_v[HG][HEADS_WAVES];
+    __shared__ int s_i[HG][HEADS_WAVES];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const bool al = aligned16(rp);
-    float bv = -INFINITY;
-    int bi = (t * E < V) ? t * E : INT_MAX;
-#pragma unroll 4
-    for (int e0 = t * E; e0 < V; e0 += TAIL_WG * E) {
-        float x[E];
-        load_elems<DT>(rp, al, e0, V, -INFINITY, x);
+    bool al = true;
+    for (int h = 0; h < nrows; ++h)
+        al = al && aligned16(rp + h * stride);
+    float bv[HG];
+    int bi[HG];
 #pragma unroll
-        for (int k = 0; k < E; ++k)
-            if (x[k] > bv) {
-                bv = x[k];
-                bi = e0 + k;
-            }
+    for (int h = 0; h < HG; ++h) {
+        bv[h] = -INFINITY;
+        bi[h] = (t * E < V) ? t * E : INT_MAX;
     }
-    wave_argmax(bv, bi);
-    if (lane == 0) {
-        s_v[w] = bv;
-        s_i[w] = bi;
+    for (int e0 = t * E; e0 < V; e0 += HEADS_WG * E * HV) {
+        uint4 raw[HG][HV];
+#pragma unroll
+        for (int h = 0; h < HG; ++h)
+#pragma unroll
+            for (int v = 0; v < HV; ++v) {
+                const int e = e0 + v * HEADS_WG * E;
+                if (h < nrows && al && e + E <= V)
+                    raw[h][v] = load_stream(rp + h * stride + (size_t)e * BY);
+            }
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+            if (h >= nrows)
+                continue;
+#pragma unroll
+            for (int v = 0; v < HV; ++v) {
+                const int e = e0 + v * HEADS_WG * E;
+                if (e >= V)
+                    continue;
+                float x[E];
+                if (al && e + E <= V)
+                    Elt<DT>::unpack(raw[h][v], x);
+                else
+                    load_elems<DT>(rp + h * stride, al, e, V, -INFINITY, x);
+#pragma unroll
+                for (int k = 0; k < E; ++k)
+                    if (x[k] > bv[h]) {
+                        bv[h] = x[k];
+                        bi[h] = e + k;
+                    }
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+        wave_argmax(bv[h], bi[h]);
+        if (lane == 0) {
+            s_v[h][w] = bv[h];
+            s_i[h][w] = bi[h];
+        }
     }
     __syncthreads();
-    float v = s_v[0];
-    int id = s_i[0];
-    for (int k = 1; k < TAIL_WAVES; ++k)
-        take_better(v, id, s_v[k], s_i[k]);
-    __syncthreads();  // s_v / s_i may be reused by the next call
-    return id;
+    if (t < nrows) {
+        float v = s_v[t][0];
+        int id = s_i[t][0];
+        for (int k = 1; k < HEADS_WAVES; ++k)
+            take_better(v, id, s_v[t][k], s_i[t][k]);
+        ids[t] = id;
+    }
+    __syncthreads();  // s_v / s_i may be reused by the next group
 }
 
-// Greedy blockwise verify with the next block's proposals (one 1024-thread workgroup per
+// Greedy blockwise verify with the next block's proposals (one 512-thread workgroup per
 // sequence): head 0's row argmaxes g_j from k_argmax's partials, the longest matching prefix
 // L, the emitted g_0..g_L, then the first argmax of each of heads 1..H-1 at position L (rows
-// ((b*(K+1) + L)*H + h) of the input), the next block's proposals.
+// ((b*(K+1) + L)*H + h) of the input, up to HG of them read together), the next block's
+// proposals.
 template <int DT>
-__global__ __launch_bounds__(TAIL_WG) void k_greedy_heads(const char *__restrict__ logits,
+__global__ __launch_bounds__(HEADS_WG) void k_greedy_heads(const char *__restrict__ logits,
                                                           const int32_t *__restrict__ props,
                                                           int K, int H, int V, int nch,
                                                           const float2 *__restrict__ part,
@@ -1245,7 +1286,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_greedy_heads(const char *__restrict
     __shared__ int s_L;
     const int b = blockIdx.x, P = K + 1;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, np = nch * WAVES;
-    for (int j = w; j < P; j += TAIL_WAVES) {
+    for (int j = w; j < P; j += HEADS_WAVES) {
         const float2 *pr = part + ((size_t)b * P + j) * np;
         float v = -INFINITY;
         int id = INT_MAX;
@@ -1286,15 +1327,15 @@ __global__ __launch_bounds__(TAIL_WG) void k_greedy_heads(const char *__restrict
         return;
     int32_t *nx = next_props + (size_t)b * (H - 1);
     if (L < 0) {
-        for (int h = t + 1; h < H; h += TAIL_WG)
+        for (int h = t + 1; h < H; h += HEADS_WG)
             nx[h - 1] = -1;
         return;
     }
-    for (int h = 1; h < H; ++h) {
-        const char *rp = logits + (((size_t)b * P + L) * H + h) * (size_t)V * BY;
-        const int id = block_row_argmax<DT>(rp, V);
-        if (t == 0)
-            nx[h - 1] = id;
+    const size_t row_bytes = (size_t)V * BY;
+    for (int h0 = 1; h0 < H; h0 += HG) {
+        const int n = (H - h0 < HG) ? H - h0 : HG;
+        const char *rp = logits + (((size_t)b * P + L) * H + h0) * row_bytes;
+        block_rows_argmax<DT>(rp, row_bytes, n, V, nx + (h0 - 1));
     }
 }
 
@@ -1596,7 +1637,7 @@ hipError_t greedy_heads_impl(const Launch &ln, const Workspace &ws, int B, int K
     }
     {
         Timer tm(ln, KIND_GREEDY_EMIT);
-        hipLaunchKernelGGL(k_greedy_heads<DT>, dim3(B), dim3(TAIL_WG), 0, ln.stream, lg, props, K,
+        hipLaunchKernelGGL(k_greedy_heads<DT>, dim3(B), dim3(HEADS_WG), 0, ln.stream, lg, props, K,
                            H, V, nch, ws.part, acc_len, out_tokens, next_props);
     }
     return hipGetLastError();
