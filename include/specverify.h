@@ -31,7 +31,9 @@
  *    it and return; results are valid once the caller has synchronised that stream.
  *  - The context owns a device workspace sized at creation; one call may be in flight per
  *    context at a time (use one context per concurrent stream).  Only specverify_create
- *    allocates device memory.
+ *    allocates device memory.  The run_* calls only launch kernels (no allocation, memset
+ *    or synchronisation), so a caller may capture them in a HIP graph and replay it; replays
+ *    on one context must not overlap either.
  *  - Host-detectable errors return before anything is enqueued and leave all outputs
  *    untouched: NULL context or required pointer, negative sizes, V < 1, a non-positive or
  *    non-finite temperature, or a misaligned pointer -> SPECVERIFY_EINVAL; B, K or V above

@@ -305,3 +305,48 @@ def test_split_draw_matches_single_workgroup_draw(ctx):
             assert np.array_equal(g.accepted_len, full.accepted_len[idx]), (rep, idx)
             assert np.array_equal(g.out_tokens, full.out_tokens[idx]), (rep, idx)
             assert np.array_equal(g.out_probs, full.out_probs[idx]), (rep, idx)
+
+
+def test_calls_replay_under_hip_graph_capture(ctx):
+    """The run_* calls allocate, clear and synchronise nothing, so a caller may capture them
+    in a HIP graph: every replay (with eager work in between) must equal the eager result.
+    The small batch takes the shared-draw path, whose arrival counts must return to zero."""
+    ws = synth.make_sampling(24, 5, 40000, BF16, 0.8, seed=61, target_sigma=3.0, draft_sigma=1.2)
+    wg = synth.make_greedy(16, 6, 20000, BF16, seed=62, sigma=2.0)
+    d = {k: dev(v) for k, v in (("t", ws.target), ("d", ws.draft), ("x", ws.tokens),
+                                 ("u", ws.uniforms), ("gt", wg.target), ("gx", wg.tokens))}
+    outs = {"acc": torch.empty(24, dtype=torch.int32, device="cuda"),
+            "tok": torch.empty((24, 6), dtype=torch.int32, device="cuda"),
+            "pr": torch.empty((24, 5, 2), dtype=torch.float32, device="cuda"),
+            "eacc": torch.empty(24, dtype=torch.int32, device="cuda"),
+            "etok": torch.empty((24, 6), dtype=torch.int32, device="cuda"),
+            "gacc": torch.empty(16, dtype=torch.int32, device="cuda"),
+            "gtok": torch.empty((16, 7), dtype=torch.int32, device="cuda")}
+    s = torch.cuda.Stream()
+
+    def calls():
+        sv.specverify_run_sampling(ctx, s, BF16, 24, 5, ws.V, ws.temperature, d["t"], d["d"],
+                                   d["x"], d["u"], outs["acc"], outs["tok"], outs["pr"])
+        sv.specverify_run_sampling_early_exit(ctx, s, BF16, 24, 5, ws.V, ws.temperature, d["t"],
+                                              d["d"], d["x"], d["u"], outs["eacc"], outs["etok"])
+        sv.specverify_run_greedy(ctx, s, BF16, 16, 6, wg.V, d["gt"], d["gx"], outs["gacc"],
+                                 outs["gtok"])
+
+    with torch.cuda.stream(s):
+        calls()
+        s.synchronize()
+        ref = {k: v.clone() for k, v in outs.items()}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            calls()
+        for r in range(4):
+            for v in outs.values():
+                v.fill_(-3)
+            calls() if r == 2 else None      # eager work between replays
+            s.synchronize()
+            for v in outs.values():
+                v.fill_(-3)
+            g.replay()
+            s.synchronize()
+            for k, v in outs.items():
+                assert torch.equal(v, ref[k]), (r, k)
