@@ -1,22 +1,28 @@
 // gfx950 kernels for the batched verify-and-accept step of speculative decoding.
 //
-// A sampling or contrastive call is four launches on the caller's stream:
+// A sampling or contrastive call is two launches on the caller's stream:
 //   k_stats_*  one read of every logit row (nontemporal 128-bit loads).  Each 256-thread
-//              workgroup reduces one chunk of a row to per-wave (max, sum exp2) partials.
-//   k_accept   one workgroup per sequence merges its partials in fp64, gathers
-//              p_j(x_j), q_j(x_j), accepts iff p > 0 and u * q <= p, finds the first
-//              rejection L and records row L.
-//   k_resid    re-read of row L (target and draft, or the target alone for the bonus
-//              draw): per chunk, the sum of w = max(0, p - q) (or p).
-//   k_draw     one workgroup per sequence finds the chunk holding t = u_K * W, then the
-//              vector and the id inside it (block scans), and emits the first id whose
-//              prefix weight exceeds t.
-// A greedy blockwise call is two launches: k_argmax reduces chunks to (max, first id) and
-// k_greedy_final compares each sequence's row argmaxes with its proposals.
+//              workgroup reduces one chunk of a row to per-wave (max, sum exp2) partials;
+//              the contrastive form reads the expert and amateur rows of a position together.
+//   k_tail     one 1024-thread workgroup per sequence (or G of them sharing one draw when
+//              the batch is too small to fill the chip) merges the partials in fp64,
+//              gathers p_j(x_j) and q_j(x_j), accepts iff p > 0 and u * q <= p, finds the
+//              first rejection L, re-reads row L into per-unit sums of w = max(0, p - q)
+//              (or p for the bonus draw), locates the unit holding t = u_K * W and emits the
+//              first id whose prefix weight exceeds t.
+// With early exit the statistics of the first positions come first (k_stats_prefix or
+// k_pairs_prefix), k_alive lists the sequences not yet rejected there, k_stats_rest /
+// k_pairs_rest read only their remaining rows, and k_tail finishes as above.
+// A greedy blockwise call is k_argmax (chunk (max, first id)) and k_greedy_final, or
+// k_greedy_heads when the same pass also carries the next block's proposal heads.
+// The draft-token sampler runs k_stats_sampling and k_tail with no draft (K = 0, each row
+// its own sequence), and k_quantile_cut is a per-row radix select for an alpha-quantile of
+// reward scores.
 //
 // The operations follow the speculative rejection sampling page (steps 2-4, and the
 // "key guarantee" that fixes the residual law), the blockwise parallel decoding page
-// (section 3.5, Verify/Accept) and the speculative contrastive decoding review (SCD).
+// (section 3.5, Verify/Accept, and the merged predict-verify step), the speculative
+// contrastive decoding review (SCD) and the Speculative Rejection page (the quantile cut).
 #include <float.h>
 #include <math.h>
 
