@@ -217,17 +217,21 @@ const char *specverify_strerror(int status);
  *   contrastive, sampler), 2 row argmax (greedy), 3 proposal compare and emit (greedy, with
  *   the next proposals for the heads variant), 4 quantile cut, 5 early-exit accept tests on
  *   the first positions, 6 early-exit statistics of the remaining rows.
- * specverify_profile_begin(ctx, max_calls, kinds) creates hipEvent pairs for up to
- * max_calls subsequent run_* calls and records one pair around every kernel they launch
- * whose kind k has bit (1 << k) set in `kinds` (0 = every kind), on the call's stream.
+ * specverify_profile_begin(ctx, max_calls, kinds, stride) creates hipEvent pairs for up to
+ * max_calls timed calls: of the calls that follow, the 1st, (stride+1)-th, (2*stride+1)-th,
+ * ... are timed (stride 1 = every call).  In a timed call every kernel whose kind k has bit
+ * (1 << k) set in `kinds` (0 = every kind) is launched with its start and stop events
+ * attached to the dispatch (hipExtLaunchKernel), on the call's stream; its duration is the
+ * kernel's own execution.  A timed dispatch costs a few microseconds more than an untimed
+ * one, so a stride above 1 keeps the timing out of the rate of a long run of calls.
  * specverify_profile_end(ctx, ms, launches) synchronises on the recorded events, writes the
  * summed milliseconds and launch counts per kind into the two SPECVERIFY_NUM_KERNELS-long
  * arrays (either may be NULL), and releases the events.
- * Errors: EINVAL (NULL ctx, max_calls < 1, unknown kind bits, begin twice, end without
- * begin), EHIP.
+ * Errors: EINVAL (NULL ctx, max_calls < 1, stride < 1, unknown kind bits, begin twice, end
+ * without begin), EHIP.
  */
 #define SPECVERIFY_NUM_KERNELS 7
-int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds);
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds, int stride);
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
 
 #ifdef __cplusplus

@@ -80,7 +80,7 @@ def load():
         lib.specverify_destroy.restype = i
         lib.specverify_strerror.argtypes = [i]
         lib.specverify_strerror.restype = ctypes.c_char_p
-        lib.specverify_profile_begin.argtypes = [vp, i, ctypes.c_uint]
+        lib.specverify_profile_begin.argtypes = [vp, i, ctypes.c_uint, i]
         lib.specverify_profile_begin.restype = i
         lib.specverify_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                                ctypes.POINTER(ctypes.c_int)]
@@ -201,12 +201,14 @@ def specverify_destroy(ctx) -> None:
     _check(load().specverify_destroy(ctx), "specverify_destroy")
 
 
-def specverify_profile_begin(ctx, max_calls: int, kinds=None) -> None:
-    """kinds: kernel names (from KERNEL_NAMES) to time, or None for all of them."""
+def specverify_profile_begin(ctx, max_calls: int, kinds=None, stride: int = 1) -> None:
+    """kinds: kernel names (from KERNEL_NAMES) to time, or None for all of them; stride: time
+    every stride-th call (the first, then every stride-th after it)."""
     mask = 0
     for k in kinds or ():
         mask |= 1 << KERNEL_NAMES.index(k)
-    _check(load().specverify_profile_begin(ctx, max_calls, mask), "specverify_profile_begin")
+    _check(load().specverify_profile_begin(ctx, max_calls, mask, stride),
+           "specverify_profile_begin")
 
 
 def specverify_profile_end(ctx):

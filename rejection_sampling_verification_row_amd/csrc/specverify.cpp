@@ -22,6 +22,8 @@ struct specverify_ctx {
     // timing
     bool prof;
     int prof_cap, prof_calls;
+    long long prof_seen;                  // calls since profile_begin
+    int prof_stride;                      // time every prof_stride-th of them
     unsigned prof_mask;                   // kernel kinds to time
     std::vector<hipEvent_t> events;       // prof_cap * 2 * SPECVERIFY_NUM_KERNELS
     std::vector<unsigned> launched;       // per recorded call: bit k = kernel kind k ran
@@ -75,7 +77,10 @@ bool bad_temperature(float t) { return !(t > 0.0f) || !isfinite(t); }
 // event pair array for the next call when timing is on, NULL otherwise
 hipEvent_t *next_events(specverify_ctx *ctx)
 {
-    if (!ctx->prof || ctx->prof_calls >= ctx->prof_cap)
+    if (!ctx->prof)
+        return nullptr;
+    const bool timed = (ctx->prof_seen++ % ctx->prof_stride) == 0;
+    if (!timed || ctx->prof_calls >= ctx->prof_cap)
         return nullptr;
     return ctx->events.data() + (size_t)ctx->prof_calls * 2 * NK;
 }
@@ -200,6 +205,8 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     ctx->bytes = total;
     ctx->prof = false;
     ctx->prof_cap = ctx->prof_calls = 0;
+    ctx->prof_seen = 0;
+    ctx->prof_stride = 1;
     ctx->prof_mask = 0;
     *out = ctx;
     return SPECVERIFY_OK;
@@ -395,9 +402,9 @@ const char *specverify_strerror(int status)
     }
 }
 
-int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds)
+int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds, int stride)
 {
-    if (!ctx || max_calls < 1 || ctx->prof || (kinds >> NK) != 0)
+    if (!ctx || max_calls < 1 || stride < 1 || ctx->prof || (kinds >> NK) != 0)
         return SPECVERIFY_EINVAL;
     DeviceGuard g(ctx->device);
     if (g.err != hipSuccess)
@@ -416,6 +423,8 @@ int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds)
     ctx->prof = true;
     ctx->prof_cap = max_calls;
     ctx->prof_calls = 0;
+    ctx->prof_seen = 0;
+    ctx->prof_stride = stride;
     ctx->prof_mask = kinds ? kinds : (1u << NK) - 1;
     return SPECVERIFY_OK;
 }
@@ -449,6 +458,8 @@ int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches)
     ctx->launched.clear();
     ctx->prof = false;
     ctx->prof_cap = ctx->prof_calls = 0;
+    ctx->prof_seen = 0;
+    ctx->prof_stride = 1;
     if (ms)
         for (int k = 0; k < NK; ++k)
             ms[k] = tot[k];

@@ -25,6 +25,7 @@
 // contrastive decoding review (SCD) and the Speculative Rejection page (the quantile cut).
 #include <float.h>
 #include <math.h>
+#include <hip/hip_ext.h>
 
 #include "sv_internal.h"
 
@@ -1490,32 +1491,31 @@ TailArgs tail_args(const Workspace &ws, int dtype, int B, int K, int V, int nch,
     return a;
 }
 
+// Launches one kernel on the call's stream.  When its kind is being timed, the kind's start
+// and stop events are handed to the dispatch itself (hipExtLaunchKernel stamps them with the
+// kernel's own begin and end), so timing puts no marker packets, and no extra gaps, between
+// dependent kernels.  Untimed launches are ordinary launches (capturable in a HIP graph).
+inline bool timed(const Launch &ln, int kind) { return ln.ev && ((ln.mask >> kind) & 1u); }
+
+#define SV_LAUNCH(ln, kind, kernel, grid, block, lds, ...)                                        \
+    do {                                                                                          \
+        if (timed((ln), (kind)))                                                                  \
+            hipExtLaunchKernelGGL(kernel, (grid), (block), (std::uint32_t)(lds), (ln).stream,     \
+                                  (ln).ev[2 * (kind)], (ln).ev[2 * (kind) + 1], 0u, __VA_ARGS__); \
+        else                                                                                      \
+            hipLaunchKernelGGL(kernel, (grid), (block), (lds), (ln).stream, __VA_ARGS__);         \
+    } while (0)
+
 template <int DT, int MODE>
-void launch_tail(const TailArgs &a, int B, size_t lds, hipStream_t stream)
+void launch_tail(const Launch &ln, const TailArgs &a, int B, size_t lds)
 {
     if (a.split > 1)
-        hipLaunchKernelGGL((k_tail<DT, MODE, true>), dim3((unsigned)(B * a.split)),
-                           dim3(TAIL_WG), lds, stream, a);
+        SV_LAUNCH(ln, KIND_TAIL, (k_tail<DT, MODE, true>), dim3((unsigned)(B * a.split)),
+                  dim3(TAIL_WG), lds, a);
     else
-        hipLaunchKernelGGL((k_tail<DT, MODE, false>), dim3((unsigned)B), dim3(TAIL_WG), lds,
-                           stream, a);
+        SV_LAUNCH(ln, KIND_TAIL, (k_tail<DT, MODE, false>), dim3((unsigned)B), dim3(TAIL_WG), lds,
+                  a);
 }
-
-struct Timer {
-    const Launch &ln;
-    int kind;
-    Timer(const Launch &l, int k) : ln(l), kind(k)
-    {
-        if (on())
-            (void)hipEventRecord(ln.ev[2 * kind], ln.stream);
-    }
-    ~Timer()
-    {
-        if (on())
-            (void)hipEventRecord(ln.ev[2 * kind + 1], ln.stream);
-    }
-    bool on() const { return ln.ev && ((ln.mask >> kind) & 1u); }
-};
 
 template <int DT, int MODE>
 hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, int V,
@@ -1526,24 +1526,18 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
     const char *t = static_cast<const char *>(tgt);
     const char *d = static_cast<const char *>(drf);
     const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
-    {
-        Timer tm(ln, KIND_STATS);
-        if (MODE == SAMPLING) {
-            const unsigned grid = (unsigned)((size_t)B * (2 * K + 1) * nch);
-            hipLaunchKernelGGL(k_stats_sampling<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
-                               V, nch, sp, ws.part);
-        } else {
-            const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
-            hipLaunchKernelGGL(k_stats_contrastive<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d,
-                               K, V, nch, sp, sq, ws.part);
-        }
+    if (MODE == SAMPLING) {
+        const unsigned grid = (unsigned)((size_t)B * (2 * K + 1) * nch);
+        SV_LAUNCH(ln, KIND_STATS, k_stats_sampling<DT>, dim3(grid), dim3(WG), 0, t, d, K, V, nch,
+                  sp, ws.part);
+    } else {
+        const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
+        SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>, dim3(grid), dim3(WG), 0, t, d, K, V,
+                  nch, sp, sq, ws.part);
     }
-    {
-        Timer tm(ln, KIND_TAIL);
-        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
-                                     out_tokens, out_probs, draw_probs, nullptr, K + 1, 0);
-        launch_tail<DT, MODE>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
-    }
+    const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
+                                 out_tokens, out_probs, draw_probs, nullptr, K + 1, 0);
+    launch_tail<DT, MODE>(ln, a, B, tail_lds_bytes(DT, K, V, nch));
     return hipGetLastError();
 }
 
@@ -1552,17 +1546,11 @@ hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int 
                        const int32_t *props, int32_t *acc_len, int32_t *out_tokens)
 {
     const int nch = num_chunks(NV_ARGMAX, DT, V);
-    {
-        Timer tm(ln, KIND_ARGMAX);
-        const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
-        hipLaunchKernelGGL(k_argmax<DT>, dim3(grid), dim3(WG), 0, ln.stream,
-                           static_cast<const char *>(tgt), V, nch, 1, ws.part);
-    }
-    {
-        Timer tm(ln, KIND_GREEDY_EMIT);
-        hipLaunchKernelGGL(k_greedy_final, dim3(B), dim3(WG), 0, ln.stream, props, K, V, nch,
-                           ws.part, acc_len, out_tokens);
-    }
+    const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
+    SV_LAUNCH(ln, KIND_ARGMAX, k_argmax<DT>, dim3(grid), dim3(WG), 0,
+              static_cast<const char *>(tgt), V, nch, 1, ws.part);
+    SV_LAUNCH(ln, KIND_GREEDY_EMIT, k_greedy_final, dim3(B), dim3(WG), 0, props, K, V, nch, ws.part,
+              acc_len, out_tokens);
     return hipGetLastError();
 }
 
@@ -1578,53 +1566,40 @@ hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, 
     const int prefix = EARLY_PREFIX < K + 1 ? EARLY_PREFIX : K + 1;
     const int *alive = nullptr;
     if (prefix == K + 1) {  // every position is in the prefix: one full pass
-        Timer tm(ln, KIND_STATS);
         if (MODE == SAMPLING)
-            hipLaunchKernelGGL(k_stats_sampling<DT>,
-                               dim3((unsigned)((size_t)B * (2 * K + 1) * nch)), dim3(WG), 0,
-                               ln.stream, t, d, K, V, nch, sp, ws.part);
+            SV_LAUNCH(ln, KIND_STATS, k_stats_sampling<DT>,
+                      dim3((unsigned)((size_t)B * (2 * K + 1) * nch)), dim3(WG), 0, t, d, K, V,
+                      nch, sp, ws.part);
         else
-            hipLaunchKernelGGL(k_stats_contrastive<DT>, dim3((unsigned)((size_t)B * (K + 1) * nch)),
-                               dim3(WG), 0, ln.stream, t, d, K, V, nch, sp, sq, ws.part);
+            SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>,
+                      dim3((unsigned)((size_t)B * (K + 1) * nch)), dim3(WG), 0, t, d, K, V, nch,
+                      sp, sq, ws.part);
     } else {
-        {
-            Timer tm(ln, KIND_STATS);
-            if (MODE == SAMPLING)
-                hipLaunchKernelGGL(k_stats_prefix<DT>,
-                                   dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0,
-                                   ln.stream, t, d, K, V, nch, prefix, sp, ws.part, ws.count);
-            else
-                hipLaunchKernelGGL(k_pairs_prefix<DT>, dim3((unsigned)((size_t)B * prefix * nch)),
-                                   dim3(WG), 0, ln.stream, t, d, K, V, nch, prefix, sp, sq,
-                                   ws.part, ws.count);
-        }
-        {
-            Timer tm(ln, KIND_EARLY_ACCEPT);
-            hipLaunchKernelGGL((k_alive<DT, MODE>), dim3(B), dim3(WG), 0, ln.stream, t, d, tokens,
-                               unif, K, V, nch, prefix, sp, sq, ws.part, ws.alive, ws.list,
-                               ws.count);
-        }
-        {
-            Timer tm(ln, KIND_EARLY_REST);
-            const size_t rows = (MODE == SAMPLING) ? (size_t)(2 * K + 1 - 2 * prefix)
-                                                   : (size_t)(K + 1 - prefix);
-            const size_t items = (size_t)B * rows * nch;
-            const unsigned grid = (unsigned)(items < (size_t)rest_grid ? items : rest_grid);
-            if (MODE == SAMPLING)
-                hipLaunchKernelGGL(k_stats_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
-                                   V, nch, prefix, sp, ws.part, ws.list, ws.count);
-            else
-                hipLaunchKernelGGL(k_pairs_rest<DT>, dim3(grid), dim3(WG), 0, ln.stream, t, d, K,
-                                   V, nch, prefix, sp, sq, ws.part, ws.list, ws.count);
-        }
+        if (MODE == SAMPLING)
+            SV_LAUNCH(ln, KIND_STATS, k_stats_prefix<DT>,
+                      dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0, t, d, K, V, nch,
+                      prefix, sp, ws.part, ws.count);
+        else
+            SV_LAUNCH(ln, KIND_STATS, k_pairs_prefix<DT>,
+                      dim3((unsigned)((size_t)B * prefix * nch)), dim3(WG), 0, t, d, K, V, nch,
+                      prefix, sp, sq, ws.part, ws.count);
+        SV_LAUNCH(ln, KIND_EARLY_ACCEPT, (k_alive<DT, MODE>), dim3(B), dim3(WG), 0, t, d, tokens,
+                  unif, K, V, nch, prefix, sp, sq, ws.part, ws.alive, ws.list, ws.count);
+        const size_t rows = (MODE == SAMPLING) ? (size_t)(2 * K + 1 - 2 * prefix)
+                                               : (size_t)(K + 1 - prefix);
+        const size_t items = (size_t)B * rows * nch;
+        const unsigned grid = (unsigned)(items < (size_t)rest_grid ? items : rest_grid);
+        if (MODE == SAMPLING)
+            SV_LAUNCH(ln, KIND_EARLY_REST, k_stats_rest<DT>, dim3(grid), dim3(WG), 0, t, d, K, V,
+                      nch, prefix, sp, ws.part, ws.list, ws.count);
+        else
+            SV_LAUNCH(ln, KIND_EARLY_REST, k_pairs_rest<DT>, dim3(grid), dim3(WG), 0, t, d, K, V,
+                      nch, prefix, sp, sq, ws.part, ws.list, ws.count);
         alive = ws.alive;
     }
-    {
-        Timer tm(ln, KIND_TAIL);
-        const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
-                                     out_tokens, out_probs, nullptr, alive, prefix, 1);
-        launch_tail<DT, MODE>(a, B, tail_lds_bytes(DT, K, V, nch), ln.stream);
-    }
+    const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
+                                 out_tokens, out_probs, nullptr, alive, prefix, 1);
+    launch_tail<DT, MODE>(ln, a, B, tail_lds_bytes(DT, K, V, nch));
     return hipGetLastError();
 }
 
@@ -1635,17 +1610,10 @@ hipError_t greedy_heads_impl(const Launch &ln, const Workspace &ws, int B, int K
 {
     const int nch = num_chunks(NV_ARGMAX, DT, V);
     const char *lg = static_cast<const char *>(logits);
-    {
-        Timer tm(ln, KIND_ARGMAX);
-        const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
-        hipLaunchKernelGGL(k_argmax<DT>, dim3(grid), dim3(WG), 0, ln.stream, lg, V, nch, H,
-                           ws.part);
-    }
-    {
-        Timer tm(ln, KIND_GREEDY_EMIT);
-        hipLaunchKernelGGL(k_greedy_heads<DT>, dim3(B), dim3(HEADS_WG), 0, ln.stream, lg, props, K,
-                           H, V, nch, ws.part, acc_len, out_tokens, next_props);
-    }
+    const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
+    SV_LAUNCH(ln, KIND_ARGMAX, k_argmax<DT>, dim3(grid), dim3(WG), 0, lg, V, nch, H, ws.part);
+    SV_LAUNCH(ln, KIND_GREEDY_EMIT, k_greedy_heads<DT>, dim3(B), dim3(HEADS_WG), 0, lg, props, K,
+              H, V, nch, ws.part, acc_len, out_tokens, next_props);
     return hipGetLastError();
 }
 
@@ -1675,9 +1643,8 @@ hipError_t launch_greedy_heads(const Launch &ln, const Workspace &ws, int dtype,
 hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const float *scores,
                                float *r_cut, uint8_t *keep, int32_t *n_keep)
 {
-    Timer tm(ln, KIND_CUT);
-    hipLaunchKernelGGL(k_quantile_cut, dim3(P), dim3(TAIL_WG), (size_t)N * sizeof(uint32_t),
-                       ln.stream, scores, N, k, r_cut, keep, n_keep);
+    SV_LAUNCH(ln, KIND_CUT, k_quantile_cut, dim3(P), dim3(TAIL_WG), (size_t)N * sizeof(uint32_t),
+              scores, N, k, r_cut, keep, n_keep);
     return hipGetLastError();
 }
 

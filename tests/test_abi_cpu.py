@@ -60,7 +60,7 @@ def test_null_context_is_rejected_on_the_host():
     assert lib.specverify_run_contrastive(None, None, 1, 1, 1, 8, 1.0, *([None] * 7)) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_run_greedy(None, None, 1, 1, 1, 8, None, None, None, None) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_destroy(None) == sv.SPECVERIFY_OK
-    assert lib.specverify_profile_begin(None, 4, 0) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_begin(None, 4, 0, 1) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_profile_end(None, None, None) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_workspace_bytes(None) == 0
     h = ctypes.c_void_p()

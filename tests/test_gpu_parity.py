@@ -270,7 +270,14 @@ def test_profile_api(ctx):
     ms, n = sv.specverify_profile_end(ctx)
     assert n["row_stats"] == 2 and n["accept_draw"] == 0 and ms["accept_draw"] == 0.0
     lib = sv.load()
-    assert lib.specverify_profile_begin(ctx, 2, 1 << sv.SPECVERIFY_NUM_KERNELS) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_begin(ctx, 2, 1 << sv.SPECVERIFY_NUM_KERNELS, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_begin(ctx, 2, 0, 0) == sv.SPECVERIFY_EINVAL
+    # a stride times the first call and every stride-th after it
+    sv.specverify_profile_begin(ctx, 8, ["row_stats", "accept_draw"], stride=3)
+    for _ in range(7):
+        run(ctx, w)
+    ms, n = sv.specverify_profile_end(ctx)
+    assert n["row_stats"] == 3 and n["accept_draw"] == 3   # calls 0, 3 and 6
 
 
 # ----------------------------------------------------------------- capacity limits
