@@ -133,10 +133,76 @@ template <> __device__ inline float tree_sum<8>(const float (&t)[8])
 }
 
 // ------------------------------------------------------------------ wave64 / block reductions
-// Butterfly reductions: every lane ends with the same bits (each step adds the same two
-// operands in both lanes), so the results are deterministic.
+// Butterfly reductions whose lane exchanges run on the VALU, with no LDS round trip: steps 0
+// and 1 are the DPP quad permutations lane^1 and lane^2; steps 2 and 3 mirror lanes within 8
+// and within 16 (once the quads are reduced, the mirrored lane holds what lane^4, lane^8
+// would); step 4 swaps 16-lane rows (lane^16, v_permlane16_swap) and step 5 the wave's halves
+// (lane^32, v_permlane32_swap).  Each step combines the same two operands in both lanes of a
+// pair, so every lane ends with the same bits and the results are deterministic.  The whole
+// wave (or, for the half-wave forms, the whole 32-lane half) must be active.
 
-__device__ inline float wave_max(float v)
+template <int S>
+__device__ __forceinline__ int lane_xch(int v)
+{
+    const int lane = threadIdx.x & 63;
+    if constexpr (S == 0)
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    else if constexpr (S == 1)
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (S == 2)
+        return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    else if constexpr (S == 3)
+        return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    else if constexpr (S == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? (int)r[0] : (int)r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? (int)r[0] : (int)r[1];
+    }
+}
+
+template <int S> __device__ __forceinline__ float xch(float v)
+{
+    return __int_as_float(lane_xch<S>(__float_as_int(v)));
+}
+
+template <int S> __device__ __forceinline__ double xch(double v)
+{
+    return __hiloint2double(lane_xch<S>(__double2hiint(v)), lane_xch<S>(__double2loint(v)));
+}
+
+template <int NS, typename T> __device__ __forceinline__ T xmax(T v)
+{
+    v = fmaxf(v, xch<0>(v));
+    v = fmaxf(v, xch<1>(v));
+    v = fmaxf(v, xch<2>(v));
+    v = fmaxf(v, xch<3>(v));
+    v = fmaxf(v, xch<4>(v));
+    if constexpr (NS == 6)
+        v = fmaxf(v, xch<5>(v));
+    return v;
+}
+
+template <int NS, typename T> __device__ __forceinline__ T xsum(T v)
+{
+    v += xch<0>(v);
+    v += xch<1>(v);
+    v += xch<2>(v);
+    v += xch<3>(v);
+    v += xch<4>(v);
+    if constexpr (NS == 6)
+        v += xch<5>(v);
+    return v;
+}
+
+__device__ inline float wave_max(float v) { return xmax<6>(v); }
+__device__ inline double wave_sum(double v) { return xsum<6>(v); }
+
+// The same reductions with the exchanges through the LDS crossbar (ds_bpermute): a longer
+// latency per call, but they leave the VALU alone, which matters where the VALU is as busy
+// as the memory pipe: the row statistics kernels and the draw's row pass.
+template <typename T> __device__ inline T wave_max_lds(T v)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
@@ -144,7 +210,7 @@ __device__ inline float wave_max(float v)
     return v;
 }
 
-__device__ inline float wave_sum_f(float v)
+template <typename T> __device__ inline T wave_sum_lds(T v)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
@@ -152,13 +218,9 @@ __device__ inline float wave_sum_f(float v)
     return v;
 }
 
-__device__ inline double wave_sum(double v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
-}
+// max and sum over each 32-lane half of the wave (the halves reduce independently)
+__device__ inline float half_max(float v) { return xmax<5>(v); }
+__device__ inline double half_sum(double v) { return xsum<5>(v); }
 
 // inclusive prefix sum over the wave's lanes (fixed order)
 __device__ inline double wave_incl_scan(double v, int lane)
@@ -181,14 +243,21 @@ __device__ inline void take_better(float &v, int &i, float v2, int i2)
     }
 }
 
+template <int S> __device__ __forceinline__ void argmax_step(float &v, int &i)
+{
+    const float v2 = xch<S>(v);
+    const int i2 = lane_xch<S>(i);
+    take_better(v, i, v2, i2);
+}
+
 __device__ inline void wave_argmax(float &v, int &i)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(v, o);
-        const int i2 = __shfl_xor(i, o);
-        take_better(v, i, v2, i2);
-    }
+    argmax_step<0>(v, i);
+    argmax_step<1>(v, i);
+    argmax_step<2>(v, i);
+    argmax_step<3>(v, i);
+    argmax_step<4>(v, i);
+    argmax_step<5>(v, i);
 }
 
 // ------------------------------------------------------------------ row statistics
@@ -227,9 +296,9 @@ __device__ inline void thread_stats(float (&x)[NV][E], const Scale &sc, float &m
 // per-wave (M, S): S = sum over lanes of s * exp2((m - M) * log2(e)/T)
 __device__ inline float2 wave_stats(float m, float s, const Scale &sc)
 {
-    const float M = wave_max(m);
+    const float M = wave_max_lds(m);
     const float e = (s > 0.0f) ? s * exp2s(m - M, sc.hi, sc.lo) : 0.0f;
-    return make_float2(M, wave_sum_f(e));
+    return make_float2(M, wave_sum_lds(e));
 }
 
 // Store the workgroup's four per-wave partials from one thread after a barrier: a single
@@ -364,24 +433,30 @@ __device__ __forceinline__ void merge_rows(const float2 *part, int b, int K, int
         }
         __syncthreads();
     }
-    for (int r = w; r < R; r += NW) {
+    // A row with at most 32 partials is merged by half a wave, so that each wave takes two
+    // rows at a time; the reductions then run over the half's 32 lanes, which gives the
+    // same values as the 64-lane ones (there the other half only adds zeros and -inf).
+    const bool half = np <= 32;
+    const int ll = half ? (lane & 31) : lane, width = half ? 32 : 64;
+    const int rstep = half ? 2 * NW : NW;
+    for (int r = half ? 2 * w + (lane >> 5) : w; r < R; r += rstep) {
         const int pos = (r <= K) ? r : r - K - 1;
         if (pos >= npos)
             continue;  // not read by this call
         const int r0 = r * np;
         const double cc = (r <= K) ? sp.c : sq.c;
         float ml = -INFINITY;
-        for (int i = lane; i < np; i += 64)
+        for (int i = ll; i < np; i += width)
             ml = fmaxf(ml, (staged ? stage[r0 + i] : pb[r0 + i]).x);
-        const float M = wave_max(ml);
+        const float M = half ? half_max(ml) : wave_max(ml);
         double sl = 0.0;
-        for (int i = lane; i < np; i += 64) {
+        for (int i = ll; i < np; i += width) {
             const float2 v = staged ? stage[r0 + i] : pb[r0 + i];
             if (v.y > 0.0f)
                 sl += (double)v.y * exp2(((double)v.x - (double)M) * cc);
         }
-        const double S = wave_sum(sl);
-        if (lane == 0) {
+        const double S = half ? half_sum(sl) : wave_sum(sl);
+        if (ll == 0) {
             sM[r] = M;
             sS[r] = S;
         }
@@ -401,7 +476,7 @@ __device__ __forceinline__ bool accept_test(const Draft &d, int j, int K, const 
 }
 
 // Sequence b after its rows' statistics (the first phase of k_tail): merge the rows of the
-// positions below npos (K+1: all of them), then wave 0 runs the accept tests, one lane per
+// positions below npos (K+1: all of them), then the last wave runs the accept tests, one lane per
 // draft position, finds the first rejection L, writes accepted_len, the kept tokens, -1
 // padding and out_probs, and leaves in *info what the draw needs (L = -1 for bad ids).
 // Positions at or past npos are only reached by a sequence that rejects before them.
@@ -419,11 +494,16 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
     __shared__ float sM[MAX_ROWS];
     __shared__ double sS[MAX_ROWS];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // The last wave gathers the draft's tokens and logits (a token load, then the logit loads
+    // that depend on it) and runs the accept tests.  The partials are staged by the first
+    // threads, so with a few hundred partials the last wave issues no staging load that would
+    // wait behind its gather: the two round trips overlap the staging instead of delaying it.
+    constexpr int GW = TAIL_WAVES - 1;
     Draft d = {0, 0.0f, 0.0f, 0.0f, false};
-    if (w == 0)  // the token and logit loads go out before the merge waits on memory
+    if (w == GW)
         d = gather_draft<DT, MODE>(tgt, drf, tokens, unif, b, K, V, lane);
     merge_rows<TAIL_WG>(part, b, K, nch, npos, sp, sq, stage, sM, sS);
-    if (w != 0)
+    if (w != GW)
         return;
 
     int32_t *ot = out_tokens + (size_t)b * (K + 1);
@@ -714,7 +794,7 @@ __device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV], 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const double s = wave_sum((double)vs[i]);
+        const double s = wave_sum_lds((double)vs[i]);
         if (lane == 0)
             units[(it * NV + i) * TAIL_WAVES + w] = s;
     }
@@ -753,42 +833,85 @@ __device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit
     }
 }
 
-// Among `nu` units with totals unit(u) (ascending ids), one wave finds the first unit whose
-// running total exceeds tt = u01 * W (W = the sum of all units, fixed order), or if rounding
-// leaves t at or past the last one, the last unit of positive weight (*fb = 1).  Returns the
-// unit (or -1 when every unit weighs 0) and writes its starting weight *base and tt.
-template <typename F>
-__device__ inline int find_unit(F unit, int nu, float u01, double *base, double *tt, int *fb)
+// Among the `nu` unit totals in LDS (ascending ids) the whole workgroup finds the first unit
+// whose running total exceeds tt = u01 * W (W = the sum of all units), or, if rounding leaves
+// t at or past the last one, the last unit of positive weight (fb = 1); -1 when every unit
+// weighs 0.  Thread t owns the units [t*U, t*U + U): it sums them in order, a wave scan and a
+// scan of the 16 wave totals (the same order in every thread, so every thread holds the same
+// W) give each thread's starting total, and each thread tests its own units.  The unit, its
+// starting total, tt and fb go to LDS, readable after the next barrier.
+__device__ inline void find_unit_block(const double *units, int nu, float u01, int *s_unit,
+                                       double *s_base, double *s_t, int *s_fb)
 {
-    const int lane = threadIdx.x & 63;
-    double W = 0.0;
-    for (int s0 = 0; s0 < nu; s0 += 64)
-        W += wave_sum((s0 + lane < nu) ? unit(s0 + lane) : 0.0);
-    *tt = (double)u01 * W;
-    double run = 0.0, found_base = 0.0, last_base = 0.0;
-    int us = -1, last = -1;
-    for (int s0 = 0; s0 < nu && us < 0; s0 += 64) {
-        const double wu = (s0 + lane < nu) ? unit(s0 + lane) : 0.0;
-        const double inc = wave_incl_scan(wu, lane);
-        double exc = __shfl_up(inc, 1);
-        if (lane == 0)
-            exc = 0.0;
-        const unsigned long long hit = __ballot(W > 0.0 && wu > 0.0 && run + inc > *tt);
-        const unsigned long long pos = __ballot(wu > 0.0);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            us = s0 + l;
-            found_base = run + __shfl(exc, l);
-        } else if (pos) {
-            const int l = 63 - __builtin_clzll(pos);
-            last = s0 + l;
-            last_base = run + __shfl(exc, l);
-        }
-        run += __shfl(inc, 63);
+    __shared__ double sw[TAIL_WAVES], shb[TAIL_WAVES], slb[TAIL_WAVES];
+    __shared__ int sh[TAIL_WAVES], sl[TAIL_WAVES];
+    // the thread index passes through an empty asm so that nothing derived from it is
+    // hoisted out of the caller's loop and kept live across the row pass before it
+    int t;
+    asm volatile("" : "=v"(t) : "0"((int)threadIdx.x));
+    const int lane = t & 63, w = t >> 6;
+    const int U = (nu + TAIL_WG - 1) / TAIL_WG;
+    const int k0 = t * U, k1 = (k0 + U < nu) ? k0 + U : nu;
+    double ts = 0.0;
+    for (int k = k0; k < k1; ++k)
+        ts += units[k];
+    const double inc = wave_incl_scan(ts, lane);
+    double exc = __shfl_up(inc, 1);
+    if (lane == 0)
+        exc = 0.0;
+    if (lane == 63)
+        sw[w] = inc;
+    __syncthreads();
+    double W = 0.0, wb = 0.0;
+#pragma unroll
+    for (int v = 0; v < TAIL_WAVES; ++v) {
+        if (v == w)
+            wb = W;
+        W += sw[v];
     }
-    *fb = (us < 0);
-    *base = (us >= 0) ? found_base : last_base;
-    return (us >= 0) ? us : last;
+    const double tt = (double)u01 * W;
+    double run = wb + exc, hb = 0.0, lb = 0.0;
+    int hit = -1, last = -1;
+    for (int k = k0; k < k1; ++k) {
+        const double wu = units[k];
+        if (hit < 0 && W > 0.0 && wu > 0.0 && run + wu > tt) {
+            hit = k;
+            hb = run;
+        }
+        if (wu > 0.0) {
+            last = k;
+            lb = run;
+        }
+        run += wu;
+    }
+    // the wave's first hit is in its lowest hitting lane, its last positive unit in the
+    // highest lane that has one
+    const unsigned long long hm = __ballot(hit >= 0), pm = __ballot(last >= 0);
+    const int lh = hm ? __builtin_ctzll(hm) : 0, lp = pm ? 63 - __builtin_clzll(pm) : 0;
+    const int wh = __shfl(hit, lh), wl = __shfl(last, lp);
+    const double whb = __shfl(hb, lh), wlb = __shfl(lb, lp);
+    if (lane == 0) {
+        sh[w] = hm ? wh : -1;
+        shb[w] = whb;
+        sl[w] = pm ? wl : -1;
+        slb[w] = wlb;
+    }
+    __syncthreads();
+    if (w == 0) {  // lane v < 16 holds wave v's candidates: the first hit, else the last positive
+        const bool in = lane < TAIL_WAVES;
+        const int hv = in ? sh[lane] : -1, lv = in ? sl[lane] : -1;
+        const double hbv = in ? shb[lane] : 0.0, lbv = in ? slb[lane] : 0.0;
+        const unsigned long long hmk = __ballot(hv >= 0), lmk = __ballot(lv >= 0);
+        const int fh = hmk ? __builtin_ctzll(hmk) : 0, fl = lmk ? 63 - __builtin_clzll(lmk) : 0;
+        const int uh = __shfl(hv, fh), ul = __shfl(lv, fl);
+        const double bh = __shfl(hbv, fh), bl = __shfl(lbv, fl);
+        if (lane == 0) {
+            *s_unit = hmk ? uh : (lmk ? ul : -1);
+            *s_base = hmk ? bh : (lmk ? bl : 0.0);
+            *s_t = tt;
+            *s_fb = hmk ? 0 : 1;
+        }
+    }
 }
 
 // Inside unit `unit` (one wave): lane l weighs the unit's vector l with the instructions of
@@ -952,17 +1075,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
                     units[k] = __hip_atomic_load(gu + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
         }
-        if (w == 0) {
-            double base, tt;
-            int fb;
-            const int us = find_unit([&](int k) { return units[k]; }, nu, u01, &base, &tt, &fb);
-            if (lane == 0) {
-                s_unit = us;
-                s_base = base;
-                s_t = tt;
-                s_fb = fb;
-            }
-        }
+        find_unit_block(units, nu, u01, &s_unit, &s_base, &s_t, &s_fb);
         __syncthreads();
         const int us = s_unit;
         if (us >= 0) {
@@ -972,7 +1085,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
             return;
         }
         // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
-        __syncthreads();  // find_unit has read the units the repeat overwrites
+        __syncthreads();  // find_unit_block has read the units the repeat overwrites
     }
     if (t == 0) {  // a row without finite logits: outside the contract
         *out = -1;
