@@ -650,10 +650,20 @@ __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict
 struct DrawRows {
     const char *p0;   // target row L (sampling) or expert row L (contrastive)
     const char *p1;   // draft row L (sampling, L < K only) or amateur row L (contrastive)
+    // the same rows as buffer resources over their V * BYTES bytes, for the row pass: its
+    // loads then take one per-thread offset register and a per-load scalar offset instead of
+    // a 64-bit address each (reads past the end of the row return zeros)
+    __amdgpu_buffer_rsrc_t b0, b1;
     bool two;         // p1 is read
     bool resid;       // L < K: w = max(0, p - q); else w = p
     bool al;          // every row read is 16-byte aligned
 };
+
+// Raw buffer resource for `bytes` bytes from p (gfx9 descriptor word 3: 32-bit data format).
+__device__ inline __amdgpu_buffer_rsrc_t row_resource(const char *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, bytes, 0x00020000);
+}
 
 template <int DT, int MODE>
 __device__ inline DrawRows draw_rows(const char *tgt, const char *drf, int b, int K, int V, int L)
@@ -670,6 +680,8 @@ __device__ inline DrawRows draw_rows(const char *tgt, const char *drf, int b, in
         r.p1 = drf + ((size_t)b * (K + 1) + L) * (size_t)V * BY;
     }
     r.al = aligned16(r.p0) && (!r.two || aligned16(r.p1));
+    r.b0 = row_resource(r.p0, V * BY);
+    r.b1 = row_resource(r.two ? r.p1 : r.p0, V * BY);
     return r;
 }
 
@@ -741,27 +753,27 @@ __device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint
 // thread t holds the NV vectors base + i*TAIL_WG*E + [0, E), base = the iteration's first id
 // + t*E, so a wave's loads are 1 KiB contiguous.  NV = NV_TAIL when a draft-side row is read
 // as well (TWO), 2 * NV_TAIL when only the target row is: the same bytes in flight either
-// way.  In an aligned row every vector wholly below V is one streamed 16-byte load per row
-// read (vectors at or past V load nothing).
+// way.  In an aligned row every vector is one streamed 16-byte buffer load per row read;
+// the ones at or past V read zeros and are not used (tail_weigh weighs the vector that
+// straddles V element by element and gives the ones past it weight 0).
 template <int DT, int NV, bool TWO>
-__device__ inline void tail_load(const DrawRows &r, int base, int V, uint4 (&a)[NV],
+__device__ inline void tail_load(const DrawRows &r, int it_first, int V, uint4 (&a)[NV],
                                  uint4 (&q)[NV])
 {
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = TAIL_WG * Elt<DT>::EPV;
     if (!r.al)
         return;
+    const int vo = (int)threadIdx.x * E * BY;   // this thread's byte offset in a vector slot
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e0 = base + i * STRIDE;
-        if (e0 + E <= V)
-            a[i] = load_stream(r.p0 + (size_t)e0 * BY);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.b0, vo, (it_first + i * STRIDE) * BY, 2);
+        a[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
     if constexpr (TWO) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int e0 = base + i * STRIDE;
-            if (e0 + E <= V)
-                q[i] = load_stream(r.p1 + (size_t)e0 * BY);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.b1, vo, (it_first + i * STRIDE) * BY, 2);
+            q[i] = make_uint4(v.x, v.y, v.z, v.w);
         }
     }
 }
@@ -808,8 +820,10 @@ __device__ __forceinline__ void tail_store_units(int it, const float (&vs)[NV], 
 // A pass over row L (and the draft row L when TWO) for the iterations first, first + step, ...
 // below nit: unit u = (it*NV + i)*TAIL_WAVES + w holds the fp64 sum of wave w's draw weights
 // at vector slot i of iteration it, i.e. the 64*E contiguous ids it*CE + i*TAIL_WG*E + w*64*E
-// + [0, 64*E); unit order is id order.  Two register buffers alternate so that the next
-// iteration's loads are in flight while the current one is weighed.
+// + [0, 64*E); unit order is id order.  Two register buffers alternate; each is reloaded
+// with the iteration after next as soon as it has been weighed, before the unit sums (a
+// chain of lane exchanges) are formed, so that two iterations' loads are in flight while
+// one is weighed and summed.
 template <int DT, int MODE, int NV, bool TWO>
 __device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit, int first,
                                                int step, bool target_law, const SeqInfo &si,
@@ -821,18 +835,20 @@ __device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit
     float vs[NV];
     if (first >= nit)
         return;
-    tail_load<DT, NV, TWO>(r, first * CE + t0, V, a0, q0);
+    tail_load<DT, NV, TWO>(r, first * CE, V, a0, q0);
+    if (first + step < nit)
+        tail_load<DT, NV, TWO>(r, (first + step) * CE, V, a1, q1);
     for (int it = first; it < nit; it += 2 * step) {
         const int it1 = it + step;
-        if (it1 < nit)
-            tail_load<DT, NV, TWO>(r, it1 * CE + t0, V, a1, q1);
         tail_weigh<DT, MODE, NV, TWO>(r, it * CE + t0, V, target_law, si, sp, sq, a0, q0, vs);
+        if (it + 2 * step < nit)
+            tail_load<DT, NV, TWO>(r, (it + 2 * step) * CE, V, a0, q0);
         tail_store_units<NV>(it, vs, units);
         if (it1 < nit) {
-            if (it1 + step < nit)
-                tail_load<DT, NV, TWO>(r, (it1 + step) * CE + t0, V, a0, q0);
             tail_weigh<DT, MODE, NV, TWO>(r, it1 * CE + t0, V, target_law, si, sp, sq, a1, q1,
                                           vs);
+            if (it1 + 2 * step < nit)
+                tail_load<DT, NV, TWO>(r, (it1 + 2 * step) * CE, V, a1, q1);
             tail_store_units<NV>(it1, vs, units);
         }
     }
