@@ -293,6 +293,48 @@ __device__ inline void thread_stats(float (&x)[NV][E], const Scale &sc, float &m
     s *= __builtin_amdgcn_exp2f(-shift);
 }
 
+// thread_stats over packed words, GV vectors at a time with an online merge: the running
+// (m, s) is rescaled by exp2((m - m') log2(e)/T) when a group raises the maximum to m'.  Each
+// group's exponent arguments have the fma-reference form with that group's running maximum.
+// Fewer values are live at once than in thread_stats, at the cost of two exps per group.
+template <int DT, int NV, int GV>
+__device__ inline void thread_stats_words(const uint4 (&raw)[NV], const Scale &sc, float &m,
+                                          float &s)
+{
+    constexpr int E = Elt<DT>::EPV;
+    m = -INFINITY;
+    s = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NV; g += GV) {
+        float x[GV][E];
+#pragma unroll
+        for (int i = 0; i < GV; ++i)
+            Elt<DT>::unpack(raw[g + i], x[i]);
+        float mg = m;
+#pragma unroll
+        for (int i = 0; i < GV; ++i)
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                mg = fmaxf(mg, x[i][k]);
+        const float mr = (mg == -INFINITY) ? 0.0f : mg;  // an all -inf group sums exact zeros
+        const float R = mr * sc.hi;
+        const float shift = __builtin_fmaf(mr, sc.lo, __builtin_fmaf(mr, sc.hi, -R));
+        float sg = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GV; ++i) {
+            float t[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                t[k] = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(x[i][k], sc.lo, __builtin_fmaf(x[i][k], sc.hi, -R)));
+            sg += tree_sum<E>(t);
+        }
+        sg *= __builtin_amdgcn_exp2f(-shift);
+        s = (s > 0.0f) ? s * exp2s(m - mg, sc.hi, sc.lo) + sg : sg;
+        m = mg;
+    }
+}
+
 // per-wave (M, S): S = sum over lanes of s * exp2((m - M) * log2(e)/T)
 __device__ inline float2 wave_stats(float m, float s, const Scale &sc)
 {
@@ -365,6 +407,55 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             load_elems<DT>(rp, al, cbase + (i * WG + threadIdx.x) * E, V, -INFINITY, x[i]);
+    }
+}
+
+// The same chunk as load_chunk, kept as NV raw 16-byte words per thread (ids >= V read as
+// -inf bits): vectors wholly below V in an aligned row are one streamed load each, the rest
+// are packed element by element.  Holding the packed words instead of NV*E floats keeps the
+// sampling statistics kernel at 46 VGPRs, 8 waves per SIMD.
+template <int DT>
+__device__ inline uint4 pack_elems(const char *rp, int e0, int V)
+{
+    uint32_t w[4];
+    if constexpr (Elt<DT>::EPV == 8) {  // bfloat16: element 2j in the low half of word j
+        const uint16_t *h = reinterpret_cast<const uint16_t *>(rp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = (e0 + 2 * j < V) ? (uint32_t)h[e0 + 2 * j] : 0xff80u;
+            const uint32_t hi = (e0 + 2 * j + 1 < V) ? (uint32_t)h[e0 + 2 * j + 1] : 0xff80u;
+            w[j] = lo | (hi << 16);
+        }
+    } else {
+        const uint32_t *f = reinterpret_cast<const uint32_t *>(rp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = (e0 + j < V) ? f[e0 + j] : 0xff800000u;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int DT, int NV>
+__device__ inline void load_chunk_words(const char *rp, bool al, int cbase, int V,
+                                        uint4 (&raw)[NV])
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    constexpr uint32_t NEG_INF_WORD = (BY == 2) ? 0xff80ff80u : 0xff800000u;
+    if (al && cbase + WG * NV * E <= V) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e0 = cbase + (i * WG + threadIdx.x) * E;
+            if (al && e0 + E <= V)
+                raw[i] = load_stream(rp + (size_t)e0 * BY);
+            else if (e0 >= V)
+                raw[i] = make_uint4(NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD);
+            else
+                raw[i] = pack_elems<DT>(rp, e0, V);
+        }
     }
 }
 
@@ -564,6 +655,28 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
     }
 }
 
+// Per-thread (max, sum) of one chunk of a sampling row.  bfloat16 keeps the chunk as packed
+// words and reduces it two vectors at a time (46 VGPRs, 8 waves per SIMD: 1-2 us faster per
+// launch at B=256, K=8, V=128256 than 64 unpacked floats at 79 VGPRs, 6 waves); float32 keeps
+// the unpacked values (its 32 per thread are no burden, and it ran slower as packed words).
+// The full-read and the early-exit statistics both use this, so they agree bit for bit.
+template <int DT>
+__device__ __forceinline__ void sampling_chunk_stats(const char *rp, int V, int c, const Scale &sc,
+                                                     float &m, float &s)
+{
+    constexpr int E = Elt<DT>::EPV;
+    const int cbase = c * WG * NV_STATS * E;
+    if constexpr (E == 8) {
+        uint4 raw[NV_STATS];
+        load_chunk_words<DT, NV_STATS>(rp, aligned16(rp), cbase, V, raw);
+        thread_stats_words<DT, NV_STATS, 2>(raw, sc, m, s);
+    } else {
+        float x[NV_STATS][E];
+        load_chunk<DT, NV_STATS>(rp, aligned16(rp), cbase, V, x);
+        thread_stats<E, NV_STATS>(x, sc, m, s);
+    }
+}
+
 // rows b*(2K+1)+r: r <= K target row (b, r), else draft row (b, r-K-1); each wave stores its
 // (max, sum) partial at part[blockIdx.x * WAVES + wave]
 template <int DT>
@@ -577,10 +690,8 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
     const int b = row / R, r = row - b * R;
     const char *rp = (r <= K) ? tgt + ((size_t)b * (K + 1) + r) * (size_t)V * BY
                               : drf + ((size_t)b * K + (r - K - 1)) * (size_t)V * BY;
-    float x[NV_STATS][E];
-    load_chunk<DT, NV_STATS>(rp, aligned16(rp), c * WG * NV_STATS * E, V, x);
     float m, s;
-    thread_stats<E, NV_STATS>(x, sc, m, s);
+    sampling_chunk_stats<DT>(rp, V, c, sc, m, s);
     // each wave stores its own partial: no barrier holds the workgroup at its end (measured
     // 1-2.5 us faster per launch at B=256, K=8, V=128256 than one 32-byte store after a barrier)
     const float2 ws = wave_stats(m, s, sc);
@@ -1129,11 +1240,8 @@ template <int DT>
 __device__ __forceinline__ void row_chunk_stats(const char *rp, int V, int c, const Scale &sc,
                                                 float2 *dst)
 {
-    constexpr int E = Elt<DT>::EPV;
-    float x[NV_STATS][E];
-    load_chunk<DT, NV_STATS>(rp, aligned16(rp), c * WG * NV_STATS * E, V, x);
     float m, s;
-    thread_stats<E, NV_STATS>(x, sc, m, s);
+    sampling_chunk_stats<DT>(rp, V, c, sc, m, s);  // as k_stats_sampling: the same bits
     store_wave_partials(wave_stats(m, s, sc), dst);
 }
 
