@@ -222,16 +222,37 @@ template <typename T> __device__ inline T wave_sum_lds(T v)
 __device__ inline float half_max(float v) { return xmax<5>(v); }
 __device__ inline double half_sum(double v) { return xsum<5>(v); }
 
-// inclusive prefix sum over the wave's lanes (fixed order)
-__device__ inline double wave_incl_scan(double v, int lane)
+// Inclusive prefix sum of a double over the wave's lanes, with DPP moves (fixed order): row
+// shifts by 1, 2, 4, 8 give each 16-lane row its own scan, then lane 15's total is added into
+// rows 1 and 3 (row_bcast:15) and lane 31's into rows 2 and 3 (row_bcast:31).  Lanes with no
+// source read 0.  The whole wave must be active.
+template <int CTRL, int ROWS> __device__ __forceinline__ double dpp_move(double v)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double n = __shfl_up(v, o);
-        if (lane >= o)
-            v += n;
-    }
+    return __hiloint2double(__builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xF, false),
+                            __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xF, false));
+}
+
+__device__ inline double wave_incl_scan(double v)
+{
+    v += dpp_move<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_move<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_move<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_move<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_move<0x142, 0xA>(v);  // row_bcast:15, rows 1 and 3
+    v += dpp_move<0x143, 0xC>(v);  // row_bcast:31, rows 2 and 3
     return v;
+}
+
+// The exclusive prefix from the inclusive one: each lane takes its left neighbour's value
+// (DPP wave_shr:1), lane 0 takes 0.
+__device__ inline double wave_excl_from_incl(double inc) { return dpp_move<0x138, 0xF>(inc); }
+
+// A lane's value read by the whole wave; the lane index must be the same in every lane.
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_value(double v, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
 }
 
 // lexicographic "better": larger value, then lower id
@@ -987,10 +1008,8 @@ __device__ inline void find_unit_block(const double *units, int nu, float u01, i
     double ts = 0.0;
     for (int k = k0; k < k1; ++k)
         ts += units[k];
-    const double inc = wave_incl_scan(ts, lane);
-    double exc = __shfl_up(inc, 1);
-    if (lane == 0)
-        exc = 0.0;
+    const double inc = wave_incl_scan(ts);
+    const double exc = wave_excl_from_incl(inc);
     if (lane == 63)
         sw[w] = inc;
     __syncthreads();
@@ -1020,8 +1039,8 @@ __device__ inline void find_unit_block(const double *units, int nu, float u01, i
     // highest lane that has one
     const unsigned long long hm = __ballot(hit >= 0), pm = __ballot(last >= 0);
     const int lh = hm ? __builtin_ctzll(hm) : 0, lp = pm ? 63 - __builtin_clzll(pm) : 0;
-    const int wh = __shfl(hit, lh), wl = __shfl(last, lp);
-    const double whb = __shfl(hb, lh), wlb = __shfl(lb, lp);
+    const int wh = lane_value(hit, lh), wl = lane_value(last, lp);
+    const double whb = lane_value(hb, lh), wlb = lane_value(lb, lp);
     if (lane == 0) {
         sh[w] = hm ? wh : -1;
         shb[w] = whb;
@@ -1035,8 +1054,8 @@ __device__ inline void find_unit_block(const double *units, int nu, float u01, i
         const double hbv = in ? shb[lane] : 0.0, lbv = in ? slb[lane] : 0.0;
         const unsigned long long hmk = __ballot(hv >= 0), lmk = __ballot(lv >= 0);
         const int fh = hmk ? __builtin_ctzll(hmk) : 0, fl = lmk ? 63 - __builtin_clzll(lmk) : 0;
-        const int uh = __shfl(hv, fh), ul = __shfl(lv, fl);
-        const double bh = __shfl(hbv, fh), bl = __shfl(lbv, fl);
+        const int uh = lane_value(hv, fh), ul = lane_value(lv, fl);
+        const double bh = lane_value(hbv, fh), bl = lane_value(lbv, fl);
         if (lane == 0) {
             *s_unit = hmk ? uh : (lmk ? ul : -1);
             *s_base = hmk ? bh : (lmk ? bl : 0.0);
@@ -1069,10 +1088,8 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
             wv[k] = 0.0f;
     }
     const float vsum = tree_sum<E>(wv);
-    const double inc = wave_incl_scan((double)vsum, lane);
-    double exc = __shfl_up(inc, 1);
-    if (lane == 0)
-        exc = 0.0;
+    const double inc = wave_incl_scan((double)vsum);
+    const double exc = wave_excl_from_incl(inc);
     const double bt = base + exc;
     const unsigned long long hit = __ballot(!fb && vsum > 0.0f && bt + (double)vsum > tt);
     const unsigned long long pos = __ballot(vsum > 0.0f);
