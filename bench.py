@@ -115,7 +115,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed calls first: the GPU takes ~60 calls of this size (~12 ms) to reach "
+                         "its steady clocks")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work for the oracle baseline sample (0 disables it)")

@@ -431,27 +431,20 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
     }
 }
 
-// The same chunk as load_chunk, kept as NV raw 16-byte words per thread (ids >= V read as
-// -inf bits): vectors wholly below V in an aligned row are one streamed load each, the rest
-// are packed element by element.  Holding the packed words instead of NV*E floats keeps the
-// sampling statistics kernel at 46 VGPRs, 8 waves per SIMD.
-template <int DT>
-__device__ inline uint4 pack_elems(const char *rp, int e0, int V)
+// The same chunk of a bfloat16 row as load_chunk, kept as NV packed 16-byte words per thread
+// (ids >= V read as -inf bits): vectors wholly below V in an aligned row are one streamed
+// load each, the rest are packed element by element (element 2j in the low half of word j).
+// Holding the packed words instead of NV*8 floats keeps the sampling statistics kernel at 46
+// VGPRs, 8 waves per SIMD.
+__device__ inline uint4 pack_bf16(const char *rp, int e0, int V)
 {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(rp);
     uint32_t w[4];
-    if constexpr (Elt<DT>::EPV == 8) {  // bfloat16: element 2j in the low half of word j
-        const uint16_t *h = reinterpret_cast<const uint16_t *>(rp);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = (e0 + 2 * j < V) ? (uint32_t)h[e0 + 2 * j] : 0xff80u;
-            const uint32_t hi = (e0 + 2 * j + 1 < V) ? (uint32_t)h[e0 + 2 * j + 1] : 0xff80u;
-            w[j] = lo | (hi << 16);
-        }
-    } else {
-        const uint32_t *f = reinterpret_cast<const uint32_t *>(rp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = (e0 + j < V) ? f[e0 + j] : 0xff800000u;
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (e0 + 2 * j < V) ? (uint32_t)h[e0 + 2 * j] : 0xff80u;
+        const uint32_t hi = (e0 + 2 * j + 1 < V) ? (uint32_t)h[e0 + 2 * j + 1] : 0xff80u;
+        w[j] = lo | (hi << 16);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -460,8 +453,9 @@ template <int DT, int NV>
 __device__ inline void load_chunk_words(const char *rp, bool al, int cbase, int V,
                                         uint4 (&raw)[NV])
 {
+    static_assert(Elt<DT>::EPV == 8, "packed words are used for bfloat16 rows only");
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
-    constexpr uint32_t NEG_INF_WORD = (BY == 2) ? 0xff80ff80u : 0xff800000u;
+    constexpr uint32_t NEG_INF_WORD = 0xff80ff80u;
     if (al && cbase + WG * NV * E <= V) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -475,7 +469,7 @@ __device__ inline void load_chunk_words(const char *rp, bool al, int cbase, int 
             else if (e0 >= V)
                 raw[i] = make_uint4(NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD, NEG_INF_WORD);
             else
-                raw[i] = pack_elems<DT>(rp, e0, V);
+                raw[i] = pack_bf16(rp, e0, V);
         }
     }
 }
