@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_row_amd", "csrc", "sv_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
 
 # workload key -> (description, timed kernel kind, its kernel name, traffic summary file)
 WORKLOADS = {
@@ -75,7 +76,7 @@ def measured_traffic(name):
     summary, if there is one and it was taken on the current kernel source; else None."""
     if not name:
         return None
-    path = os.path.join(ROOT, "profiles", name)
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     vals = {}
