@@ -888,9 +888,11 @@ __device__ inline void raw_weights(const DrawRows &r, const uint4 &a, const uint
 // thread t holds the NV vectors base + i*TAIL_WG*E + [0, E), base = the iteration's first id
 // + t*E, so a wave's loads are 1 KiB contiguous.  NV = NV_TAIL when a draft-side row is read
 // as well (TWO), 2 * NV_TAIL when only the target row is: the same bytes in flight either
-// way.  In an aligned row every vector is one streamed 16-byte buffer load per row read;
-// the ones at or past V read zeros and are not used (tail_weigh weighs the vector that
-// straddles V element by element and gives the ones past it weight 0).
+// way.  In an aligned row every vector is one streamed 16-byte buffer load per row read.
+// The whole byte offset goes in the VGPR operand, the part the range check covers (the SGPR
+// offset is outside it), so the ones at or past V read zeros from the V-element resource and
+// never touch memory past the row; they are not used either (tail_weigh weighs the vector
+// that straddles V element by element and gives the ones past it weight 0).
 template <int DT, int NV, bool TWO>
 __device__ inline void tail_load(const DrawRows &r, int it_first, int V, uint4 (&a)[NV],
                                  uint4 (&q)[NV])
@@ -898,18 +900,17 @@ __device__ inline void tail_load(const DrawRows &r, int it_first, int V, uint4 (
     constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, STRIDE = TAIL_WG * Elt<DT>::EPV;
     if (!r.al)
         return;
-    const int vo = (int)threadIdx.x * E * BY;   // this thread's byte offset in a vector slot
+    const int vo = ((int)threadIdx.x * E + it_first) * BY;   // this thread's first vector
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int so = (it_first + i * STRIDE) * BY;
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.b0, vo, so, 2);  // 2: nontemporal
+        const u32x4 v =
+            __builtin_amdgcn_raw_buffer_load_b128(r.b0, vo + i * STRIDE * BY, 0, 2);  // 2: nontemporal
         a[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
     if constexpr (TWO) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int so = (it_first + i * STRIDE) * BY;
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.b1, vo, so, 2);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.b1, vo + i * STRIDE * BY, 0, 2);
             q[i] = make_uint4(v.x, v.y, v.z, v.w);
         }
     }
