@@ -10,8 +10,9 @@ step reads logits the previous one left in the 256 MB last-level cache.
 
 Prints one JSON line: verified draft positions/s (B*K per step), the dominant kernel's
 bytes/s against the 8 TB/s HBM peak (HIP events attached to that kernel's dispatch on the
-call's stream, in every 8th step of the timed loop), and the fp64 CPU oracle timed on a
-bounded sample of the same batch.
+call's stream, in every 8th step of the timed loop), the fp64 CPU oracle timed on a bounded
+sample of the same batch (on one thread, then on all host threads up to 16), and a check of
+the GPU's outputs for the whole batch against that oracle run.
 
 --workload names one of the other synthetic workloads (the tiny and mid-size sampling ones,
 greedy blockwise, contrastive, and the operations next to the verify step: the draft-token
@@ -93,23 +94,148 @@ def measured_traffic(name):
         return None
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle, single-threaded, one sequence at a time in batch order (starting over at
-    the end of the batch) until `seconds` have passed."""
+def percentiles(ms: list) -> dict:
+    """p10, median and p90 of the timed launches' durations (ms), by linear interpolation."""
+    if not ms:
+        return {"p10_ms": None, "median_ms": None, "p90_ms": None}
+    xs = sorted(ms)
+
+    def q(f):
+        x = f * (len(xs) - 1)
+        i = int(x)
+        j = min(i + 1, len(xs) - 1)
+        return xs[i] + (xs[j] - xs[i]) * (x - i)
+
+    return {"p10_ms": q(0.1), "median_ms": q(0.5), "p90_ms": q(0.9)}
+
+
+CPU_SHARE = 16   # host threads that go with one GPU
+
+
+def host_threads() -> int:
+    """Threads for the oracle's parallel leg: the CPUs this process may run on, at most the
+    host share of one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(CPU_SHARE, n))
+
+
+def run_calls(work, threads: int, seconds: float, first: int):
+    """Call work(i) for i = 0, 1, 2, ... on `threads` threads until `seconds` of wall time
+    have passed and every i < first has been called.  ctypes releases the GIL inside the
+    oracle's C functions, so the threads run side by side.  Returns (calls finished, wall
+    seconds, {i: work(i) for i < first})."""
+    import itertools
+    import threading
+    ids, lock, firsts, done = itertools.count(), threading.Lock(), {}, [0]
+    t0 = time.perf_counter()
+
+    def loop():
+        while True:
+            with lock:
+                i = next(ids)
+            if i >= first and time.perf_counter() - t0 >= seconds:
+                return
+            r = work(i)
+            with lock:
+                done[0] += 1
+                if i < first:
+                    firsts[i] = r
+
+    pool = [threading.Thread(target=loop) for _ in range(threads)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    return done[0], time.perf_counter() - t0, firsts
+
+
+def cpu_baseline(w, seconds: float, threads: int = 0):
+    """The oracle (fp64 C), one sequence per call in batch order, starting over at the end of
+    the batch: a single-threaded leg for a third of `seconds`, then `threads` threads (all the
+    host threads, up to the share of one GPU) for about two thirds of `seconds` of CPU work,
+    and never less than one pass over the batch.  Returns the baseline (the parallel leg's
+    rate) and the parallel leg's first result for every sequence, for oracle_check."""
     import oracle
     oracle.build(force=False)
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        oracle.run_workload(w.subset([done % w.B]))
-        done += 1
-    dt = time.perf_counter() - t0
-    if w.mode == "sample":
-        value, unit, what = done / dt, "sampled tokens/s", "rows"
-    else:
-        value, unit, what = done * w.K / dt, "verified draft positions/s", "sequences"
-    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": "%d %s (%.2f passes over the %d of the same batch), one at a time, "
-                      "%.1f s single-threaded fp64 C" % (done, what, done / w.B, w.B, dt)}
+    threads = threads or host_threads()
+
+    def work(i):
+        return oracle.run_workload(w.subset([i % w.B]))
+
+    n1, dt1, _ = run_calls(work, 1, seconds / 3, 0)
+    n, dt, firsts = run_calls(work, threads, 2 * seconds / 3 / threads, w.B)
+    per = 1 if w.mode == "sample" else w.K
+    unit = "sampled tokens/s" if w.mode == "sample" else "verified draft positions/s"
+    what = "rows" if w.mode == "sample" else "sequences"
+    return {"value": n * per / dt, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": "%d %s (%.2f passes over the %d of the same batch) on %d threads in "
+                      "%.2f s, one %s per oracle call, fp64 C" % (n, what, n / w.B, w.B, threads,
+                                                                  dt, what[:-1]),
+            "single_core_value": n1 * per / dt1,
+            "single_core_sample": "%d %s in %.1f s on one thread" % (n1, what, dt1)}, firsts
+
+
+def oracle_check(w, gpu: dict, firsts: dict, early: bool = False) -> dict:
+    """The GPU's outputs for the whole batch against the oracle's (firsts[b] = the oracle on
+    sequence b alone), under the tests' parity rule: greedy ids, lengths and next proposals
+    exact; sampling, contrastive and the sampler exact wherever the oracle's decision margins
+    are >= 1e-6 (low-margin draws may take the id across the interval edge, low-margin accept
+    tests need only a well-formed result); probabilities within 1e-5 relative."""
+    import numpy as np
+    import oracle
+    low = oracle.LOW_MARGIN
+
+    def close(g, o):
+        g, o = np.asarray(g, np.float64), np.asarray(o, np.float64)
+        return bool(np.all(np.abs(g - o) <= 1e-5 * np.maximum(np.abs(g), np.abs(o)) + 1e-30))
+
+    exact = lowm = bad = 0
+    for b in range(w.B):
+        o = firsts[b]
+        if w.mode == "sample":
+            tg, to = int(gpu["out"][b, 0]), int(o.tokens[0])
+            if o.margin[0] >= low:
+                ok = tg == to
+                exact += ok
+            else:
+                lowm += 1
+                ok = tg in (to, int(o.alt_token[0]))
+            ok = ok and close(gpu["draw_p"][b], o.probs[0])
+        elif w.mode in ("greedy", "greedy_heads"):
+            ok = (int(gpu["acc"][b]) == int(o.accepted_len[0])
+                  and np.array_equal(gpu["out"][b], o.out_tokens[0]))
+            if w.mode == "greedy_heads":
+                ok = ok and np.array_equal(gpu["next"][b], o.next_proposals[0])
+            exact += ok
+        else:
+            Lg, Lo = int(gpu["acc"][b]), int(o.accepted_len[0])
+            tg, to = gpu["out"][b], o.out_tokens[0]
+            ma, ms = float(o.margin_accept[0]), float(o.margin_sample[0])
+            if Lo < 0:
+                ok = Lg == -1 and bool(np.all(tg == -1))
+            elif ma >= low and ms >= low:
+                ok = Lg == Lo and np.array_equal(tg, to)
+                exact += ok
+            elif ma >= low:
+                lowm += 1
+                ok = (Lg == Lo and np.array_equal(tg[:Lo], to[:Lo])
+                      and int(tg[Lo]) in (int(to[Lo]), int(o.alt_token[0]))
+                      and bool(np.all(tg[Lo + 1:] == -1)))
+            else:
+                lowm += 1
+                ok = (0 <= Lg <= w.K and np.array_equal(tg[:Lg], w.tokens[b, :Lg])
+                      and 0 <= int(tg[Lg]) < w.V and bool(np.all(tg[Lg + 1:] == -1)))
+            if ok and Lo >= 0 and w.K > 0:
+                nj = min(Lg + 1, w.K) if early else w.K   # early exit: probabilities up to L
+                ok = close(gpu["probs"][b, :nj], o.out_probs[0, :nj])
+        bad += not ok
+    return {"items": w.B, "bit_exact": int(exact), "low_margin": int(lowm),
+            "mismatched": int(bad),
+            "rule": "ids and lengths exact where the oracle's margins are >= 1e-6, "
+                    "probabilities within 1e-5 relative"}
 
 
 def main():
@@ -203,6 +329,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    kdur = sv.specverify_profile_launches(ctx, kind)
     kms, kn = sv.specverify_profile_end(ctx)
     mean_L = float(acc.float().mean().item())
     # per-kernel breakdown from a separate, untimed pass with events around every kernel
@@ -220,6 +347,8 @@ def main():
         torch.cuda.synchronize()
         log("copied %d bytes once for counter calibration" % src.nbytes)
     sv.specverify_destroy(ctx)
+    gout = {"acc": acc.cpu().numpy(), "out": out.cpu().numpy(), "probs": probs.cpu().numpy(),
+            "next": nxt.cpu().numpy(), "draw_p": draw_p.cpu().numpy()}
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = kms[kind] / max(kn[kind], 1)
@@ -268,13 +397,17 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(traffic_file),
                      "kernel": kname, "algorithmic_bytes": kern_bytes, "avg_ms": kern_ms,
-                     "timed_launches": kn[kind], "timing_stride": TIMING_STRIDE},
+                     **percentiles(kdur), "timed_launches": kn[kind],
+                     "timing_stride": TIMING_STRIDE},
         "kernels_ms_per_step": {k: bms[k] / bn[k] for k in bms if bn[k]},
         "mean_accepted_len": mean_L if w.mode != synth.SAMPLE else None,
     }
     if args.cpu_seconds > 0:
-        log("CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log("CPU oracle baseline (~%.0f s of CPU work)" % args.cpu_seconds)
+        res["cpu_baseline"], firsts = cpu_baseline(w, args.cpu_seconds)
+        res["oracle_check"] = oracle_check(w, gout, firsts, early)
+        if res["oracle_check"]["mismatched"]:
+            log("the GPU's outputs disagree with the oracle's: %s" % res["oracle_check"])
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
@@ -310,8 +443,10 @@ def bench_cut(args, desc, kind, kname):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    kdur = sv.specverify_profile_launches(ctx, kind)
     kms, kn = sv.specverify_profile_end(ctx)
     sv.specverify_destroy(ctx)
+    gcut, gkeep, gn = cut.cpu().numpy(), keep.cpu().numpy(), n.cpu().numpy()
     ms_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = kms[kind] / max(kn[kind], 1)
     nbytes = P * N * 4 + P * N + P * 8               # scores in; keep bytes, cut and count out
@@ -325,22 +460,37 @@ def bench_cut(args, desc, kind, kname):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": kname, "algorithmic_bytes": nbytes, "avg_ms": kern_ms,
-                     "timed_launches": kn[kind], "timing_stride": TIMING_STRIDE,
+                     **percentiles(kdur), "timed_launches": kn[kind],
+                     "timing_stride": TIMING_STRIDE,
                      "note": "latency-bound: one workgroup per prompt, four selection passes"},
         "mean_kept": float(n.float().mean().item()),
     }
     if args.cpu_seconds > 0:
+        import numpy as np
         import oracle
         oracle.build(force=False)
-        t0, done = time.perf_counter(), 0
-        while time.perf_counter() - t0 < args.cpu_seconds and done < 1000:
-            oracle.quantile_cut(P, N, w.alpha, w.scores)
-            done += 1
-        dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": done * P / dt, "unit": "prompts/s", "cores": 1,
+        threads = host_threads()
+
+        def work(i):
+            return oracle.quantile_cut(P, N, w.alpha, w.scores)
+
+        n1, dt1, _ = run_calls(work, 1, args.cpu_seconds / 3, 0)
+        done, dt, firsts = run_calls(work, threads, 2 * args.cpu_seconds / 3 / threads, 1)
+        res["cpu_baseline"] = {"value": done * P / dt, "unit": "prompts/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": "the whole batch %d times, %.1f s single-threaded C"
-                                         % (done, dt)}
+                               "sample": "the whole batch %d times on %d threads in %.2f s, "
+                                         "C" % (done, threads, dt),
+                               "single_core_value": n1 * P / dt1,
+                               "single_core_sample": "the whole batch %d times in %.1f s on "
+                                                     "one thread" % (n1, dt1)}
+        o = firsts[0]
+        same = ((o.r_cut.view(np.uint32) == gcut.view(np.uint32))
+                & (o.keep == gkeep.astype(bool)).all(axis=1) & (o.n_keep == gn))
+        res["oracle_check"] = {"items": P, "bit_exact": int(same.sum()), "low_margin": 0,
+                               "mismatched": int(P - same.sum()),
+                               "rule": "cut value (bits), keep mask and count exact"}
+        if res["oracle_check"]["mismatched"]:
+            log("the GPU's outputs disagree with the oracle's: %s" % res["oracle_check"])
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -224,14 +224,21 @@ const char *specverify_strerror(int status);
  * attached to the dispatch (hipExtLaunchKernel), on the call's stream; its duration is the
  * kernel's own execution.  A timed dispatch costs a few microseconds more than an untimed
  * one, so a stride above 1 keeps the timing out of the rate of a long run of calls.
+ * specverify_profile_launches(ctx, kind, ms, cap), between begin and end, synchronises on the
+ * events of the timed launches of kernel kind `kind` so far and writes their durations in
+ * milliseconds, in call order, into the host array ms[0..cap) (cap 0 with ms NULL only
+ * counts them).  It returns the number of such launches (which may exceed cap: only the
+ * first cap are written) or a negative status.
  * specverify_profile_end(ctx, ms, launches) synchronises on the recorded events, writes the
  * summed milliseconds and launch counts per kind into the two SPECVERIFY_NUM_KERNELS-long
  * arrays (either may be NULL), and releases the events.
  * Errors: EINVAL (NULL ctx, max_calls < 1, stride < 1, unknown kind bits, begin twice, end
- * without begin), EHIP.
+ * or launches without begin, kind outside [0, SPECVERIFY_NUM_KERNELS), cap < 0, cap > 0
+ * with ms NULL), EHIP.
  */
 #define SPECVERIFY_NUM_KERNELS 7
 int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds, int stride);
+int specverify_profile_launches(specverify_ctx *ctx, int kind, float *ms, int cap);
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches);
 
 #ifdef __cplusplus

@@ -82,6 +82,8 @@ def load():
         lib.specverify_strerror.restype = ctypes.c_char_p
         lib.specverify_profile_begin.argtypes = [vp, i, ctypes.c_uint, i]
         lib.specverify_profile_begin.restype = i
+        lib.specverify_profile_launches.argtypes = [vp, i, ctypes.POINTER(ctypes.c_float), i]
+        lib.specverify_profile_launches.restype = i
         lib.specverify_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                                ctypes.POINTER(ctypes.c_int)]
         lib.specverify_profile_end.restype = i
@@ -209,6 +211,19 @@ def specverify_profile_begin(ctx, max_calls: int, kinds=None, stride: int = 1) -
         mask |= 1 << KERNEL_NAMES.index(k)
     _check(load().specverify_profile_begin(ctx, max_calls, mask, stride),
            "specverify_profile_begin")
+
+
+def specverify_profile_launches(ctx, kind: str) -> list:
+    """Durations in ms of the timed launches of kernel `kind` (a KERNEL_NAMES entry) since
+    specverify_profile_begin, in call order."""
+    lib = load()
+    k = KERNEL_NAMES.index(kind)
+    n = lib.specverify_profile_launches(ctx, k, None, 0)
+    _check(min(n, 0), "specverify_profile_launches")
+    ms = (ctypes.c_float * max(n, 1))()
+    got = lib.specverify_profile_launches(ctx, k, ms, n)
+    _check(min(got, 0), "specverify_profile_launches")
+    return list(ms)[:min(n, got)]
 
 
 def specverify_profile_end(ctx):

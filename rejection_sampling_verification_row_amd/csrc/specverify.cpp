@@ -429,6 +429,30 @@ int specverify_profile_begin(specverify_ctx *ctx, int max_calls, unsigned kinds,
     return SPECVERIFY_OK;
 }
 
+int specverify_profile_launches(specverify_ctx *ctx, int kind, float *ms, int cap)
+{
+    if (!ctx || !ctx->prof || kind < 0 || kind >= NK || cap < 0 || (cap > 0 && !ms))
+        return SPECVERIFY_EINVAL;
+    DeviceGuard g(ctx->device);
+    if (g.err != hipSuccess)
+        return SPECVERIFY_EHIP;
+    int n = 0;
+    for (int c = 0; c < ctx->prof_calls; ++c) {
+        if (!(ctx->launched[c] & (1u << kind)))
+            continue;
+        if (n < cap) {
+            hipEvent_t a = ctx->events[((size_t)c * NK + kind) * 2];
+            hipEvent_t b = ctx->events[((size_t)c * NK + kind) * 2 + 1];
+            float t = 0.0f;
+            if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&t, a, b) != hipSuccess)
+                return SPECVERIFY_EHIP;
+            ms[n] = t;
+        }
+        ++n;
+    }
+    return n;
+}
+
 int specverify_profile_end(specverify_ctx *ctx, double *ms, int *launches)
 {
     if (!ctx || !ctx->prof)

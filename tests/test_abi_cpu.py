@@ -62,6 +62,7 @@ def test_null_context_is_rejected_on_the_host():
     assert lib.specverify_destroy(None) == sv.SPECVERIFY_OK
     assert lib.specverify_profile_begin(None, 4, 0, 1) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_profile_end(None, None, None) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_launches(None, 0, None, 0) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_workspace_bytes(None) == 0
     h = ctypes.c_void_p()
     assert lib.specverify_create(None, 0, 1, 1, 1) == sv.SPECVERIFY_EINVAL

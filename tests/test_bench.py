@@ -5,6 +5,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -12,6 +13,7 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 from rejection_sampling_verification_row_amd import synth  # noqa: E402
+import oracle  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -37,10 +39,62 @@ def test_traffic_summary_needs_the_current_kernel_source(tmp_path, monkeypatch):
 
 def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     w = synth.make_sampling(3, 2, 500, synth.F32, 1.0, 5, target_sigma=2.0)
-    cb = bench.cpu_baseline(w, 0.2)
-    assert cb["kind"] == "oracle" and cb["cores"] == 1
+    cb, firsts = bench.cpu_baseline(w, 0.3, threads=2)
+    assert cb["kind"] == "oracle" and cb["cores"] == 2
     assert cb["unit"] == "verified draft positions/s" and cb["value"] > 0
-    assert "passes over the 3" in cb["sample"]
+    assert cb["single_core_value"] > 0 and "on one thread" in cb["single_core_sample"]
+    assert "passes over the 3" in cb["sample"] and "on 2 threads" in cb["sample"]
+    assert sorted(firsts) == [0, 1, 2]          # every sequence at least once
+    assert 1 <= bench.host_threads() <= bench.CPU_SHARE
+
+
+def test_percentiles_interpolate_like_numpy():
+    xs = [5.0, 1.0, 4.0, 2.0, 3.0, 9.0, 7.0]
+    got = bench.percentiles(xs)
+    assert np.allclose([got["p10_ms"], got["median_ms"], got["p90_ms"]],
+                       np.percentile(xs, [10, 50, 90]))
+    assert bench.percentiles([])["median_ms"] is None
+
+
+def test_run_calls_covers_the_first_items_however_short_the_time():
+    seen = []
+    n, dt, firsts = bench.run_calls(lambda i: seen.append(i) or i * i, 3, 0.0, 10)
+    assert sorted(firsts) == list(range(10)) and firsts[7] == 49
+    assert n == len(seen) >= 10
+
+
+def _as_gpu(res, probs=True):
+    g = {"acc": res.accepted_len.copy(), "out": res.out_tokens.copy()}
+    if probs:
+        g["probs"] = res.out_probs.astype(np.float32)
+    return g
+
+
+def test_oracle_check_counts_agreement_and_catches_a_planted_mismatch():
+    w = synth.make_sampling(6, 3, 400, synth.F32, 1.0, 7, target_sigma=2.0)
+    whole = oracle.run_workload(w)                      # stands in for the GPU's outputs
+    firsts = {b: oracle.run_workload(w.subset([b])) for b in range(w.B)}
+    g = _as_gpu(whole)
+    chk = bench.oracle_check(w, g, firsts)
+    assert chk["mismatched"] == 0 and chk["bit_exact"] + chk["low_margin"] == w.B
+    b = next(i for i in range(w.B) if firsts[i].margin[0] >= oracle.LOW_MARGIN)
+    L = int(g["acc"][b])                                # plant a wrong draw in sequence b
+    g["out"][b, L] = (g["out"][b, L] + 1) % w.V
+    assert bench.oracle_check(w, g, firsts)["mismatched"] == 1
+    g = _as_gpu(whole)
+    g["probs"][1, 0, 0] *= 1.001                        # a probability off by 1e-3
+    assert bench.oracle_check(w, g, firsts)["mismatched"] == 1
+
+
+def test_oracle_check_greedy_is_exact():
+    w = synth.make_greedy(5, 4, 300, synth.BF16, 11)
+    whole = oracle.run_workload(w)
+    firsts = {b: oracle.run_workload(w.subset([b])) for b in range(w.B)}
+    g = _as_gpu(whole, probs=False)
+    assert bench.oracle_check(w, g, firsts) | {"rule": ""} == {
+        "items": 5, "bit_exact": 5, "low_margin": 0, "mismatched": 0, "rule": ""}
+    g["acc"][2] = (g["acc"][2] + 1) % (w.K + 1)
+    assert bench.oracle_check(w, g, firsts)["mismatched"] == 1
 
 
 @pytest.mark.gpu
@@ -62,5 +116,8 @@ def test_bench_line_has_the_contract_fields():
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert rf["timed_launches"] == 2 and rf["timing_stride"] == 8   # steps 0 and 8 of 16
+    assert 0 < rf["p10_ms"] <= rf["median_ms"] <= rf["p90_ms"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+    chk = d["oracle_check"]
+    assert chk["items"] == 1 and chk["mismatched"] == 0

@@ -278,6 +278,20 @@ def test_profile_api(ctx):
         run(ctx, w)
     ms, n = sv.specverify_profile_end(ctx)
     assert n["row_stats"] == 3 and n["accept_draw"] == 3   # calls 0, 3 and 6
+    # per-launch durations, in call order, sum to what profile_end reports
+    sv.specverify_profile_begin(ctx, 8, ["row_stats"])
+    for _ in range(3):
+        run(ctx, w)
+    d = sv.specverify_profile_launches(ctx, "row_stats")
+    assert len(d) == 3 and all(x > 0 for x in d)
+    assert sv.specverify_profile_launches(ctx, "accept_draw") == []
+    assert lib.specverify_profile_launches(ctx, 0, None, 0) == 3
+    assert lib.specverify_profile_launches(ctx, sv.SPECVERIFY_NUM_KERNELS, None, 0) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_launches(ctx, 0, None, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_profile_launches(ctx, 0, None, -1) == sv.SPECVERIFY_EINVAL
+    ms, n = sv.specverify_profile_end(ctx)
+    assert n["row_stats"] == 3 and abs(sum(d) - ms["row_stats"]) <= 1e-6 * ms["row_stats"] + 1e-9
+    assert lib.specverify_profile_launches(ctx, 0, None, 0) == sv.SPECVERIFY_EINVAL   # after end
 
 
 # ----------------------------------------------------------------- capacity limits
