@@ -48,8 +48,8 @@ WORKLOADS = {
            "k_argmax<bf16>", "row_argmax_bf16_B512_K8_V32000_traffic.md"),
     "c5": ("contrastive verify B=128 K=4 V=152064 bf16 logits tau=1", "row_stats",
            "k_stats_contrastive<bf16>", "contrastive_stats_bf16_B128_K4_V152064_traffic.md"),
-    "sample": ("draft-token sampler N=256 V=128256 bf16 logits T=0.7", "accept_draw",
-               "k_tail<bf16> (draw: one re-read of every row)", None),
+    "sample": ("draft-token sampler N=256 V=128256 bf16 logits T=0.7", "row_stats",
+               "k_stats_sampling<bf16>", None),
     "heads": ("greedy verify with next-block proposals B=512 K=4 H=4 V=32000 bf16 logits",
               "row_argmax", "k_argmax<bf16> (head 0 rows)", None),
     "cut": ("alpha-quantile cut P=128 N=1000 alpha=0.5 f32 scores", "quantile_cut",
@@ -356,7 +356,7 @@ def main():
     if w.mode == synth.SAMPLE:
         positions = B / (ms_step * 1e-3)             # tokens drawn per second
         unit = "sampled tokens/s"
-        kern_bytes = logit_bytes                     # the draw re-reads every row once
+        kern_bytes = logit_bytes                     # the statistics read every row once
     elif w.mode == synth.GREEDY_HEADS:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"

@@ -1147,6 +1147,105 @@ struct TailArgs {
     int K, V, nch, prefix, mask_probs, split, nu_stride;
 };
 
+// The draw when its weights are the target law p_L (sampling verify's bonus draw at L = K,
+// and the sampler).  The row statistics left every chunk's per-wave partials (m, s), so the
+// chunk sums S_c = sum over the chunk's waves of s * 2^((m - M_p) log2(e)/T) / S_p (fp64, in
+// chunk order) locate the chunk that holds t = u * W, W = sum_c S_c, and only that chunk is
+// read again.  A statistics chunk is two vectors per thread of this workgroup, so the chunk
+// is weighed exactly as an iteration of the whole-row pass with two vectors, into 32 unit
+// sums; one wave finds the unit holding t and the id inside it as that pass does.  The chunk
+// sums carry the fp32 rounding of the statistics (about 1e-7 relative each), the same order
+// as the whole-row pass's unit sums.  Returns false, having written nothing, if every chunk
+// weighs 0 or rounding leaves the chosen chunk's ids without weight; the caller then makes
+// the draw from a pass over the whole row.
+template <int DT>
+__device__ __forceinline__ bool chunk_draw(const TailArgs &a, const DrawRows &r,
+                                           const SeqInfo &si, int b, float u01, double *units,
+                                           int32_t *out, float *out_prob)
+{
+    __shared__ int s_c, s_fb, s_u;
+    __shared__ double s_base, s_t;
+    constexpr int E = Elt<DT>::EPV, NVC = 2, CH = TAIL_WG * NVC * E;
+    static_assert(CH == WG * NV_STATS * E, "a statistics chunk is two vectors per tail thread");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, nch = a.nch;
+    if (w == 0) {
+        const float2 *pr = a.part + ((size_t)b * (2 * a.K + 1) + si.L) * (size_t)nch * WAVES;
+        double carry = 0.0;
+        for (int c0 = 0; c0 < nch; c0 += 64) {  // units[c] = running total through chunk c
+            const int c = c0 + lane;
+            double sc = 0.0;
+            if (c < nch) {
+#pragma unroll
+                for (int k = 0; k < WAVES; ++k) {
+                    const float2 v = pr[c * WAVES + k];
+                    if (v.y > 0.0f)
+                        sc += (double)v.y * exp2(((double)v.x - (double)si.Mp) * a.sp.c);
+                }
+                sc /= si.Sp;
+            }
+            const double inc = wave_incl_scan(sc) + carry;
+            if (c < nch)
+                units[c] = inc;
+            carry = lane_value(inc, 63);
+        }
+        // lanes read their neighbours' totals next: keep those reads after the writes
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const double tt = (double)u01 * carry;
+        // the first chunk whose running total exceeds tt, else (rounding at u near 1) the
+        // last chunk that adds weight
+        int hit = -1, lastp = -1;
+        for (int c0 = 0; c0 < nch; c0 += 64) {
+            const int c = c0 + lane;
+            const double inc = (c < nch) ? units[c] : 0.0;
+            const double prev = (c < nch && c > 0) ? units[c - 1] : 0.0;
+            const unsigned long long hm = __ballot(c < nch && inc > tt);
+            const unsigned long long pm = __ballot(c < nch && inc > prev);
+            if (hit < 0 && hm)
+                hit = c0 + __builtin_ctzll(hm);
+            if (pm)
+                lastp = c0 + 63 - __builtin_clzll(pm);
+        }
+        const int ck = (hit >= 0) ? hit : lastp;
+        if (lane == 0) {
+            s_c = ck;
+            s_fb = (hit >= 0) ? 0 : 1;
+            s_base = (ck > 0) ? units[ck - 1] : 0.0;
+            s_t = tt;
+        }
+    }
+    __syncthreads();
+    const int ck = s_c;
+    if (ck < 0)
+        return false;
+    uint4 av[NVC], qv[NVC];
+    float vs[NVC];
+    tail_load<DT, NVC, false>(r, ck * CH, a.V, av, qv);
+    tail_weigh<DT, SAMPLING, NVC, false>(r, ck * CH + t * E, a.V, false, si, a.sp, a.sq, av, qv,
+                                         vs);
+    tail_store_units<NVC>(0, vs, units);  // the chunk totals were read before the barrier
+    __syncthreads();
+    if (w == 0) {
+        const bool fb = s_fb != 0;
+        const double base = s_base, tt = s_t;
+        constexpr int NU = NVC * TAIL_WAVES;  // 32 units, in id order
+        const double uv = (lane < NU) ? units[lane] : 0.0;
+        const double inc = wave_incl_scan(uv);
+        const double exc = wave_excl_from_incl(inc);
+        const unsigned long long hm = __ballot(!fb && uv > 0.0 && base + inc > tt);
+        const unsigned long long pm = __ballot(uv > 0.0);
+        const bool fb2 = fb || hm == 0;
+        const int un = pm == 0 ? -1 : (fb2 ? 63 - __builtin_clzll(pm) : __builtin_ctzll(hm));
+        if (un >= 0)
+            search_unit<DT, SAMPLING>(r, si, a.V, NVC, ck * NU + un,
+                                      base + lane_value(exc, un), tt, fb2, false, a.sp, a.sq,
+                                      out, out_prob);
+        if (lane == 0)
+            s_u = un;
+    }
+    __syncthreads();
+    return s_u >= 0;
+}
+
 // `split` workgroups of 1024 threads per sequence, after the row statistics.  Each runs the
 // accept phase (merge, gather, accept tests, L: the same decisions in every one; the first
 // writes the outputs), then weighs its share of the pass over row L (and the draft row L),
@@ -1182,18 +1281,32 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     if (si.L < 0)
         return;
     const DrawRows r = draw_rows<DT, MODE>(a.tgt, a.drf, b, K, V, si.L);
-    // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
-    const bool two = (MODE == CONTRASTIVE) || r.two;
-    const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
-    const int nit = (V + ce - 1) / ce, per_it = nv * TAIL_WAVES, nu = nit * per_it;
     const float u01 = a.unif[(size_t)b * (K + 1) + K];
     int32_t *out = a.out_tokens + (size_t)b * (K + 1) + si.L;
     float *out_prob = a.draw_probs ? a.draw_probs + b : nullptr;
     double *units = dyn;
+    // solo: this workgroup makes the whole-row pass alone (the other workgroups of a split
+    // sequence have left)
+    bool solo = false;
+    if constexpr (MODE == SAMPLING) {
+        if (!r.two) {  // w = p_L: one chunk of the row is read again, not the whole row
+            if (SPLIT && g != 0)
+                return;
+            if (chunk_draw<DT>(a, r, si, b, u01, units, out, out_prob))
+                return;
+            solo = true;
+        }
+    }
+    // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
+    const bool two = (MODE == CONTRASTIVE) || r.two;
+    const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
+    const int nit = (V + ce - 1) / ce, per_it = nv * TAIL_WAVES, nu = nit * per_it;
     for (int pass = 0; pass < 2; ++pass) {
         const bool target_law = (pass == 1);
-        // the first pass is shared by the sequence's workgroups; a repeat is done by one alone
-        const int first = (pass == 0) ? g : 0, step = (pass == 0) ? G : 1;
+        // the first pass is shared by the sequence's workgroups; a repeat, or a pass after a
+        // chunk draw that found no weight, is done by one alone
+        const bool shared = pass == 0 && !solo;
+        const int first = shared ? g : 0, step = shared ? G : 1;
         if (two)
             tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, first, step, target_law, si, a.sp,
                                                     a.sq, units);
@@ -1201,7 +1314,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
             tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, first, step, target_law, si,
                                                          a.sp, a.sq, units);
         __syncthreads();
-        if (SPLIT && pass == 0) {
+        if (SPLIT && shared) {
             double *gu = a.gunits + (size_t)b * a.nu_stride;
             if (w == 0) {
                 // The sums go out as device-coherent stores, and the wave waits until they

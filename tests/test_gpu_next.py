@@ -40,6 +40,43 @@ def test_sampler_small_shapes(ctx, dtype, N, V, misalign):
     compare_sample(w, tok, pr, oracle.run_workload(w))
 
 
+U_LO, U_HI = 0.5 * 2.0 ** -23, 1.0 - 2.0 ** -24   # the two ends of the uniforms' lattice
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_sampler_sparse_rows_and_extreme_uniforms(ctx, dtype, misalign):
+    """All weight in a few ids of a few chunks (every other logit -inf), in some rows only in
+    the ragged last chunk, with uniforms at the two ends of their lattice and in the middle:
+    the draw finds its chunk from the row statistics' chunk sums, and at u near 1 rounding
+    can leave t at the end of the row (the last id of positive weight is then drawn)."""
+    N, V = 30, 3 * 16384 + 777
+    w = synth.make_sampler(N, V, dtype, 1.0, seed=4242, sigma=2.0)
+    rng = np.random.default_rng(4243)
+    x = np.full((N, V), -np.inf, np.float32)
+    for n in range(N):
+        ids = (np.array([V - 1 - n]) if n % 3 == 0
+               else rng.choice(V, size=1 + n % 5, replace=False))
+        x[n, ids] = rng.normal(0.0, 1.5, ids.size).astype(np.float32)
+    w.target = synth.f32_to_bf16_bits(x) if dtype == BF16 else x
+    w.uniforms = np.array([[U_LO], [U_HI], [0.5]] * (N // 3), np.float32)
+    tok, pr = run_sample(ctx, w, misalign=misalign)
+    compare_sample(w, tok, pr, oracle.run_workload(w))
+    finite = np.isfinite(x)
+    assert all(finite[n, tok[n]] for n in range(N))
+
+
+@pytest.mark.parametrize("dtype,V", [(F32, 8192 * 5 + 3), (BF16, 16384 * 7 + 1), (BF16, 16384 * 2)])
+def test_sampler_uniforms_across_the_lattice(ctx, dtype, V):
+    """Uniforms spread over the whole lattice on dense rows of several chunks (so that t falls
+    in every chunk in turn), whole and ragged last chunks."""
+    N = 64
+    w = synth.make_sampler(N, V, dtype, 0.8, seed=77 + V, sigma=1.0)
+    w.uniforms = ((np.arange(N, dtype=np.float64) + 0.5) / N).astype(np.float32).reshape(N, 1)
+    tok, pr = run_sample(ctx, w)
+    compare_sample(w, tok, pr, oracle.run_workload(w))
+
+
 def test_sampler_matches_verify_with_no_draft(ctx):
     """The sampler is the K = 0 case of sampling verify: same ids for the same rows."""
     w = synth.make_sampler(64, 5000, BF16, 0.7, seed=17, sigma=3.0)

@@ -314,6 +314,21 @@ def test_capacity_limits(mode, dtype, B, K, V):
         sv.specverify_destroy(h)
 
 
+@pytest.mark.parametrize("dtype,B,K,V", [(BF16, 6, 3, 16384 * 3 + 5), (F32, 5, 2, 8192 * 4),
+                                         (BF16, 160, 2, 40000), (F32, 150, 1, 9000)])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_bonus_draws_after_accepting_every_token(ctx, dtype, B, K, V, misalign):
+    """An identical draft accepts every token, so every sequence draws its bonus token from
+    p_K alone: from the chunk of row K that the statistics' chunk sums point at (B <= 128 runs
+    the kernel that can share a draw among workgroups, larger B the one-workgroup kernel)."""
+    w = synth.make_sampling(B, K, V, dtype, 0.9, seed=6100 + B + V, target_sigma=2.5,
+                            draft_sigma=0.0)
+    g = run(ctx, w, misalign=misalign)
+    o = oracle.run_workload(w)
+    compare(w, g, o)
+    assert np.all(g.accepted_len == K) and np.all(o.accepted_len == K)
+
+
 def test_split_draw_matches_single_workgroup_draw(ctx):
     """A batch above half the CU count draws each sequence with one workgroup; a small batch
     shares each draw among several.  The same sequences must come out bit for bit the same,
