@@ -7,9 +7,10 @@
 //   k_tail     one 1024-thread workgroup per sequence (or G of them sharing one draw when
 //              the batch is too small to fill the chip) merges the partials in fp64,
 //              gathers p_j(x_j) and q_j(x_j), accepts iff p > 0 and u * q <= p, finds the
-//              first rejection L, re-reads row L into per-unit sums of w = max(0, p - q)
-//              (or p for the bonus draw), locates the unit holding t = u_K * W and emits the
-//              first id whose prefix weight exceeds t.
+//              first rejection L, re-reads row L into per-unit sums of w = max(0, p - q),
+//              locates the unit holding t = u_K * W and emits the first id whose prefix
+//              weight exceeds t.  A draw from p alone (the bonus draw, the sampler) finds
+//              the chunk holding t from the statistics' chunk sums and re-reads only it.
 // With early exit the statistics of the first positions come first (k_stats_prefix or
 // k_pairs_prefix), k_alive lists the sequences not yet rejected there, k_stats_rest /
 // k_pairs_rest read only their remaining rows, and k_tail finishes as above.
