@@ -1148,26 +1148,29 @@ struct TailArgs {
     int K, V, nch, prefix, mask_probs, split, nu_stride;
 };
 
-// The draw when its weights are the target law p_L (sampling verify's bonus draw at L = K,
-// and the sampler).  The row statistics left every chunk's per-wave partials (m, s), so the
-// chunk sums S_c = sum over the chunk's waves of s * 2^((m - M_p) log2(e)/T) / S_p (fp64, in
-// chunk order) locate the chunk that holds t = u * W, W = sum_c S_c, and only that chunk is
-// read again.  A statistics chunk is two vectors per thread of this workgroup, so the chunk
-// is weighed exactly as an iteration of the whole-row pass with two vectors, into 32 unit
-// sums; one wave finds the unit holding t and the id inside it as that pass does.  The chunk
-// sums carry the fp32 rounding of the statistics (about 1e-7 relative each), the same order
-// as the whole-row pass's unit sums.  Returns false, having written nothing, if every chunk
-// weighs 0 or rounding leaves the chosen chunk's ids without weight; the caller then makes
-// the draw from a pass over the whole row.
-template <int DT>
+// The draw when its weights are the target law p_L alone (the bonus draw at L = K, which is
+// every draw of the sampler).  The row statistics left every chunk's per-wave partials (m, s)
+// of p_L, so the chunk sums S_c = sum over the chunk's waves of s * 2^((m - M_p) log2(e)/T) /
+// S_p (fp64, in chunk order) locate the chunk that holds t = u * W, W = sum_c S_c, and only
+// that chunk is read again (contrastive: the chunk of the expert and of the amateur row).  A
+// statistics chunk is NVC vectors per thread of this workgroup (two for sampling rows, one
+// for contrastive row pairs), so it is weighed exactly as an iteration of the whole-row pass
+// with NVC vectors, into NVC * 16 unit sums; one wave finds the unit holding t and the id
+// inside it as that pass does.  The chunk sums carry the fp32 rounding of the statistics
+// (about 1e-7 relative each), the same order as the whole-row pass's unit sums.  Returns
+// false, having written nothing, if every chunk weighs 0 or rounding leaves the chosen
+// chunk's ids without weight; the caller then makes the draw from a pass over the whole row.
+template <int DT, int MODE>
 __device__ __forceinline__ bool chunk_draw(const TailArgs &a, const DrawRows &r,
                                            const SeqInfo &si, int b, float u01, double *units,
                                            int32_t *out, float *out_prob)
 {
     __shared__ int s_c, s_fb, s_u;
     __shared__ double s_base, s_t;
-    constexpr int E = Elt<DT>::EPV, NVC = 2, CH = TAIL_WG * NVC * E;
-    static_assert(CH == WG * NV_STATS * E, "a statistics chunk is two vectors per tail thread");
+    constexpr bool TWO = (MODE == CONTRASTIVE);
+    constexpr int E = Elt<DT>::EPV, NVC = TWO ? 1 : 2, CH = TAIL_WG * NVC * E;
+    static_assert(CH == WG * (TWO ? NV_PAIR : NV_STATS) * E,
+                  "a statistics chunk is NVC vectors per tail thread");
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, nch = a.nch;
     if (w == 0) {
         const float2 *pr = a.part + ((size_t)b * (2 * a.K + 1) + si.L) * (size_t)nch * WAVES;
@@ -1220,9 +1223,8 @@ __device__ __forceinline__ bool chunk_draw(const TailArgs &a, const DrawRows &r,
         return false;
     uint4 av[NVC], qv[NVC];
     float vs[NVC];
-    tail_load<DT, NVC, false>(r, ck * CH, a.V, av, qv);
-    tail_weigh<DT, SAMPLING, NVC, false>(r, ck * CH + t * E, a.V, false, si, a.sp, a.sq, av, qv,
-                                         vs);
+    tail_load<DT, NVC, TWO>(r, ck * CH, a.V, av, qv);
+    tail_weigh<DT, MODE, NVC, TWO>(r, ck * CH + t * E, a.V, false, si, a.sp, a.sq, av, qv, vs);
     tail_store_units<NVC>(0, vs, units);  // the chunk totals were read before the barrier
     __syncthreads();
     if (w == 0) {
@@ -1237,7 +1239,7 @@ __device__ __forceinline__ bool chunk_draw(const TailArgs &a, const DrawRows &r,
         const bool fb2 = fb || hm == 0;
         const int un = pm == 0 ? -1 : (fb2 ? 63 - __builtin_clzll(pm) : __builtin_ctzll(hm));
         if (un >= 0)
-            search_unit<DT, SAMPLING>(r, si, a.V, NVC, ck * NU + un,
+            search_unit<DT, MODE>(r, si, a.V, NVC, ck * NU + un,
                                       base + lane_value(exc, un), tt, fb2, false, a.sp, a.sq,
                                       out, out_prob);
         if (lane == 0)
@@ -1289,14 +1291,12 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     // solo: this workgroup makes the whole-row pass alone (the other workgroups of a split
     // sequence have left)
     bool solo = false;
-    if constexpr (MODE == SAMPLING) {
-        if (!r.two) {  // w = p_L: one chunk of the row is read again, not the whole row
-            if (SPLIT && g != 0)
-                return;
-            if (chunk_draw<DT>(a, r, si, b, u01, units, out, out_prob))
-                return;
-            solo = true;
-        }
+    if (!r.resid) {  // w = p_L: one chunk of the row is read again, not the whole row
+        if (SPLIT && g != 0)
+            return;
+        if (chunk_draw<DT, MODE>(a, r, si, b, u01, units, out, out_prob))
+            return;
+        solo = true;
     }
     // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
     const bool two = (MODE == CONTRASTIVE) || r.two;

@@ -329,6 +329,21 @@ def test_bonus_draws_after_accepting_every_token(ctx, dtype, B, K, V, misalign):
     assert np.all(g.accepted_len == K) and np.all(o.accepted_len == K)
 
 
+@pytest.mark.parametrize("dtype,B,K,V", [(BF16, 6, 3, 8192 * 3 + 5), (F32, 150, 2, 4096 * 5),
+                                         (BF16, 140, 1, 30001)])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_contrastive_bonus_draws_after_accepting_every_token(ctx, dtype, B, K, V, misalign):
+    """With the amateur at exactly half the expert and tau = 1 the contrastive target law
+    softmax(l_e - l_a) equals the amateur's, so every token is accepted and every sequence
+    draws its bonus token from p_K: from one chunk of the expert and the amateur row K."""
+    w = synth.make_contrastive(B, K, V, dtype, 1.0, seed=6200 + B + V, amateur_scale=0.5,
+                               amateur_sigma=0.0)
+    g = run(ctx, w, misalign=misalign)
+    o = oracle.run_workload(w)
+    compare(w, g, o)
+    assert np.all(g.accepted_len == K) and np.all(o.accepted_len == K)
+
+
 def test_split_draw_matches_single_workgroup_draw(ctx):
     """A batch above half the CU count draws each sequence with one workgroup; a small batch
     shares each draw among several.  The same sequences must come out bit for bit the same,
