@@ -66,14 +66,22 @@ def test_sampler_sparse_rows_and_extreme_uniforms(ctx, dtype, misalign):
     assert all(finite[n, tok[n]] for n in range(N))
 
 
-@pytest.mark.parametrize("dtype,V", [(F32, 8192 * 5 + 3), (BF16, 16384 * 7 + 1), (BF16, 16384 * 2)])
+@pytest.mark.parametrize("dtype,V", [(F32, 8192 * 5 + 3), (BF16, 16384 * 7 + 1), (BF16, 16384 * 2),
+                                     (F32, 8192 * 100 + 7), (F32, 1 << 20), (BF16, (1 << 20) - 3)])
 def test_sampler_uniforms_across_the_lattice(ctx, dtype, V):
     """Uniforms spread over the whole lattice on dense rows of several chunks (so that t falls
-    in every chunk in turn), whole and ragged last chunks."""
+    in every chunk in turn), whole and ragged last chunks; float32 rows of more than 64 chunks
+    carry the chunks' running total from one 64-chunk block to the next."""
     N = 64
     w = synth.make_sampler(N, V, dtype, 0.8, seed=77 + V, sigma=1.0)
     w.uniforms = ((np.arange(N, dtype=np.float64) + 0.5) / N).astype(np.float32).reshape(N, 1)
-    tok, pr = run_sample(ctx, w)
+    big = V > 160000   # beyond the module context's vocabulary: a context of its own
+    h = sv.specverify_create(0, N, 0, V) if big else ctx
+    try:
+        tok, pr = run_sample(h, w)
+    finally:
+        if big:
+            sv.specverify_destroy(h)
     compare_sample(w, tok, pr, oracle.run_workload(w))
 
 
