@@ -60,6 +60,15 @@ WORKLOADS = {
                  "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)", None),
 }
 TIMING_STRIDE = 8   # the dominant kernel is timed in steps 0, 8, 16, ... of the timed loop
+TIMED_LAUNCHES = 25  # ... or, in longer runs, in about this many steps spread over the loop
+
+
+def timing_stride(steps: int) -> int:
+    """Time every stride-th step: every 8th, or fewer so that about 25 launches are timed.
+    A timed dispatch costs the call several microseconds more (its completion signalling),
+    which is negligible for a 200 us call but not for a 5 us one, so longer runs of short
+    calls time proportionally fewer of them."""
+    return max(TIMING_STRIDE, steps // TIMED_LAUNCHES)
 METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
 
@@ -293,27 +302,35 @@ def main():
     nxt = torch.empty((B, max(H - 1, 1)), dtype=torch.int32, device="cuda")
     draw_p = torch.empty(B, dtype=torch.float32, device="cuda")
     ctx = sv.specverify_create(0, B, K, V)
-    stream = torch.cuda.current_stream()
+    # The loops pass device addresses and the stream handle as plain integers, which the
+    # binding forwards as they are: checking and converting tensors on every call costs the
+    # Python side several microseconds, more than the GPU needs for the smallest workloads.
+    sh = torch.cuda.current_stream().cuda_stream
+    pcopies = [(a.data_ptr(), None if d is None else d.data_ptr()) for a, d in copies]
+    p_toks, p_acc, p_out = toks.data_ptr(), acc.data_ptr(), out.data_ptr()
+    p_unif = None if unif is None else unif.data_ptr()
+    p_probs, p_nxt, p_draw = probs.data_ptr(), nxt.data_ptr(), draw_p.data_ptr()
 
     def step(i):
-        tg, dr = copies[i & 1]
+        tg, dr = pcopies[i & 1]
         if w.mode == synth.SAMPLE:
-            sv.specverify_sample(ctx, stream, w.dtype, B, V, w.temperature, tg, unif, out, draw_p)
+            sv.specverify_sample(ctx, sh, w.dtype, B, V, w.temperature, tg, p_unif, p_out, p_draw)
         elif w.mode == synth.GREEDY_HEADS:
-            sv.specverify_run_greedy_heads(ctx, stream, w.dtype, B, K, H, V, tg, toks, acc, out,
-                                           nxt)
+            sv.specverify_run_greedy_heads(ctx, sh, w.dtype, B, K, H, V, tg, p_toks, p_acc, p_out,
+                                           p_nxt)
         elif w.mode == synth.GREEDY:
-            sv.specverify_run_greedy(ctx, stream, w.dtype, B, K, V, tg, toks, acc, out)
+            sv.specverify_run_greedy(ctx, sh, w.dtype, B, K, V, tg, p_toks, p_acc, p_out)
         elif early:
             fn = (sv.specverify_run_sampling_early_exit if w.mode == synth.SAMPLING
                   else sv.specverify_run_contrastive_early_exit)
-            fn(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr, toks, unif, acc, out, probs)
+            fn(ctx, sh, w.dtype, B, K, V, w.temperature, tg, dr, p_toks, p_unif, p_acc, p_out,
+               p_probs)
         elif w.mode == synth.CONTRASTIVE:
-            sv.specverify_run_contrastive(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
-                                          toks, unif, acc, out, probs)
+            sv.specverify_run_contrastive(ctx, sh, w.dtype, B, K, V, w.temperature, tg, dr,
+                                          p_toks, p_unif, p_acc, p_out, p_probs)
         else:
-            sv.specverify_run_sampling(ctx, stream, w.dtype, B, K, V, w.temperature, tg, dr,
-                                       toks, unif, acc, out, probs)
+            sv.specverify_run_sampling(ctx, sh, w.dtype, B, K, V, w.temperature, tg, dr,
+                                       p_toks, p_unif, p_acc, p_out, p_probs)
 
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
@@ -321,8 +338,9 @@ def main():
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
     # HIP events on the dominant kernel's dispatch, on the call's stream, in every
-    # TIMING_STRIDE-th timed step (a timed dispatch costs a few microseconds more)
-    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=TIMING_STRIDE)
+    # timing_stride-th timed step (a timed dispatch costs a few microseconds more)
+    stride = timing_stride(args.steps)
+    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=stride)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -398,7 +416,7 @@ def main():
                      "traffic": measured_traffic(traffic_file),
                      "kernel": kname, "algorithmic_bytes": kern_bytes, "avg_ms": kern_ms,
                      **percentiles(kdur), "timed_launches": kn[kind],
-                     "timing_stride": TIMING_STRIDE},
+                     "timing_stride": stride},
         "kernels_ms_per_step": {k: bms[k] / bn[k] for k in bms if bn[k]},
         "mean_accepted_len": mean_L if w.mode != synth.SAMPLE else None,
     }
@@ -428,15 +446,19 @@ def bench_cut(args, desc, kind, kname):
     keep = torch.empty((P, N), dtype=torch.uint8, device="cuda")
     n = torch.empty(P, dtype=torch.int32, device="cuda")
     ctx = sv.specverify_create(0, 1, 0, 1)
-    stream = torch.cuda.current_stream()
+    # plain integer addresses and stream handle, as in the verify loops
+    sh = torch.cuda.current_stream().cuda_stream
+    ps = [x.data_ptr() for x in s]
+    p_cut, p_keep, p_n = cut.data_ptr(), keep.data_ptr(), n.data_ptr()
 
     def step(i):
-        sv.specverify_quantile_cut(ctx, stream, P, N, w.alpha, s[i & 1], cut, keep, n)
+        sv.specverify_quantile_cut(ctx, sh, P, N, w.alpha, ps[i & 1], p_cut, p_keep, p_n)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=TIMING_STRIDE)
+    stride = timing_stride(args.steps)
+    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=stride)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -461,7 +483,7 @@ def bench_cut(args, desc, kind, kname):
                      "frac": nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": kname, "algorithmic_bytes": nbytes, "avg_ms": kern_ms,
                      **percentiles(kdur), "timed_launches": kn[kind],
-                     "timing_stride": TIMING_STRIDE,
+                     "timing_stride": stride,
                      "note": "latency-bound: one workgroup per prompt, four selection passes"},
         "mean_kept": float(n.float().mean().item()),
     }

@@ -1748,29 +1748,34 @@ __global__ __launch_bounds__(TAIL_WG) void k_quantile_cut(const float *__restric
                                                           int32_t *n_keep)
 {
     extern __shared__ uint32_t keys[];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_prefix, s_rank;
+    // two histograms and two (prefix, rank) slots alternate between passes, so that a pass
+    // needs two barriers: the next pass's bins are cleared while wave 0 scans this pass's
+    __shared__ uint32_t hist[2][256];
+    __shared__ uint32_t s_prefix[2], s_rank[2];
     __shared__ int s_cnt[TAIL_WAVES];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float *row = scores + (size_t)blockIdx.x * N;
     for (int i = t; i < N; i += TAIL_WG)
         keys[i] = order_key(row[i]);
+    if (t < 256)
+        hist[0][t] = 0;
+    __syncthreads();
     uint32_t prefix = 0, mask = 0, rank = (uint32_t)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (t < 256)
-            hist[t] = 0;
-        __syncthreads();
+    int pb = 0;
+    for (int shift = 24; shift >= 0; shift -= 8, pb ^= 1) {
         for (int i = t; i < N; i += TAIL_WG) {
             const uint32_t key = keys[i];
             if ((key & mask) == prefix)
-                atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                atomicAdd(&hist[pb][(key >> shift) & 255u], 1u);
         }
         __syncthreads();
+        if (t >= 64 && t < 64 + 256)  // waves 1-4 clear the next pass's bins
+            hist[pb ^ 1][t - 64] = 0;
         if (w == 0) {  // lane l owns bins 4l..4l+3: find the bin holding the rank-th key
             uint32_t c[4], sum = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                c[q] = hist[4 * lane + q];
+                c[q] = hist[pb][4 * lane + q];
                 sum += c[q];
             }
             uint32_t inc = sum;
@@ -1790,20 +1795,20 @@ __global__ __launch_bounds__(TAIL_WG) void k_quantile_cut(const float *__restric
                     below += c[q];
                     ++q;
                 }
-                s_rank = rank - below;
-                s_prefix = prefix | ((uint32_t)(4 * l + q) << shift);
+                s_rank[pb] = rank - below;
+                s_prefix[pb] = prefix | ((uint32_t)(4 * l + q) << shift);
             }
         }
         __syncthreads();
-        rank = s_rank;
-        prefix = s_prefix;
+        rank = s_rank[pb];
+        prefix = s_prefix[pb];
         mask |= 0xffu << shift;
-        __syncthreads();  // everyone has read s_rank / s_prefix before the next pass
     }
     const float cut = key_to_float(prefix);
     int cnt = 0;
     for (int i = t; i < N; i += TAIL_WG) {
-        const bool kk = row[i] >= cut;
+        // the score's own bits, back from its order key: compared as floats (-0 == +0)
+        const bool kk = key_to_float(keys[i]) >= cut;
         keep[(size_t)blockIdx.x * N + i] = kk ? 1 : 0;
         cnt += kk;
     }

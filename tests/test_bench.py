@@ -48,6 +48,12 @@ def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     assert 1 <= bench.host_threads() <= bench.CPU_SHARE
 
 
+def test_timing_stride_keeps_about_25_timed_launches():
+    assert bench.timing_stride(16) == 8 and bench.timing_stride(200) == 8
+    assert bench.timing_stride(2000) == 80
+    assert len(range(0, 2000, bench.timing_stride(2000))) == 25
+
+
 def test_percentiles_interpolate_like_numpy():
     xs = [5.0, 1.0, 4.0, 2.0, 3.0, 9.0, 7.0]
     got = bench.percentiles(xs)
