@@ -131,6 +131,18 @@ def host_threads() -> int:
     return max(1, min(CPU_SHARE, n))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_calls(work, threads: int, seconds: float, first: int):
     """Call work(i) for i = 0, 1, 2, ... on `threads` threads until `seconds` of wall time
     have passed and every i < first has been called.  ctypes releases the GIL inside the
@@ -184,7 +196,8 @@ def cpu_baseline(w, seconds: float, threads: int = 0):
                       "%.2f s, one %s per oracle call, fp64 C" % (n, what, n / w.B, w.B, threads,
                                                                   dt, what[:-1]),
             "single_core_value": n1 * per / dt1,
-            "single_core_sample": "%d %s in %.1f s on one thread" % (n1, what, dt1)}, firsts
+            "single_core_sample": "%d %s in %.1f s on one thread" % (n1, what, dt1),
+            "cpu_model": cpu_model()}, firsts
 
 
 def oracle_check(w, gpu: dict, firsts: dict, early: bool = False) -> dict:
@@ -504,7 +517,8 @@ def bench_cut(args, desc, kind, kname):
                                          "C" % (done, threads, dt),
                                "single_core_value": n1 * P / dt1,
                                "single_core_sample": "the whole batch %d times in %.1f s on "
-                                                     "one thread" % (n1, dt1)}
+                                                     "one thread" % (n1, dt1),
+                               "cpu_model": cpu_model()}
         o = firsts[0]
         # the cut compares as a float: the oracle's sort may return either zero of a tie
         # between -0 and +0, the radix selection on order keys takes -0 first

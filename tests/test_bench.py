@@ -45,6 +45,7 @@ def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     assert cb["single_core_value"] > 0 and "on one thread" in cb["single_core_sample"]
     assert "passes over the 3" in cb["sample"] and "on 2 threads" in cb["sample"]
     assert sorted(firsts) == [0, 1, 2]          # every sequence at least once
+    assert cb["cpu_model"] and cb["cpu_model"] == bench.cpu_model()
     assert 1 <= bench.host_threads() <= bench.CPU_SHARE
 
 
