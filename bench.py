@@ -49,15 +49,18 @@ WORKLOADS = {
     "c5": ("contrastive verify B=128 K=4 V=152064 bf16 logits tau=1", "row_stats",
            "k_stats_contrastive<bf16>", "contrastive_stats_bf16_B128_K4_V152064_traffic.md"),
     "sample": ("draft-token sampler N=256 V=128256 bf16 logits T=0.7", "row_stats",
-               "k_stats_sampling<bf16>", None),
+               "k_stats_sampling<bf16>", "sampler_stats_bf16_N256_V128256_traffic.md"),
     "heads": ("greedy verify with next-block proposals B=512 K=4 H=4 V=32000 bf16 logits",
-              "row_argmax", "k_argmax<bf16> (head 0 rows)", None),
+              "row_argmax", "k_argmax<bf16> (head 0 rows)",
+              "head0_argmax_bf16_B512_K4_H4_V32000_traffic.md"),
     "cut": ("alpha-quantile cut P=128 N=1000 alpha=0.5 f32 scores", "quantile_cut",
             "k_quantile_cut", None),
     "early": ("sampling verify with early exit B=256 K=8 V=128256 bf16 logits T=0.7",
-              "row_stats", "k_stats_prefix<bf16> (positions 0-1 of every sequence)", None),
+              "row_stats", "k_stats_prefix<bf16> (positions 0-1 of every sequence)",
+              "prefix_stats_bf16_B256_K8_V128256_traffic.md"),
     "early_c5": ("contrastive verify with early exit B=128 K=4 V=152064 bf16 logits tau=1",
-                 "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)", None),
+                 "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)",
+                 "prefix_pairs_bf16_B128_K4_V152064_traffic.md"),
 }
 TIMING_STRIDE = 8   # the dominant kernel is timed in steps 0, 8, 16, ... of the timed loop
 TIMED_LAUNCHES = 25  # ... or, in longer runs, in about this many steps spread over the loop
