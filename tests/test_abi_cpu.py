@@ -80,3 +80,65 @@ def test_binding_constants_match_the_header():
     enums = dict((k, int(v)) for k, v in re.findall(r"\b(SPECVERIFY_[A-Z0-9]+) = (-?\d+)", text))
     for k, v in enums.items():
         assert getattr(sv, k) == v, k
+
+
+C_CALLER = r"""
+#include <stddef.h>
+#include <stdint.h>
+#include <stdio.h>
+#include "specverify.h"
+
+/* Every entry point called from plain C with a NULL context: each must return
+   SPECVERIFY_EINVAL before it touches a device. */
+int main(void)
+{
+    int bad = 0, k = 0;
+    specverify_ctx *ctx = NULL;
+#define EXPECT(call, want) do { if ((call) != (want)) bad |= 1 << k; ++k; } while (0)
+    EXPECT(specverify_create(NULL, 0, 1, 1, 1), SPECVERIFY_EINVAL);
+    EXPECT(specverify_create(&ctx, 0, 0, 1, 1), SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_sampling(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, 1.0f, NULL, NULL, NULL,
+                                   NULL, NULL, NULL, NULL), SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_sampling_early_exit(NULL, NULL, SPECVERIFY_F32, 1, 1, 8, 1.0f, NULL,
+                                              NULL, NULL, NULL, NULL, NULL, NULL),
+           SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_contrastive(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, 1.0f, NULL, NULL,
+                                      NULL, NULL, NULL, NULL, NULL), SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_contrastive_early_exit(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, 1.0f,
+                                                 NULL, NULL, NULL, NULL, NULL, NULL, NULL),
+           SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_greedy(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, NULL, NULL, NULL, NULL),
+           SPECVERIFY_EINVAL);
+    EXPECT(specverify_sample(NULL, NULL, SPECVERIFY_F32, 1, 8, 1.0f, NULL, NULL, NULL, NULL),
+           SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_greedy_heads(NULL, NULL, SPECVERIFY_BF16, 1, 1, 2, 8, NULL, NULL, NULL,
+                                       NULL, NULL), SPECVERIFY_EINVAL);
+    EXPECT(specverify_quantile_cut(NULL, NULL, 1, 4, 0.5f, NULL, NULL, NULL, NULL),
+           SPECVERIFY_EINVAL);
+    EXPECT(specverify_profile_begin(NULL, 4, 0u, 1), SPECVERIFY_EINVAL);
+    EXPECT(specverify_profile_launches(NULL, 0, NULL, 0), SPECVERIFY_EINVAL);
+    EXPECT(specverify_profile_end(NULL, NULL, NULL), SPECVERIFY_EINVAL);
+    EXPECT(specverify_workspace_bytes(NULL), 0);
+    EXPECT(specverify_destroy(NULL), SPECVERIFY_OK);
+    if (specverify_strerror(SPECVERIFY_EINVAL) == NULL || ctx != NULL)
+        bad |= 1 << k;
+    printf("%d\n", bad);
+    return bad != 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
+    """A C99 program (pedantic, warnings as errors) includes the header, links against the
+    library and calls every entry point with a NULL context: no C++ in the header, C linkage
+    for every symbol, and host-side rejection before any device work."""
+    sv.load()                                   # builds the library if it is missing
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = str(tmp_path / "caller")
+    libdir = os.path.dirname(build.LIB)
+    subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", exe,
+                    "-L" + libdir, "-lspecverify", "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr)
