@@ -215,6 +215,44 @@ def test_deterministic_and_stream_ordered(ctx):
     assert np.array_equal(a.out_probs.view(np.uint32), b.out_probs.view(np.uint32))
 
 
+def test_two_contexts_on_two_streams_at_once():
+    """One context per concurrent stream: calls on two contexts and two streams, enqueued
+    alternately with no synchronisation between them, give the bits each gives alone (the
+    workspaces, including the shared-draw counters of a small batch, do not interfere)."""
+    wa = synth.c2_sampling_mid(B=24, seed=4100)                       # small B: shared draws
+    wb = synth.make_contrastive(40, 3, 20000, BF16, 1.1, seed=4101)
+    ha, hb = sv.specverify_create(0, 64, 8, 32000), sv.specverify_create(0, 64, 8, 32000)
+    try:
+        alone_a, alone_b = run(ha, wa), run(hb, wb)
+
+        def bufs(w):
+            return dict(tgt=dev(w.target), drf=dev(w.draft), tok=dev(w.tokens),
+                        unif=dev(w.uniforms),
+                        acc=torch.full((w.B,), -7, dtype=torch.int32, device="cuda"),
+                        out=torch.full((w.B, w.K + 1), -7, dtype=torch.int32, device="cuda"),
+                        pr=torch.full((w.B, w.K, 2), -7.0, dtype=torch.float32, device="cuda"))
+
+        a, b = bufs(wa), bufs(wb)
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for _ in range(6):
+            sv.specverify_run_sampling(ha, sa, wa.dtype, wa.B, wa.K, wa.V, wa.temperature,
+                                       a["tgt"], a["drf"], a["tok"], a["unif"], a["acc"],
+                                       a["out"], a["pr"])
+            sv.specverify_run_contrastive(hb, sb, wb.dtype, wb.B, wb.K, wb.V, wb.temperature,
+                                          b["tgt"], b["drf"], b["tok"], b["unif"], b["acc"],
+                                          b["out"], b["pr"])
+        torch.cuda.synchronize()
+        for alone, got in ((alone_a, a), (alone_b, b)):
+            assert np.array_equal(got["acc"].cpu().numpy(), alone.accepted_len)
+            assert np.array_equal(got["out"].cpu().numpy(), alone.out_tokens)
+            assert np.array_equal(got["pr"].cpu().numpy().view(np.uint32),
+                                  alone.out_probs.view(np.uint32))
+    finally:
+        sv.specverify_destroy(ha)
+        sv.specverify_destroy(hb)
+
+
 def test_null_out_probs(ctx):
     w = synth.c1_sampling_tiny(B=8, seed=5)
     a = run(ctx, w, with_probs=False)
