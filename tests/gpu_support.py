@@ -69,6 +69,24 @@ def run(ctx: int, w, misalign: int = 0, stream=None, with_probs: bool = True) ->
                   None if probs is None else probs.cpu().numpy())
 
 
+def oracle_whole_batch(w, threads: int = 0) -> oracle.Result:
+    """The oracle on every sequence of a sampling, contrastive or greedy workload, one sequence
+    per call on a pool of threads (ctypes releases the GIL inside the C call), stitched back
+    into one result in batch order: the same values as one call over the whole batch."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    n = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(lambda b: oracle.run_workload(w.subset([b])), range(w.B)))
+
+    def cat(name):
+        first = getattr(parts[0], name)
+        return None if first is None else np.concatenate([getattr(q, name) for q in parts])
+
+    return oracle.Result(cat("accepted_len"), cat("out_tokens"), cat("out_probs"),
+                         cat("margin_accept"), cat("margin_sample"), cat("alt_token"))
+
+
 @dataclass
 class Report:
     n: int = 0
