@@ -366,9 +366,14 @@ def main():
     kdur = sv.specverify_profile_launches(ctx, kind)
     kms, kn = sv.specverify_profile_end(ctx)
     mean_L = float(acc.float().mean().item())
-    # per-kernel breakdown from a separate, untimed pass with events around every kernel
-    nb = min(args.steps, 20)
-    sv.specverify_profile_begin(ctx, nb)
+    # per-kernel breakdown from a separate pass that times every kernel of every 8th call, as
+    # the timed loop times the dominant one (events on every call slow the kernels down), after
+    # calls that bring the clocks back up from the idle wait at the end of the timed loop
+    nb = min(args.steps, 20 * TIMING_STRIDE)
+    for i in range(min(args.warmup, 60)):
+        step(i)
+    sv.specverify_profile_begin(ctx, (nb + TIMING_STRIDE - 1) // TIMING_STRIDE,
+                                stride=TIMING_STRIDE)
     for i in range(nb):
         step(i)
     torch.cuda.synchronize()
