@@ -58,6 +58,9 @@ WORKLOADS = {
     "early": ("sampling verify with early exit B=256 K=8 V=128256 bf16 logits T=0.7",
               "row_stats", "k_stats_prefix<bf16> (positions 0-1 of every sequence)",
               "prefix_stats_bf16_B256_K8_V128256_traffic.md"),
+    "early_c4": ("greedy blockwise verify with early exit B=512 K=8 V=32000 bf16 logits",
+                 "row_argmax", "k_argmax_prefix<bf16> (positions 0-2 of every sequence)",
+                 "prefix_argmax_bf16_B512_K8_V32000_traffic.md"),
     "early_c5": ("contrastive verify with early exit B=128 K=4 V=152064 bf16 logits tau=1",
                  "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)",
                  "prefix_pairs_bf16_B128_K4_V152064_traffic.md"),
@@ -295,8 +298,8 @@ def main():
     desc, kind, kname, traffic_file = WORKLOADS[args.workload]
     if args.workload == "cut":
         return bench_cut(args, desc, kind, kname)
-    early = args.workload in ("early", "early_c5")
-    base = {"early": "c3", "early_c5": "c5"}.get(args.workload, args.workload)
+    early = args.workload in ("early", "early_c5", "early_c4")
+    base = {"early": "c3", "early_c5": "c5", "early_c4": "c4"}.get(args.workload, args.workload)
     w = (synth.CONFIGS.get(base) or synth.NEXT_CONFIGS[base])()
     B, K, V = w.B, w.K, w.V
     log("generated %s (seed %d); uploading %.3f GB of logits x2"
@@ -335,7 +338,8 @@ def main():
             sv.specverify_run_greedy_heads(ctx, sh, w.dtype, B, K, H, V, tg, p_toks, p_acc, p_out,
                                            p_nxt)
         elif w.mode == synth.GREEDY:
-            sv.specverify_run_greedy(ctx, sh, w.dtype, B, K, V, tg, p_toks, p_acc, p_out)
+            fn = sv.specverify_run_greedy_early_exit if early else sv.specverify_run_greedy
+            fn(ctx, sh, w.dtype, B, K, V, tg, p_toks, p_acc, p_out)
         elif early:
             fn = (sv.specverify_run_sampling_early_exit if w.mode == synth.SAMPLING
                   else sv.specverify_run_contrastive_early_exit)
@@ -403,8 +407,9 @@ def main():
     elif early:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"
-        # positions 0 and 1: target and draft rows (sampling) or expert and amateur rows
-        kern_bytes = 4 * B * V * w.target.itemsize
+        # the prefix: positions 0-1 of the target and draft rows (sampling) or of the expert
+        # and amateur rows (contrastive), positions 0-2 of the target rows (greedy)
+        kern_bytes = (3 if w.mode == synth.GREEDY else 4) * B * V * w.target.itemsize
     else:
         positions = B * K / (ms_step * 1e-3)
         unit = "verified draft positions/s"

@@ -12,8 +12,8 @@
  *    (output distribution identical to the target's), which fixes the replacement law
  *    as the normalised residual max(0, p - q); the bonus token after K acceptances is
  *    the gamma+1 draw of the "Speculative Contrastive Decoding" review, SCD section.
- *  - Greedy blockwise verify: "Blockwise Parallel Decoding", section 3.5 (Verify and
- *    Accept: longest prefix on which the target's argmax equals the proposals).
+ *  - Greedy blockwise verify (also with early exit): "Blockwise Parallel Decoding", section
+ *    3.5 (Verify and Accept: longest prefix on which the target's argmax equals the proposals).
  *  - Contrastive-target verify: "Speculative Contrastive Decoding" review, sections on
  *    contrastive decoding (large-model minus small-model distribution) and SCD.
  *  - Draft-token sampler: "推测性拒绝采样", step 1 (the draft model proposes its tokens one
@@ -150,6 +150,20 @@ int specverify_run_contrastive_early_exit(specverify_ctx *ctx, void *hip_stream,
 int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
                           const void *target_logits, const int32_t *proposals,
                           int32_t *accepted_len, int32_t *out_tokens);
+
+/*
+ * Greedy blockwise verify with early exit: accepted_len and out_tokens exactly as
+ * specverify_run_greedy (the same argmaxes, bit for bit), but a sequence's rows after its
+ * first mismatch are not read, since the emitted tokens stop there ("Blockwise Parallel
+ * Decoding", section 3.5, Accept: the longest matching prefix and the target's token after
+ * it).  Every sequence's first positions are read; the rows after them only for the
+ * sequences whose proposals matched all of them.  Same arguments, layout and errors as
+ * specverify_run_greedy.
+ */
+int specverify_run_greedy_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                     int K, int V, const void *target_logits,
+                                     const int32_t *proposals, int32_t *accepted_len,
+                                     int32_t *out_tokens);
 
 /*
  * Contrastive-target verify: as specverify_run_sampling with the target law

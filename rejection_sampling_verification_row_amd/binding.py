@@ -70,6 +70,8 @@ def load():
         lib.specverify_run_contrastive_early_exit.restype = i
         lib.specverify_run_greedy.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, vp]
         lib.specverify_run_greedy.restype = i
+        lib.specverify_run_greedy_early_exit.argtypes = lib.specverify_run_greedy.argtypes
+        lib.specverify_run_greedy_early_exit.restype = i
         lib.specverify_sample.argtypes = [vp, vp, i, i, i, f, vp, vp, vp, vp]
         lib.specverify_sample.restype = i
         lib.specverify_run_greedy_heads.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp]
@@ -176,6 +178,13 @@ def specverify_run_greedy(ctx, stream, dtype, B, K, V, target_logits, proposals,
     _check(load().specverify_run_greedy(
         ctx, _stream(stream), dtype, B, K, V, _ptr(target_logits), _ptr(proposals),
         _ptr(accepted_len), _ptr(out_tokens)), "specverify_run_greedy")
+
+
+def specverify_run_greedy_early_exit(ctx, stream, dtype, B, K, V, target_logits, proposals,
+                                     accepted_len, out_tokens) -> None:
+    _check(load().specverify_run_greedy_early_exit(
+        ctx, _stream(stream), dtype, B, K, V, _ptr(target_logits), _ptr(proposals),
+        _ptr(accepted_len), _ptr(out_tokens)), "specverify_run_greedy_early_exit")
 
 
 def specverify_sample(ctx, stream, dtype, N, V, temperature, logits, uniforms, out_tokens,

@@ -235,9 +235,11 @@ int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype,
                              out_probs, false);
 }
 
-int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
-                          const void *target_logits, const int32_t *proposals,
-                          int32_t *accepted_len, int32_t *out_tokens)
+namespace {
+
+int run_greedy_like(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
+                    const void *target_logits, const int32_t *proposals, int32_t *accepted_len,
+                    int32_t *out_tokens, bool early_exit)
 {
     int rc = check_common(ctx, dtype, B, K, V);
     if (rc != SPECVERIFY_OK)
@@ -255,10 +257,38 @@ int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int 
         return SPECVERIFY_EHIP;
     hipEvent_t *ev = next_events(ctx);
     sv::Launch ln{static_cast<hipStream_t>(hip_stream), ev, ctx->prof_mask};
-    hipError_t e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
-                                     accepted_len, out_tokens);
-    note_call(ctx, ev, (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT));
+    hipError_t e;
+    unsigned kinds = (1u << sv::KIND_ARGMAX) | (1u << sv::KIND_GREEDY_EMIT);
+    if (early_exit) {
+        // the survivors' rows: as many workgroups as the sampling early exit uses
+        e = sv::launch_greedy_early_exit(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
+                                         accepted_len, out_tokens, 24 * ctx->num_cus);
+        kinds |= (1u << sv::KIND_EARLY_ACCEPT) | (1u << sv::KIND_EARLY_REST);
+    } else {
+        e = sv::launch_greedy(ln, ctx->ws, dtype, B, K, V, target_logits, proposals,
+                              accepted_len, out_tokens);
+    }
+    note_call(ctx, ev, kinds);
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+}  // namespace
+
+int specverify_run_greedy(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K, int V,
+                          const void *target_logits, const int32_t *proposals,
+                          int32_t *accepted_len, int32_t *out_tokens)
+{
+    return run_greedy_like(ctx, hip_stream, dtype, B, K, V, target_logits, proposals,
+                           accepted_len, out_tokens, false);
+}
+
+int specverify_run_greedy_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,
+                                     int K, int V, const void *target_logits,
+                                     const int32_t *proposals, int32_t *accepted_len,
+                                     int32_t *out_tokens)
+{
+    return run_greedy_like(ctx, hip_stream, dtype, B, K, V, target_logits, proposals,
+                           accepted_len, out_tokens, true);
 }
 
 int specverify_run_sampling_early_exit(specverify_ctx *ctx, void *hip_stream, int dtype, int B,

@@ -31,6 +31,8 @@ constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the ac
 constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
 constexpr int MAX_CUT_N = 8192;       // scores per prompt of the quantile cut (32 KiB of LDS)
 constexpr int EARLY_PREFIX = 2;       // positions every sequence reads before early exit
+constexpr int EARLY_PREFIX_GREEDY = 3; // the same for greedy verify (B=512 K=8 V=32000, proposals
+                                      // matching w.p. 0.7: 39.1 us against 41.2 with 2 and 39.5 with 4)
 constexpr int TAIL_MAX_SPLIT = 8;     // most workgroups that share one sequence's draw
 
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
@@ -148,5 +150,12 @@ hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const floa
 hipError_t launch_greedy(const Launch &ln, const Workspace &ws, int dtype, int B, int K, int V,
                          const void *tgt, const int32_t *props, int32_t *acc_len,
                          int32_t *out_tokens);
+
+// greedy verify reading rows only up to each sequence's first mismatch: the first
+// EARLY_PREFIX_GREEDY positions of every sequence, then the rest of the sequences that matched
+// them (rest_grid workgroups); accepted_len and out_tokens exactly as launch_greedy
+hipError_t launch_greedy_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B, int K,
+                                    int V, const void *tgt, const int32_t *props,
+                                    int32_t *acc_len, int32_t *out_tokens, int rest_grid);
 
 }  // namespace sv

@@ -1505,15 +1505,13 @@ __global__ __launch_bounds__(WG) void k_pairs_rest(const char *__restrict__ ex,
 
 // ------------------------------------------------------------------ greedy blockwise
 
-// per chunk of a row: (max, first id of the max) per wave.  Logical row r is stored at row
-// r * row_stride of the input (1 for [B][K+1][V]; H to take head 0 of [B][K+1][H][V]).
+// One chunk of a row (rp, V ids): per wave, the max and the first id of the max, stored at
+// dst[0..WAVES).  Every greedy pass (the full one and the early-exit prefix and rest) computes a
+// chunk with this, so they agree bit for bit.
 template <int DT>
-__global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int V, int nch,
-                                               int row_stride, float2 *part)
+__device__ __forceinline__ void chunk_argmax(const char *rp, int V, int c, float2 *dst)
 {
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
-    const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
-    const char *rp = tgt + (size_t)row * row_stride * (size_t)V * BY;
+    constexpr int E = Elt<DT>::EPV;
     const int cbase = c * WG * NV_ARGMAX * E;
     float x[NV_ARGMAX][E];
     load_chunk<DT, NV_ARGMAX>(rp, aligned16(rp), cbase, V, x);
@@ -1531,7 +1529,19 @@ __global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int
                 bi = cbase + (i * WG + threadIdx.x) * E + k;
             }
     wave_argmax(bv, bi);
-    store_wave_partials(make_float2(bv, __int_as_float(bi)), part + (size_t)blockIdx.x * WAVES);
+    store_wave_partials(make_float2(bv, __int_as_float(bi)), dst);
+}
+
+// per chunk of a row: (max, first id of the max) per wave.  Logical row r is stored at row
+// r * row_stride of the input (1 for [B][K+1][V]; H to take head 0 of [B][K+1][H][V]).
+template <int DT>
+__global__ __launch_bounds__(WG) void k_argmax(const char *__restrict__ tgt, int V, int nch,
+                                               int row_stride, float2 *part)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
+    chunk_argmax<DT>(tgt + (size_t)row * row_stride * (size_t)V * BY, V, c,
+                     part + (size_t)blockIdx.x * WAVES);
 }
 
 // one workgroup per sequence: row argmaxes g_j, then the longest matching prefix
@@ -1574,6 +1584,86 @@ __global__ __launch_bounds__(WG) void k_greedy_final(const int32_t *__restrict__
         ot[lane] = (lane <= L) ? sg[lane] : -1;
     if (lane == 0)
         acc_len[b] = L;
+}
+
+// ------------------------------------------------------------------ greedy with early exit
+//
+// A sequence's emitted tokens stop at its first mismatch, so rows after it are not needed.
+// k_argmax_prefix takes positions 0..prefix-1 of every sequence, k_alive_greedy lists the
+// sequences whose (valid) proposals match the argmax at all of them, k_argmax_rest takes the
+// remaining rows of the listed ones, and k_greedy_final finishes every sequence as in the full
+// pass: a sequence not listed mismatches inside the prefix (or has a bad id), so the rows it
+// did not read are never emitted.
+
+// rows (b, j) for j < prefix, chunk by chunk; workgroup 0 also clears the survivor count
+template <int DT>
+__global__ __launch_bounds__(WG) void k_argmax_prefix(const char *__restrict__ tgt, int K, int V,
+                                                      int nch, int prefix, float2 *part,
+                                                      int *count)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    const int per = prefix * nch;
+    const int b = blockIdx.x / per, rem = blockIdx.x - b * per;
+    const int j = rem / nch, c = rem - j * nch;
+    const size_t row = (size_t)b * (K + 1) + j;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *count = 0;
+    chunk_argmax<DT>(tgt + row * (size_t)V * BY, V, c, part + (row * nch + c) * WAVES);
+}
+
+// One 256-thread workgroup per sequence: the argmaxes g_j of rows j < prefix (merged as
+// k_greedy_final merges them), then alive iff every proposal id is in [0, V) and x_j == g_j
+// for every j < prefix; an alive sequence is appended to list (count = list length).
+__global__ __launch_bounds__(WG) void k_alive_greedy(const int32_t *__restrict__ props, int K,
+                                                     int V, int nch, int prefix,
+                                                     const float2 *__restrict__ part,
+                                                     int *list, int *count)
+{
+    __shared__ int sg[64];
+    const int b = blockIdx.x, P = K + 1;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, np = nch * WAVES;
+    for (int j = w; j < prefix; j += WAVES) {
+        const float2 *pr = part + ((size_t)b * P + j) * np;
+        float v = -INFINITY;
+        int id = INT_MAX;
+        for (int i = lane; i < np; i += 64) {
+            const float2 e = pr[i];
+            take_better(v, id, e.x, __float_as_int(e.y));
+        }
+        wave_argmax(v, id);
+        if (lane == 0)
+            sg[j] = id;
+    }
+    __syncthreads();
+    if (w != 0)
+        return;
+    const int32_t xp = (lane < K) ? props[(size_t)b * K + lane] : 0;
+    const bool bad = (lane < K) && (xp < 0 || xp >= V);
+    const bool miss = (lane < prefix) && xp != sg[lane];
+    const bool live = __ballot(bad) == 0 && __ballot(miss) == 0;
+    if (lane == 0 && live)
+        list[atomicAdd(count, 1)] = b;
+}
+
+// The rows of positions prefix..K of the listed sequences: item i of count * rows * nch is one
+// chunk of one row, taken by workgroup i mod gridDim in turn; the loop bound is read from the
+// count k_alive_greedy left, so every workgroup ends.
+template <int DT>
+__global__ __launch_bounds__(WG) void k_argmax_rest(const char *__restrict__ tgt, int K, int V,
+                                                    int nch, int prefix, float2 *part,
+                                                    const int *__restrict__ list,
+                                                    const int *__restrict__ count)
+{
+    constexpr int BY = Elt<DT>::BYTES;
+    const int per = (K + 1 - prefix) * nch;
+    const long total = (long)(*count) * per;
+    for (long item = blockIdx.x; item < total; item += gridDim.x) {
+        const int a = (int)(item / per), rem = (int)(item - (long)a * per);
+        const int lr = rem / nch, c = rem - lr * nch;
+        const size_t row = (size_t)list[a] * (K + 1) + prefix + lr;
+        chunk_argmax<DT>(tgt + row * (size_t)V * BY, V, c, part + (row * nch + c) * WAVES);
+        __syncthreads();  // the LDS of store_wave_partials is reused by the next item
+    }
 }
 
 // First argmaxes of up to HG rows at once across the workgroup: row h starts at
@@ -1927,6 +2017,32 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
 }
 
 template <int DT>
+hipError_t greedy_early_impl(const Launch &ln, const Workspace &ws, int B, int K, int V,
+                             const void *tgt, const int32_t *props, int32_t *acc_len,
+                             int32_t *out_tokens, int rest_grid)
+{
+    const int nch = num_chunks(NV_ARGMAX, DT, V);
+    const char *t = static_cast<const char *>(tgt);
+    const int prefix = EARLY_PREFIX_GREEDY < K + 1 ? EARLY_PREFIX_GREEDY : K + 1;
+    if (prefix == K + 1) {  // every position is in the prefix: one full pass
+        SV_LAUNCH(ln, KIND_ARGMAX, k_argmax<DT>, dim3((unsigned)((size_t)B * (K + 1) * nch)),
+                  dim3(WG), 0, t, V, nch, 1, ws.part);
+    } else {
+        SV_LAUNCH(ln, KIND_ARGMAX, k_argmax_prefix<DT>, dim3((unsigned)((size_t)B * prefix * nch)),
+                  dim3(WG), 0, t, K, V, nch, prefix, ws.part, ws.count);
+        SV_LAUNCH(ln, KIND_EARLY_ACCEPT, k_alive_greedy, dim3(B), dim3(WG), 0, props, K, V, nch,
+                  prefix, ws.part, ws.list, ws.count);
+        const size_t items = (size_t)B * (K + 1 - prefix) * nch;
+        const unsigned grid = (unsigned)(items < (size_t)rest_grid ? items : rest_grid);
+        SV_LAUNCH(ln, KIND_EARLY_REST, k_argmax_rest<DT>, dim3(grid), dim3(WG), 0, t, K, V, nch,
+                  prefix, ws.part, ws.list, ws.count);
+    }
+    SV_LAUNCH(ln, KIND_GREEDY_EMIT, k_greedy_final, dim3(B), dim3(WG), 0, props, K, V, nch, ws.part,
+              acc_len, out_tokens);
+    return hipGetLastError();
+}
+
+template <int DT>
 hipError_t greedy_impl(const Launch &ln, const Workspace &ws, int B, int K, int V, const void *tgt,
                        const int32_t *props, int32_t *acc_len, int32_t *out_tokens)
 {
@@ -2052,6 +2168,15 @@ hipError_t launch_greedy(const Launch &ln, const Workspace &ws, int dtype, int B
 {
     return dtype == 1 ? greedy_impl<1>(ln, ws, B, K, V, tgt, props, acc_len, out_tokens)
                       : greedy_impl<0>(ln, ws, B, K, V, tgt, props, acc_len, out_tokens);
+}
+
+hipError_t launch_greedy_early_exit(const Launch &ln, const Workspace &ws, int dtype, int B, int K,
+                                    int V, const void *tgt, const int32_t *props,
+                                    int32_t *acc_len, int32_t *out_tokens, int rest_grid)
+{
+    return dtype == 1
+               ? greedy_early_impl<1>(ln, ws, B, K, V, tgt, props, acc_len, out_tokens, rest_grid)
+               : greedy_early_impl<0>(ln, ws, B, K, V, tgt, props, acc_len, out_tokens, rest_grid);
 }
 
 }  // namespace sv

@@ -206,11 +206,16 @@ def run_cut(ctx: int, P: int, N: int, alpha: float, scores: np.ndarray, misalign
 
 
 def run_early(ctx: int, w, misalign: int = 0, with_probs: bool = True) -> GpuOut:
-    """The early-exit entry point of a sampling or contrastive workload."""
+    """The early-exit entry point of a sampling, contrastive or greedy workload."""
     put = (lambda a: dev_offset(a, misalign)) if misalign else dev
     B, K = w.B, w.K
     acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     tok = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+    if w.mode == "greedy":
+        sv.specverify_run_greedy_early_exit(ctx, None, w.dtype, B, K, w.V, put(w.target),
+                                            dev(w.tokens), acc, tok)
+        torch.cuda.synchronize()
+        return GpuOut(acc.cpu().numpy(), tok.cpu().numpy(), None)
     probs = torch.full((B, K, 2), -7.0, dtype=torch.float32, device="cuda") if with_probs else None
     drf = put(w.draft) if w.draft is not None and w.draft.size else None
     fn = (sv.specverify_run_sampling_early_exit if w.mode == "sampling"

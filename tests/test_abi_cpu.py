@@ -109,6 +109,8 @@ int main(void)
            SPECVERIFY_EINVAL);
     EXPECT(specverify_run_greedy(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, NULL, NULL, NULL, NULL),
            SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_greedy_early_exit(NULL, NULL, SPECVERIFY_BF16, 1, 1, 8, NULL, NULL, NULL,
+                                            NULL), SPECVERIFY_EINVAL);
     EXPECT(specverify_sample(NULL, NULL, SPECVERIFY_F32, 1, 8, 1.0f, NULL, NULL, NULL, NULL),
            SPECVERIFY_EINVAL);
     EXPECT(specverify_run_greedy_heads(NULL, NULL, SPECVERIFY_BF16, 1, 1, 2, 8, NULL, NULL, NULL,

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import compare_early, oracle_whole_batch, run, run_early
+from gpu_support import compare, compare_early, oracle_whole_batch, run, run_early
 from rejection_sampling_verification_row_amd import binding as sv
 from rejection_sampling_verification_row_amd import synth
 from rejection_sampling_verification_row_amd.synth import BF16, F32
@@ -104,3 +104,63 @@ def test_contrastive_early_exit_with_survivors(ctx):
     compare_early(w, g, oracle.run_workload(w))
     _same_as_full(ctx, w, g)
     assert np.mean(g.accepted_len >= 2) > 0.5
+
+
+# ----------------------------------------------------------------- greedy with early exit
+
+def _greedy_same_as_full(ctx, w, g):
+    f = run(ctx, w)
+    assert np.array_equal(g.accepted_len, f.accepted_len)
+    assert np.array_equal(g.out_tokens, f.out_tokens)
+
+
+def test_greedy_early_exit_full_size(ctx):
+    """Every sequence of the full-size greedy workload: the oracle's tokens exactly, and the
+    full-read entry point's."""
+    w = synth.CONFIGS["c4"]()
+    g = run_early(ctx, w)
+    rep = compare(w, g, oracle_whole_batch(w))
+    print("\n[early exit %s] %s" % (w.name, rep), flush=True)
+    _greedy_same_as_full(ctx, w, g)
+
+
+@pytest.mark.parametrize("dtype,B,K,V", [(BF16, 7, 0, 100), (F32, 9, 1, 300), (BF16, 11, 2, 16385),
+                                         (F32, 6, 5, 8193), (BF16, 13, 8, 32000),
+                                         (BF16, 3, 16, 5000), (F32, 5, 12, 40001)])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_greedy_early_exit_small_shapes(ctx, dtype, B, K, V, misalign):
+    w = synth.make_greedy(B, K, V, dtype, seed=1700 + B + K + V,
+                          sigma=1.0 if dtype == BF16 else 3.0)
+    g = run_early(ctx, w, misalign=misalign)
+    compare(w, g, oracle.run_workload(w))
+    _greedy_same_as_full(ctx, w, g)
+
+
+@pytest.mark.parametrize("match", [1.0, 0.0])
+def test_greedy_early_exit_all_and_none_matching(ctx, match):
+    """Proposals equal to the argmax everywhere (every sequence reads every row) or nowhere
+    (no sequence reads past the prefix)."""
+    w = synth.make_greedy(40, 6, 20000, BF16, seed=1801, match_prob=match)
+    g = run_early(ctx, w)
+    compare(w, g, oracle.run_workload(w))
+    _greedy_same_as_full(ctx, w, g)
+    assert np.all(g.accepted_len == (6 if match == 1.0 else 0))
+
+
+def test_greedy_early_exit_bad_id_past_the_prefix(ctx):
+    w = synth.make_greedy(8, 6, 3000, F32, seed=1802, match_prob=1.0)
+    w.tokens[5, 4] = 3000
+    g = run_early(ctx, w)
+    assert g.accepted_len[5] == -1 and np.all(g.out_tokens[5] == -1)
+    compare(w, g, oracle.run_workload(w))
+
+
+def test_greedy_early_exit_ignores_rows_left_from_an_earlier_call(ctx):
+    """Rows a sequence does not read keep the previous call's partials in the workspace; they
+    must never reach the output."""
+    first = synth.make_greedy(32, 8, 30000, BF16, seed=1803, match_prob=0.95)
+    second = synth.make_greedy(32, 8, 30000, BF16, seed=1804, match_prob=0.5)
+    run(ctx, first)
+    g = run_early(ctx, second)
+    compare(second, g, oracle.run_workload(second))
+    _greedy_same_as_full(ctx, second, g)
