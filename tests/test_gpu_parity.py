@@ -395,7 +395,8 @@ def test_split_draw_matches_single_workgroup_draw(ctx):
 def test_calls_replay_under_hip_graph_capture(ctx):
     """The run_* calls allocate, clear and synchronise nothing, so a caller may capture them
     in a HIP graph: every replay (with eager work in between) must equal the eager result.
-    The small batch takes the shared-draw path, whose arrival counts must return to zero."""
+    The small batch takes the shared-draw path, whose arrival counts must return to zero; the
+    early-exit calls clear their survivor counts with a kernel, not a memset."""
     ws = synth.make_sampling(24, 5, 40000, BF16, 0.8, seed=61, target_sigma=3.0, draft_sigma=1.2)
     wg = synth.make_greedy(16, 6, 20000, BF16, seed=62, sigma=2.0)
     d = {k: dev(v) for k, v in (("t", ws.target), ("d", ws.draft), ("x", ws.tokens),
@@ -406,7 +407,9 @@ def test_calls_replay_under_hip_graph_capture(ctx):
             "eacc": torch.empty(24, dtype=torch.int32, device="cuda"),
             "etok": torch.empty((24, 6), dtype=torch.int32, device="cuda"),
             "gacc": torch.empty(16, dtype=torch.int32, device="cuda"),
-            "gtok": torch.empty((16, 7), dtype=torch.int32, device="cuda")}
+            "gtok": torch.empty((16, 7), dtype=torch.int32, device="cuda"),
+            "geacc": torch.empty(16, dtype=torch.int32, device="cuda"),
+            "getok": torch.empty((16, 7), dtype=torch.int32, device="cuda")}
     s = torch.cuda.Stream()
 
     def calls():
@@ -416,6 +419,8 @@ def test_calls_replay_under_hip_graph_capture(ctx):
                                               d["d"], d["x"], d["u"], outs["eacc"], outs["etok"])
         sv.specverify_run_greedy(ctx, s, BF16, 16, 6, wg.V, d["gt"], d["gx"], outs["gacc"],
                                  outs["gtok"])
+        sv.specverify_run_greedy_early_exit(ctx, s, BF16, 16, 6, wg.V, d["gt"], d["gx"],
+                                            outs["geacc"], outs["getok"])
 
     with torch.cuda.stream(s):
         calls()
