@@ -82,7 +82,12 @@ enum specverify_status {
  * V <= max_vocab, allocating its device workspace there (a few MB for the largest
  * vocabularies; see specverify_workspace_bytes).  On success *out receives the context.
  * Errors: EINVAL (out NULL, sizes < 1, max_k > SPECVERIFY_MAX_K,
- * max_vocab > SPECVERIFY_MAX_VOCAB), EHIP (bad device), ENOMEM (allocation failed).
+ * max_vocab > SPECVERIFY_MAX_VOCAB, or a capacity whose largest launch would exceed the
+ * 2^32 - 1 work-items one dispatch can cover: with 256 threads per chunk of 8192 float32 ids,
+ * max_batch * (2 * max_k + 1) * ceil(max_vocab / 8192) must stay below 2^24, and likewise
+ * max_batch * (max_k + 1) * ceil(max_vocab / 4096); e.g. max_batch <= 8191 at max_k = 63 and
+ * max_vocab = 128256), EHIP (bad device), ENOMEM (allocation failed).  These are checked
+ * before the device is touched.
  */
 int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab);
 
@@ -200,7 +205,8 @@ int specverify_sample(specverify_ctx *ctx, void *hip_stream, int dtype, int N, i
  * the first argmaxes of heads 1..H-1 at position L, the proposals for the positions after
  * the emitted g_L (-1 for a sequence with bad ids); may be NULL when H = 1.
  * Errors: EINVAL for H < 1 and as specverify_run_greedy; ECAPACITY for B, K or V above the
- * context's capacity.
+ * context's capacity, or B * (H - 1) >= 2^24 (one 256-thread workgroup per sequence and extra
+ * head).
  */
 int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
                                 int H, int V, const void *logits, const int32_t *proposals,
@@ -213,7 +219,8 @@ int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype
  * (k+1)-th smallest score of prompt p, keep[p][i] = (scores[p][i] >= r_cut[p]) as 0/1 bytes,
  * n_keep[p] = the number kept (>= N - k; ties at r_cut are all kept).  Exact: comparisons
  * only.  Errors: EINVAL (NULL pointers, P < 0, N < 1, alpha outside [0, 1] or NaN),
- * ECAPACITY (N > SPECVERIFY_MAX_CUT_N).  Needs no workspace: the context supplies the
+ * ECAPACITY (N > SPECVERIFY_MAX_CUT_N, or P >= 2^22: one 1024-thread workgroup per prompt).
+ * Needs no workspace: the context supplies the
  * device and the timing.
  */
 int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N, float alpha,

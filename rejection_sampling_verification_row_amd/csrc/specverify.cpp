@@ -74,6 +74,22 @@ int check_common(const specverify_ctx *ctx, int dtype, int B, int K, int V)
 
 bool bad_temperature(float t) { return !(t > 0.0f) || !isfinite(t); }
 
+// A dispatch covers at most 2^32 - 1 work-items along its one grid dimension.
+constexpr size_t MAX_ITEMS = 0xffffffffull;
+
+// work-items of the largest launch a context of this capacity can make, over both dtypes: the
+// row statistics and the greedy argmax (at most 2K+1 rows of float32 chunks of 8 vectors per
+// thread), the contrastive pairs (K+1 rows of the smaller pair chunks) and the draw (one
+// workgroup per sequence)
+size_t largest_launch(int max_batch, int max_k, int max_vocab)
+{
+    const size_t k = (size_t)max_k;
+    const size_t stats = (2 * k + 1) * (size_t)sv::num_chunks(sv::NV_STATS, 0, max_vocab);
+    const size_t pairs = (k + 1) * (size_t)sv::max_chunks(max_vocab);
+    const size_t per_seq = std::max(std::max(stats, pairs) * sv::WG, (size_t)sv::TAIL_WG);
+    return (size_t)max_batch * per_seq;
+}
+
 // event pair array for the next call when timing is on, NULL otherwise
 hipEvent_t *next_events(specverify_ctx *ctx)
 {
@@ -146,7 +162,7 @@ extern "C" {
 int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k, int max_vocab)
 {
     if (!out || max_batch < 1 || max_k < 0 || max_k > SPECVERIFY_MAX_K || max_vocab < 1 ||
-        max_vocab > SPECVERIFY_MAX_VOCAB)
+        max_vocab > SPECVERIFY_MAX_VOCAB || largest_launch(max_batch, max_k, max_vocab) > MAX_ITEMS)
         return SPECVERIFY_EINVAL;
     *out = nullptr;
     int ndev = 0;
@@ -354,6 +370,8 @@ int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype
         return rc;
     if (H < 1)
         return SPECVERIFY_EINVAL;
+    if ((size_t)B * (size_t)(H > 1 ? H - 1 : 1) * sv::WG > MAX_ITEMS)
+        return SPECVERIFY_ECAPACITY;
     if (B == 0)
         return SPECVERIFY_OK;
     if (!logits || !accepted_len || !out_tokens || (K > 0 && !proposals) ||
@@ -382,7 +400,7 @@ int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N,
         return SPECVERIFY_EINVAL;
     if (P < 0 || N < 1 || !(alpha >= 0.0f && alpha <= 1.0f))
         return SPECVERIFY_EINVAL;
-    if (N > SPECVERIFY_MAX_CUT_N)
+    if (N > SPECVERIFY_MAX_CUT_N || (size_t)P * sv::TAIL_WG > MAX_ITEMS)
         return SPECVERIFY_ECAPACITY;
     if (P == 0)
         return SPECVERIFY_OK;

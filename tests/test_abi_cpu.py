@@ -71,6 +71,22 @@ def test_null_context_is_rejected_on_the_host():
     assert lib.specverify_create(ctypes.byref(h), 0, 1, 1, sv.SPECVERIFY_MAX_VOCAB + 1) == sv.SPECVERIFY_EINVAL
 
 
+def test_capacity_beyond_one_dispatch_is_rejected_on_the_host():
+    """A context whose largest launch would pass the 2^32 - 1 work-items of one dispatch is
+    refused before the device is touched.  At max_k = 63 and max_vocab = 128256 the contrastive
+    pairs (64 rows of 32 float32 chunks, 256 threads each) set the limit: max_batch 8191 fits,
+    8192 does not."""
+    lib = sv.load()
+    h = ctypes.c_void_p()
+    assert lib.specverify_create(ctypes.byref(h), 0, 8192, 63, 128256) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_create(ctypes.byref(h), 0, 1 << 30, 0, 1) == sv.SPECVERIFY_EINVAL
+    assert lib.specverify_create(ctypes.byref(h), 0, 1024, 63, sv.SPECVERIFY_MAX_VOCAB) == sv.SPECVERIFY_EINVAL
+    rc = lib.specverify_create(ctypes.byref(h), 0, 8191, 63, 128256)
+    assert rc != sv.SPECVERIFY_EINVAL       # EHIP without a device
+    if rc == sv.SPECVERIFY_OK:
+        lib.specverify_destroy(h)
+
+
 def test_binding_constants_match_the_header():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (SPECVERIFY_\w+) (.+)", text))

@@ -167,7 +167,11 @@ def test_heads_errors(ctx):
     E = sv.SpecVerifyError
     for args, want in [((F32, 2, 2, 0, 10, lg, x, acc, tok, nxt), sv.SPECVERIFY_EINVAL),
                        ((F32, 2, 2, 3, 10, lg, x, acc, tok, None), sv.SPECVERIFY_EINVAL),
-                       ((F32, 2, 17, 3, 10, lg, x, acc, tok, nxt), sv.SPECVERIFY_ECAPACITY)]:
+                       ((F32, 2, 17, 3, 10, lg, x, acc, tok, nxt), sv.SPECVERIFY_ECAPACITY),
+                       # B * (H - 1) workgroups of 256 threads would pass 2^32 - 1 work-items;
+                       # refused on the host before any launch
+                       ((F32, 2, 2, (1 << 23) + 1, 10, lg, x, acc, tok, nxt),
+                        sv.SPECVERIFY_ECAPACITY)]:
         with pytest.raises(E) as ei:
             sv.specverify_run_greedy_heads(ctx, None, *args)
         assert ei.value.status == want
@@ -220,7 +224,9 @@ def test_cut_errors(ctx):
                        ((2, 0, 0.5, s, cut, keep, n), sv.SPECVERIFY_EINVAL),
                        ((2, 8, 0.5, None, cut, keep, n), sv.SPECVERIFY_EINVAL),
                        ((2, sv.SPECVERIFY_MAX_CUT_N + 1, 0.5, s, cut, keep, n),
-                        sv.SPECVERIFY_ECAPACITY)]:
+                        sv.SPECVERIFY_ECAPACITY),
+                       # 2^22 prompts of one 1024-thread workgroup each: 2^32 work-items
+                       ((1 << 22, 8, 0.5, s, cut, keep, n), sv.SPECVERIFY_ECAPACITY)]:
         with pytest.raises(E) as ei:
             sv.specverify_quantile_cut(ctx, None, *args)
         assert ei.value.status == want
