@@ -78,6 +78,25 @@ def timing_stride(steps: int) -> int:
 METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf16"
 
 
+PREHEAT_SECONDS = 0.03  # untimed calls before the warm-up steps, by wall time
+
+
+def preheat(step, sync, seconds: float = PREHEAT_SECONDS) -> int:
+    """Untimed calls for about `seconds` of wall time, synchronising every 8 calls so that the
+    host does not run ahead of the GPU.  The GPU raises its clocks only after ~12 ms of
+    continuous work, whatever the call size; running this before the warm-up steps keeps a
+    short --warmup from leaving the first timed steps in that ramp.  Returns the calls made."""
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while True:
+        for _ in range(8):
+            step(n)
+            n += 1
+        sync()
+        if time.perf_counter() >= t_end:
+            return n
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -269,7 +288,7 @@ def oracle_check(w, gpu: dict, firsts: dict, early: bool = False) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed calls first: the GPU takes ~60 calls of this size (~12 ms) to reach "
                          "its steady clocks")
@@ -352,6 +371,7 @@ def main():
             sv.specverify_run_sampling(ctx, sh, w.dtype, B, K, V, w.temperature, tg, dr,
                                        p_toks, p_unif, p_acc, p_out, p_probs)
 
+    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize))
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
         step(i)
@@ -480,6 +500,7 @@ def bench_cut(args, desc, kind, kname):
     def step(i):
         sv.specverify_quantile_cut(ctx, sh, P, N, w.alpha, ps[i & 1], p_cut, p_keep, p_n)
 
+    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize))
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -55,6 +55,15 @@ def test_timing_stride_keeps_about_25_timed_launches():
     assert len(range(0, 2000, bench.timing_stride(2000))) == 25
 
 
+def test_preheat_runs_calls_for_its_time_and_syncs_every_8():
+    calls, syncs = [], []
+    n = bench.preheat(calls.append, lambda: syncs.append(len(calls)), seconds=0.01)
+    assert n == len(calls) >= 8 and n % 8 == 0
+    assert calls == list(range(n))
+    assert syncs == list(range(8, n + 1, 8))
+    assert bench.preheat(calls.append, lambda: None, seconds=0.0) == 8   # at least one round
+
+
 def test_percentiles_interpolate_like_numpy():
     xs = [5.0, 1.0, 4.0, 2.0, 3.0, 9.0, 7.0]
     got = bench.percentiles(xs)
