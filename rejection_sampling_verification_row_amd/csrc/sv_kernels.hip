@@ -15,7 +15,9 @@
 // k_pairs_prefix), k_alive lists the sequences not yet rejected there, k_stats_rest /
 // k_pairs_rest read only their remaining rows, and k_tail finishes as above.
 // A greedy blockwise call is k_argmax (chunk (max, first id)) and k_greedy_final, or
-// k_greedy_heads when the same pass also carries the next block's proposal heads.
+// k_greedy_heads when the same pass also carries the next block's proposal heads.  Its early
+// exit runs k_argmax_prefix over the first positions, k_alive_greedy, then k_argmax_rest over
+// the survivors' remaining rows before k_greedy_final.
 // The draft-token sampler runs k_stats_sampling and k_tail with no draft (K = 0, each row
 // its own sequence), and k_quantile_cut is a per-row radix select for an alpha-quantile of
 // reward scores.
@@ -437,7 +439,7 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
 // (ids >= V read as -inf bits): vectors wholly below V in an aligned row are one streamed
 // load each, the rest are packed element by element (element 2j in the low half of word j).
 // Holding the packed words instead of NV*8 floats keeps the sampling statistics kernel at 46
-// VGPRs, 8 waves per SIMD, and the contrastive one at 70 instead of 90.
+// VGPRs, 8 waves per SIMD, and the contrastive one at 69 instead of 90.
 __device__ inline uint4 pack_bf16(const char *rp, int e0, int V)
 {
     const uint16_t *h = reinterpret_cast<const uint16_t *>(rp);
@@ -733,7 +735,7 @@ __device__ __forceinline__ void pair_chunk_stats(const char *ex, const char *am,
     float xd[NV_PAIR][E], xa[NV_PAIR][E];
     if constexpr (E == 8) {
         // bfloat16: both rows as packed words first (one load path for every case), then
-        // unpacked: 70 VGPRs instead of 90 (7 waves per SIMD instead of 5), 1 us faster per
+        // unpacked: 69 VGPRs instead of 90 (7 waves per SIMD instead of 5), 1 us faster per
         // launch at B=128, K=4, V=152064, with the same values
         uint4 we[NV_PAIR], wa[NV_PAIR];
         load_chunk_words<DT, NV_PAIR>(re, al, cbase, V, we);
@@ -786,9 +788,9 @@ __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict
 struct DrawRows {
     const char *p0;   // target row L (sampling) or expert row L (contrastive)
     const char *p1;   // draft row L (sampling, L < K only) or amateur row L (contrastive)
-    // the same rows as buffer resources over their V * BYTES bytes, for the row pass: its
-    // loads then take one per-thread offset register and a per-load scalar offset instead of
-    // a 64-bit address each (reads past the end of the row return zeros)
+    // the same rows as buffer resources over their V * BYTES bytes, for the row pass: each of
+    // its loads then takes one 32-bit byte offset register instead of a 64-bit address (reads
+    // past the end of the row return zeros)
     __amdgpu_buffer_rsrc_t b0, b1;
     bool two;         // p1 is read
     bool resid;       // L < K: w = max(0, p - q); else w = p
