@@ -256,6 +256,19 @@ def test_null_out_probs(ctx):
     assert np.array_equal(a.out_tokens, b.out_tokens)
 
 
+def test_capacity_at_the_one_dispatch_limit_is_accepted():
+    """The largest capacity whose launches fit one dispatch (max_batch 8191 at max_k 63 and
+    max_vocab 128256) creates a context (about 1 GB of workspace); one more sequence does not."""
+    h = sv.specverify_create(0, 8191, 63, 128256)
+    try:
+        assert sv.specverify_workspace_bytes(h) > 8191 * 127 * 32 * 4 * 8
+    finally:
+        sv.specverify_destroy(h)
+    with pytest.raises(sv.SpecVerifyError) as ei:
+        sv.specverify_create(0, 8192, 63, 128256)
+    assert ei.value.status == sv.SPECVERIFY_EINVAL
+
+
 def test_host_side_errors(ctx):
     w = synth.c1_sampling_tiny(B=2, seed=3)
     t, d, x, u = dev(w.target), dev(w.draft), dev(w.tokens), dev(w.uniforms)
