@@ -10,9 +10,10 @@ step reads logits the previous one left in the 256 MB last-level cache.
 
 Prints one JSON line: verified draft positions/s (B*K per step), the dominant kernel's
 bytes/s against the 8 TB/s HBM peak (HIP events attached to that kernel's dispatch on the
-call's stream, in every 8th step of the timed loop), the fp64 CPU oracle timed on a bounded
-sample of the same batch (on one thread, then on all host threads up to 16), and a check of
-the GPU's outputs for the whole batch against that oracle run.
+call's stream, in about 25 steps spread over the timed loop: every 40th of the default 1000),
+the fp64 CPU oracle timed on a bounded sample of the same batch (on one thread, then on all
+host threads up to 16), and a check of the GPU's outputs for the whole batch against that
+oracle run.
 
 --workload names one of the other synthetic workloads (the tiny and mid-size sampling ones,
 greedy blockwise, contrastive, and the operations next to the verify step: the draft-token
