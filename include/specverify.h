@@ -110,8 +110,10 @@ int64_t specverify_workspace_bytes(const specverify_ctx *ctx);
  *  Outputs: accepted_len [B] int32 (L, or -1 for bad ids), out_tokens [B][K+1] int32
  *  (x_0..x_{L-1}, the drawn token, then -1), out_probs [B][K][2] float
  *  (p_j(x_j), q_j(x_j) for every j < K) or NULL.
- *  Arithmetic: fp32 row statistics from one read of every logit, fp64 combination,
- *  decisions and residual prefix sums.
+ *  Arithmetic: fp32 row statistics from one read of every logit, fp64 combination and
+ *  decisions.  The residual draw is computed in fp64 from the logits of row L (per-id terms
+ *  and both normalising sums), so that its cumulative weights over W carry an fp64 error
+ *  however small the residual mass W is.
  */
 int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,
                             int V, float temperature, const void *target_logits,
@@ -225,6 +227,22 @@ int specverify_run_greedy_heads(specverify_ctx *ctx, void *hip_stream, int dtype
  */
 int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N, float alpha,
                             const float *scores, float *r_cut, uint8_t *keep, int32_t *n_keep);
+
+/*
+ * Test hook: flags that force draw paths which data rarely reaches, so that tests can compare
+ * them with a reference.  Normal callers never set them (a new context has 0).
+ *   SPECVERIFY_TEST_CHUNK_FALLBACK  a draw from p_L alone (the bonus draw, the sampler) skips
+ *                                   the one-chunk draw and weighs the whole row (the path taken
+ *                                   when rounding leaves the chosen chunk without weight)
+ *   SPECVERIFY_TEST_EXACT_TWO_PASS  the fp64 residual draw always runs its exact second pass
+ *                                   (taken when an id lies too close to the residual's edge
+ *                                   for the first pass to place it)
+ * Every flag leaves the outputs within the same parity with the definitions above.  Applies to
+ * the calls that follow on this context.  Errors: EINVAL (NULL ctx, unknown bits).
+ */
+#define SPECVERIFY_TEST_CHUNK_FALLBACK 1u
+#define SPECVERIFY_TEST_EXACT_TWO_PASS 2u
+int specverify_set_test_flags(specverify_ctx *ctx, unsigned flags);
 
 /* Release the context and its workspace.  NULL-safe; returns SPECVERIFY_OK. */
 int specverify_destroy(specverify_ctx *ctx);

@@ -28,6 +28,8 @@ SPECVERIFY_MAX_K = 63
 SPECVERIFY_MAX_VOCAB = 1 << 20
 SPECVERIFY_MAX_CUT_N = 8192
 SPECVERIFY_NUM_KERNELS = 7
+SPECVERIFY_TEST_CHUNK_FALLBACK = 1
+SPECVERIFY_TEST_EXACT_TWO_PASS = 2
 KERNEL_NAMES = ("row_stats", "accept_draw", "row_argmax", "greedy_emit", "quantile_cut",
                 "early_accept", "early_rest_stats")
 
@@ -78,6 +80,8 @@ def load():
         lib.specverify_run_greedy_heads.restype = i
         lib.specverify_quantile_cut.argtypes = [vp, vp, i, i, f, vp, vp, vp, vp]
         lib.specverify_quantile_cut.restype = i
+        lib.specverify_set_test_flags.argtypes = [vp, ctypes.c_uint]
+        lib.specverify_set_test_flags.restype = i
         lib.specverify_destroy.argtypes = [vp]
         lib.specverify_destroy.restype = i
         lib.specverify_strerror.argtypes = [i]
@@ -206,6 +210,11 @@ def specverify_quantile_cut(ctx, stream, P, N, alpha, scores, r_cut, keep, n_kee
     _check(load().specverify_quantile_cut(
         ctx, _stream(stream), P, N, float(alpha), _ptr(scores), _ptr(r_cut), _ptr(keep),
         _ptr(n_keep)), "specverify_quantile_cut")
+
+
+def specverify_set_test_flags(ctx, flags: int) -> None:
+    """Test hook: SPECVERIFY_TEST_* bits forcing rarely reached draw paths (0 = normal)."""
+    _check(load().specverify_set_test_flags(ctx, int(flags)), "specverify_set_test_flags")
 
 
 def specverify_destroy(ctx) -> None:

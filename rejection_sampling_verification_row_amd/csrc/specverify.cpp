@@ -35,6 +35,9 @@ constexpr int NK = SPECVERIFY_NUM_KERNELS;
 static_assert(NK == sv::NUM_KINDS, "kernel kinds out of step with the header");
 static_assert(SPECVERIFY_MAX_CUT_N == sv::MAX_CUT_N, "cut capacity out of step with the header");
 static_assert(SPECVERIFY_MAX_VOCAB == sv::MAX_VOCAB, "vocabulary cap out of step with the header");
+static_assert(SPECVERIFY_TEST_CHUNK_FALLBACK == sv::TEST_CHUNK_FALLBACK &&
+                  SPECVERIFY_TEST_EXACT_TWO_PASS == sv::TEST_EXACT_TWO_PASS,
+              "test flags out of step with the header");
 
 struct DeviceGuard {
     int prev = -1;
@@ -180,7 +183,11 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
         return SPECVERIFY_EHIP;
     // a sequence's draw is shared by several workgroups only when B <= cus / 2
     const int split_batch = std::min(max_batch, cus / 2);
-    const int nu_stride = std::max(sv::tail_units(0, max_vocab), sv::tail_units(1, max_vocab));
+    // per sequence of a shared draw: the fp64 pass's two sums per unit and three totals per
+    // workgroup
+    const int nu_stride =
+        2 * std::max(sv::exact_units(0, max_vocab), sv::exact_units(1, max_vocab)) +
+        3 * sv::TAIL_MAX_SPLIT;
     const size_t b_part = align_up(rows * nch * sv::WAVES * sizeof(float2));
     const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
     const size_t b_gu = align_up((size_t)split_batch * nu_stride * sizeof(double));
@@ -204,6 +211,7 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     ctx->ws.split_batch = split_batch;
     ctx->ws.nu_stride = nu_stride;
     ctx->ws.num_cus = cus;
+    ctx->ws.test_flags = 0;
     // the arrival counts start at 0; every call leaves them at 0
     if (split_batch > 0 &&
         (hipMemset(ctx->ws.gcount, 0, (size_t)split_batch * sizeof(int)) != hipSuccess ||
@@ -420,6 +428,14 @@ int specverify_quantile_cut(specverify_ctx *ctx, void *hip_stream, int P, int N,
     hipError_t e = sv::launch_quantile_cut(ln, P, N, (int)k, scores, r_cut, keep, n_keep);
     note_call(ctx, ev, 1u << sv::KIND_CUT);
     return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
+}
+
+int specverify_set_test_flags(specverify_ctx *ctx, unsigned flags)
+{
+    if (!ctx || (flags & ~(unsigned)sv::TEST_FLAGS_ALL) != 0)
+        return SPECVERIFY_EINVAL;
+    ctx->ws.test_flags = flags;
+    return SPECVERIFY_OK;
 }
 
 int specverify_destroy(specverify_ctx *ctx)

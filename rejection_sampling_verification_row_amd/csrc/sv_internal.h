@@ -35,6 +35,18 @@ constexpr int EARLY_PREFIX_GREEDY = 3; // the same for greedy verify (B=512 K=8 
                                       // matching w.p. 0.7: 39.1 us against 41.2 with 2 and 39.5 with 4)
 constexpr int TAIL_MAX_SPLIT = 8;     // most workgroups that share one sequence's draw
 
+// The residual draw (L < K) is made in fp64 from the logits of row L (see exact_pass in the
+// kernels), in iterations of TAIL_WG * NV_EXACT vectors per row laid out as the fp32 row pass's;
+// its unit is one wave's vector slot, 64 * EPV contiguous ids, with two fp64 sums per unit.
+constexpr int NV_EXACT = 2;
+
+// test-only switches (specverify_set_test_flags): reach draw paths that data rarely reaches
+enum TestFlag : unsigned {
+    TEST_CHUNK_FALLBACK = 1u,   // a draw from p_L alone skips the chunk draw: whole-row pass
+    TEST_EXACT_TWO_PASS = 2u,   // the fp64 residual pass always runs its exact second pass
+    TEST_FLAGS_ALL = 3u
+};
+
 inline int elems_per_vec(int dtype) { return dtype == 1 ? 8 : 4; }
 inline int chunk_elems(int nv, int dtype) { return WG * nv * elems_per_vec(dtype); }
 inline int num_chunks(int nv, int dtype, int V)
@@ -55,13 +67,22 @@ inline int tail_units(int dtype, int V)
     }
     return most;
 }
-// dynamic LDS of the tail kernel: the staged partials, then (reusing it) the unit sums
+// units of the fp64 residual pass: one per wave and vector slot of each iteration
+inline int exact_units(int dtype, int V)
+{
+    const int ce = TAIL_WG * NV_EXACT * elems_per_vec(dtype);
+    return (V + ce - 1) / ce * NV_EXACT * TAIL_WAVES;
+}
+// dynamic LDS of the tail kernel: the staged partials, then (reusing it) the unit sums of the
+// fp32 pass of a draw from p_L, or the two fp64 sums per unit of the residual pass
 inline size_t tail_lds_bytes(int dtype, int K, int V, int nch)
 {
     const size_t parts = (size_t)(2 * K + 1) * nch * WAVES;
     const size_t stage = parts <= (size_t)ACCEPT_STAGE ? parts * 8 : 0;
     const size_t units = (size_t)tail_units(dtype, V) * 8;
-    return stage > units ? stage : units;
+    const size_t exact = (size_t)exact_units(dtype, V) * 16;
+    size_t m = stage > units ? stage : units;
+    return m > exact ? m : exact;
 }
 
 // log2(e) / T split into two floats so that d * hi + d * lo carries ~48 bits of the
@@ -82,8 +103,8 @@ struct SeqInfo {
     int L;           // first rejected position, K if none, -1 for bad ids
     float Rp, Rq;
     float isp, isq;
-    float Mp;        // maximum and sum of the target row L, for the drawn id's probability
-    double Sp;
+    float Mp, Mq;    // maximum and merged sum (fp64) of the target row L and the draft row L
+    double Sp, Sq;
 };
 
 enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };
@@ -93,11 +114,13 @@ struct Workspace {
     int *alive;         // [B] early exit: 1 if the sequence accepted its first positions
     int *list;          // [B] early exit: the alive sequences, in no particular order
     int *count;         // early exit: the number of alive sequences
-    double *gunits;     // [split_batch][nu_stride] unit sums of a draw shared by workgroups
+    double *gunits;     // [split_batch][nu_stride] fp64 unit sums and per-workgroup totals of a
+                        // residual draw shared by workgroups
     int *gcount;        // [split_batch] arrival counts of those workgroups, 0 between calls
     int split_batch;    // largest batch whose draws may be shared (0: never)
-    int nu_stride;      // unit sums per sequence in gunits
+    int nu_stride;      // doubles per sequence in gunits
     int num_cus;        // compute units of the device
+    unsigned test_flags; // TestFlag bits (0 in normal use)
 };
 
 struct Launch {

@@ -666,6 +666,8 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         si.isp = (float)(exp2(-(double)ep) / sS[L]);
         if (L < K) {
             const float Mq = sM[K + 1 + L];
+            si.Mq = Mq;
+            si.Sq = sS[K + 1 + L];
             si.Rq = Mq * sq.hi;
             const float eq = __builtin_fmaf(Mq, sq.lo, __builtin_fmaf(Mq, sq.hi, -si.Rq));
             si.isq = (float)(exp2(-(double)eq) / sS[K + 1 + L]);
@@ -1001,9 +1003,9 @@ __device__ __forceinline__ void tail_unit_sums(const DrawRows &r, int V, int nit
 // weighs 0.  Thread t owns the units [t*U, t*U + U): it sums them in order, a wave scan and a
 // scan of the 16 wave totals (the same order in every thread, so every thread holds the same
 // W) give each thread's starting total, and each thread tests its own units.  The unit, its
-// starting total, tt and fb go to LDS, readable after the next barrier.
+// starting total, tt, fb and W go to LDS, readable after the next barrier.
 __device__ inline void find_unit_block(const double *units, int nu, float u01, int *s_unit,
-                                       double *s_base, double *s_t, int *s_fb)
+                                       double *s_base, double *s_t, int *s_fb, double *s_W)
 {
     __shared__ double sw[TAIL_WAVES], shb[TAIL_WAVES], slb[TAIL_WAVES];
     __shared__ int sh[TAIL_WAVES], sl[TAIL_WAVES];
@@ -1070,8 +1072,16 @@ __device__ inline void find_unit_block(const double *units, int nu, float u01, i
             *s_base = hmk ? bh : (lmk ? bl : 0.0);
             *s_t = tt;
             *s_fb = hmk ? 0 : 1;
+            *s_W = W;
         }
     }
+}
+
+// p(x) = exp((x - M) / T) / S in fp64, the drawn id's probability.  Out of line: its fp64 exp
+// would otherwise keep constants in registers across the whole row pass of k_tail.
+__device__ __noinline__ float drawn_prob(float x, float M, double inv_t, double S)
+{
+    return (float)(exp(((double)x - (double)M) * inv_t) / S);
 }
 
 // Inside unit `unit` (one wave): lane l weighs the unit's vector l with the instructions of
@@ -1129,9 +1139,502 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
     const int id = (y >= 0) ? y : lastpos;
     *out = id;
     if (MODE == SAMPLING && out_prob)  // p_L(id) in fp64 from the row's merged statistics
-        *out_prob = (float)(exp(((double)Elt<DT>::one(r.p0, (size_t)id) - (double)si.Mp) *
-                                sp.inv_t) /
-                            si.Sp);
+        *out_prob = drawn_prob(Elt<DT>::one(r.p0, (size_t)id), si.Mp, sp.inv_t, si.Sp);
+}
+
+// ------------------------------------------------------------------ fp64 residual draw
+//
+// The residual draw compares cumulative weights of w = max(0, p - q) with t = u * W, W the
+// residual mass, so an error in the weights enters the decision as (error) / W.  fp32 weights
+// carry about 1e-7 of p each, and the fp32 row statistics put a common error of the same order
+// on every p (or q) of a row, which max(0, p - q) does not cancel; at W of 1e-3 that is far
+// above the 1e-6 decision margins.  So the residual draw is computed in fp64 from the logits of
+// row L: e_p(v) = 2^((z_p(v) - M_p) log2(e)/T_p) and e_q(v) = 2^((x_q(v) - M_q) log2(e)/T_q)
+// (z_p the target-side logit, or the expert-minus-amateur difference formed exactly in fp64),
+// and the normalising sums S_p = sum e_p, S_q = sum e_q recomputed in fp64 in the same pass.
+// Which side of the residual an id is on, e_p / S_p > e_q / S_q, is needed before the sums are
+// known, so the pass sorts ids with the statistics' approximate sums; each unit keeps A = sum e_p
+// and B = sum e_q over its ids on the positive side, and afterwards its weight is
+// A / S_p - B / S_q with the exact sums.  An id can be sorted differently by the approximate and
+// the exact sums only if its ratio of the two sides lies between theirs, so the error of the
+// unit weights is at most |theta~/theta - 1| times the draft mass of the ids whose sides agree
+// within that (theta the ratio of the sums); the pass sums the draft mass of the ids within
+// EXACT_NEAR, and when the bound is not far below the decision scale (2^-24 W) it is repeated
+// with the exact sums.
+//
+// For bfloat16 rows the fp64 exps come from LDS tables: a bfloat16 value is one of at most
+// 65536 bit patterns, and the 5120 with 2^-12 <= |x| < 2^8 (both signs) cover the logits of a
+// language model's head; each table holds 2^((x - M) c) for them, computed once per row with
+// fp64 exp2, and ids outside the table take fp64 exp2 directly.
+
+constexpr int TAB_E0 = 115;               // bfloat16 exponent field of 2^-12
+constexpr int TAB_NE = 20;                // fields 115..134: 2^-12 <= |x| < 2^8
+constexpr int TAB_HALF = TAB_NE * 128;    // tabulated values per sign
+// Each sign's block is [below, TAB_HALF values, above]: the two sentinel slots take the
+// magnitudes below and above the tabulated ones.  A slot is found with one clamp, no branch.
+constexpr int TAB_BLOCK = TAB_HALF + 2;
+constexpr int TAB_STRIDE = 2 * TAB_BLOCK; // doubles per table (41 KiB)
+constexpr double TAB_TINY = 0x1p-60;      // a term this far below the row's largest counts as 0
+
+// the slot of a bfloat16 bit pattern: the tabulated value, or a sentinel of its sign
+__device__ __forceinline__ int tab_slot(uint32_t b)
+{
+    const int t = (int)(b & 0x7fffu) - (TAB_E0 << 7);
+    const int c = min(max(t, -1), TAB_HALF);   // clamp to [-1, TAB_HALF] (one v_med3_i32)
+    return (int)((b >> 15) & 1u) * TAB_BLOCK + 1 + c;
+}
+
+// the bfloat16 value of tabulated slot k (a slot of neither sentinel)
+__device__ __forceinline__ double tab_value(int k)
+{
+    const int sign = k / TAB_BLOCK, j = k - sign * TAB_BLOCK - 1;
+    const uint32_t b = ((uint32_t)sign << 15) | (uint32_t)((TAB_E0 << 7) + j);
+    return (double)__uint_as_float(b << 16);
+}
+
+// fp64 exp2 for the ids outside the tables: out of line, so that its constants do not take
+// registers from the table path
+__device__ __noinline__ double exp2_cold(double a) { return exp2(a); }
+
+// What the fp64 pass needs about the two rows.
+struct ExactRows {
+    const char *p0, *p1;     // target (expert) row L, draft (amateur) row L
+    __amdgpu_buffer_rsrc_t b0, b1;  // the same rows as buffer resources (see DrawRows)
+    bool al;                 // both rows 16-byte aligned
+    float Mp, Mq;            // the rows' maxima from the statistics (the exps' reference points)
+    double cp, cq;           // log2(e) / T of each law
+    double kc;               // contrastive bfloat16: 2^(-M_p cp)
+    const double *tp, *tq, *tn;  // bfloat16 tables (LDS), see exact_tables
+};
+
+// The LDS tables of the two rows (bfloat16 only), by the whole workgroup.  Sampling: tp[k] =
+// 2^((x_k - M_p) cp), tq[k] = 2^((x_k - M_q) cq).  Contrastive: tq as sampling for the amateur
+// law, and for p = 2^((x_e - x_a - M_p) cp) = tp[k_e] * tn[k_a] * kc the factors tp[k] =
+// 2^(x_k cp) and tn[k] = 2^(-x_k cp), left NaN where |x_k cp| > 1000 (their product could leave
+// the fp64 range): such ids take exp2 directly.
+template <int MODE>
+__device__ inline void exact_tables(ExactRows &x, double *tab)
+{
+    double *tp = tab, *tq = tab + TAB_STRIDE, *tn = tab + 2 * TAB_STRIDE;
+    // Sentinels hold -0.0 (the id's term comes from exp2) or +0.0 (the term is taken as 0):
+    // below -2^8 (and -inf) the term is at most 2^((-2^8 - M) c), +0.0 when that is below
+    // TAB_TINY (sampling, and the amateur law of contrastive verify).
+    const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
+    const double neg_p = (exp2((-top - (double)x.Mp) * x.cp) <= TAB_TINY) ? 0.0 : -0.0;
+    const double neg_q = (exp2((-top - (double)x.Mq) * x.cq) <= TAB_TINY) ? 0.0 : -0.0;
+    for (int k = threadIdx.x; k < TAB_STRIDE; k += TAIL_WG) {
+        const int sign = k / TAB_BLOCK, j = k - sign * TAB_BLOCK;
+        if (j == 0 || j == TAB_BLOCK - 1) {
+            const bool neg_above = sign == 1 && j == TAB_BLOCK - 1;
+            tq[k] = neg_above ? neg_q : -0.0;
+            tp[k] = (MODE == SAMPLING && neg_above) ? neg_p : -0.0;
+            if (MODE == CONTRASTIVE)
+                tn[k] = -0.0;
+            continue;
+        }
+        const double v = tab_value(k);
+        tq[k] = exp2((v - (double)x.Mq) * x.cq);
+        if (MODE == SAMPLING) {
+            tp[k] = exp2((v - (double)x.Mp) * x.cp);
+        } else {
+            // factors 2^(v cp) and 2^(-v cp); exact_rows_tabled() keeps them in range
+            tp[k] = exp2(v * x.cp);
+            tn[k] = exp2(-v * x.cp);
+        }
+    }
+    x.tp = tp;
+    x.tq = tq;
+    x.tn = tn;
+    x.kc = exp2(-(double)x.Mp * x.cp);
+}
+
+// Whether the tables serve this row pair: always for sampling; for contrastive verify while the
+// factors 2^(+-x cp) of every tabulated x (|x| < 2^8) and their products stay far inside the
+// fp64 range (|x cp| <= 2^8 cp <= 1000), else every id takes exp2.
+template <int MODE> __device__ __forceinline__ bool exact_rows_tabled(const ExactRows &x)
+{
+    return MODE == SAMPLING || (double)(1 << (TAB_E0 + TAB_NE - 127)) * x.cp <= 1000.0;
+}
+
+// -0.0: a sentinel whose id takes exp2 (see exact_tables)
+__device__ __forceinline__ bool neg_zero(double v) { return __builtin_amdgcn_class(v, 0x20); }
+
+// One id's fp64 terms from the bfloat16 tables: returns false (with e_p, e_q of 0) if a value
+// lies outside them; such ids take direct_terms.
+template <int MODE>
+__device__ __forceinline__ bool table_terms(uint32_t bp, uint32_t bq, const ExactRows &x,
+                                            double &ep, double &eq)
+{
+    const int kp = tab_slot(bp), kq = tab_slot(bq);
+    const double q = x.tq[kq];
+    bool miss = neg_zero(q);
+    double p;
+    if constexpr (MODE == SAMPLING) {
+        p = x.tp[kp];
+        miss = miss | neg_zero(p);
+    } else {
+        const double f = x.tp[kp], g = x.tn[kq];
+        miss = miss | neg_zero(f) | neg_zero(g);
+        p = (f * g) * x.kc;
+    }
+    ep = miss ? 0.0 : p;
+    eq = miss ? 0.0 : q;
+    return !miss;
+}
+
+// One id's fp64 terms by exp2 from its target-side and draft-side values.
+template <int DT, int MODE>
+__device__ __forceinline__ void direct_terms(float pv, float qv, const ExactRows &x, double &ep,
+                                             double &eq)
+{
+    const double zp = (MODE == SAMPLING) ? (double)pv : (double)pv - (double)qv;
+    const double ap = (zp - (double)x.Mp) * x.cp, aq = ((double)qv - (double)x.Mq) * x.cq;
+    if constexpr (DT == 1) {
+        ep = exp2_cold(ap);
+        eq = exp2_cold(aq);
+    } else {
+        ep = exp2(ap);
+        eq = exp2(aq);
+    }
+}
+
+// One id's fp64 terms e_p, e_q: from the tables (bfloat16) where they hold its values, else by
+// exp2.  The pass and the search compute every id's terms with these same instructions.
+template <int DT, int MODE>
+__device__ __forceinline__ void exact_terms(float pv, float qv, uint32_t bp, uint32_t bq,
+                                            const ExactRows &x, double &ep, double &eq)
+{
+    if constexpr (DT == 1) {
+        if (exact_rows_tabled<MODE>(x) && table_terms<MODE>(bp, bq, x, ep, eq))
+            return;
+    }
+    direct_terms<DT, MODE>(pv, qv, x, ep, eq);
+}
+
+// NV_EXACT consecutive vectors of a row from id e0 as raw 16-byte words (bfloat16: two ids per
+// 32-bit word, the lower id in the low half): whole vectors of an aligned row as 16-byte loads,
+// the rest (and every vector of an unaligned row) element by element; words of ids >= V are
+// filled with anything and never used
+template <int DT>
+__device__ __forceinline__ void exact_load(const char *row, bool al, int e0, int V,
+                                           uint4 (&raw)[NV_EXACT])
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+#pragma unroll
+    for (int i = 0; i < NV_EXACT; ++i) {
+        const int v0 = e0 + i * E;
+        if (al && v0 + E <= V) {
+            raw[i] = load_plain(row + (size_t)v0 * BY);
+        } else if constexpr (E == 8) {
+            raw[i] = pack_bf16(row, v0, V);
+        } else {
+            uint32_t wd[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                wd[k] = (v0 + k < V) ? __float_as_uint(Elt<DT>::one(row, (size_t)(v0 + k))) : 0u;
+            raw[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        }
+    }
+}
+
+// 32-bit word q (0..3) of a 16-byte vector
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int q)
+{
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
+// id h of a word: its float value and (bfloat16) its 16-bit pattern
+template <int DT>
+__device__ __forceinline__ float word_value(uint32_t wd, int h, uint32_t &bits)
+{
+    if constexpr (Elt<DT>::EPV == 8) {
+        bits = h ? (wd >> 16) : (wd & 0xffffu);
+        return __uint_as_float(bits << 16);
+    } else {
+        bits = 0;
+        return __uint_as_float(wd);
+    }
+}
+
+// The side test of the fp64 pass: id v is on the residual's positive side when
+// e_p(v) cp_r > e_q(v) cq_r, with cp_r, cq_r the reciprocal sums it sorts with (the statistics'
+// approximate ones, or in a second pass the exact ones).  An id whose two sides agree within
+// EXACT_NEAR (|x - y| <= EXACT_NEAR y) may be sorted differently by the exact sums; its draft
+// mass e_q is summed so that the error of such ids can be bounded once the exact sums are known.
+constexpr double EXACT_NEAR = 1.0 / 65536.0;
+
+// What one thread accumulates in the fp64 pass: per vector slot (unit) the sums A, B of e_p and
+// e_q over its ids on the positive side; over all its ids the sums of e_p, e_q, and the draft
+// mass of the ids near the threshold.
+struct ExactAcc {
+    double a[NV_EXACT], b[NV_EXACT];
+    double tp, tq, near;
+};
+
+__device__ __forceinline__ void exact_add(ExactAcc &acc, int i, double ep, double eq, double cp_r,
+                                          double cq_r)
+{
+    const double xp = ep * cp_r, yq = eq * cq_r;
+    const double m = xp > yq ? 1.0 : 0.0;
+    const double nr = fabs(xp - yq) <= EXACT_NEAR * yq ? 1.0 : 0.0;
+    acc.a[i] = __builtin_fma(ep, m, acc.a[i]);
+    acc.b[i] = __builtin_fma(eq, m, acc.b[i]);
+    acc.near = __builtin_fma(eq, nr, acc.near);
+    acc.tp += ep;
+    acc.tq += eq;
+}
+
+// Vector i of this thread in iteration it: ids it * CE + (i * TAIL_WG + t) * E + [0, E), the
+// fp32 row pass's layout (a wave's loads 1 KiB contiguous), loaded nontemporally through the
+// rows' buffer resources (past V they read zeros, which the caller never uses).
+template <int DT>
+__device__ __forceinline__ void exact_fetch(const ExactRows &x, int it, uint4 (&rp)[NV_EXACT],
+                                            uint4 (&rq)[NV_EXACT])
+{
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, CE = TAIL_WG * NV_EXACT * E;
+    const int vo = (it * CE + (int)threadIdx.x * E) * BY;
+#pragma unroll
+    for (int i = 0; i < NV_EXACT; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(x.b0, vo + i * TAIL_WG * E * BY, 0, 2);
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(x.b1, vo + i * TAIL_WG * E * BY, 0, 2);
+        rp[i] = make_uint4(v.x, v.y, v.z, v.w);
+        rq[i] = make_uint4(u.x, u.y, u.z, u.w);
+    }
+}
+
+// One fp64 pass over iterations first, first + step, ... of row L and the draft row L.  Unit
+// u = (it * NV_EXACT + i) * TAIL_WAVES + w (wave w's vector slot i of iteration it, 64 * EPV
+// contiguous ids; unit order is id order) gets units[2u] = A, units[2u+1] = B; acc holds this
+// thread's totals.  Whole vectors of bfloat16 rows whose tables serve are formed without
+// branches (every table lookup of the vector, then the arithmetic; an id outside the tables reads
+// a -0.0 sentinel and adds nothing there, and a loop that a lane enters only if it holds such an
+// id adds it by exp2); float32 rows, unaligned rows and the vectors at the end of the row go id
+// by id.  The next iteration's rows are loaded while this one is weighed.
+template <int DT, int MODE>
+__device__ inline void exact_pass(const ExactRows &x, int V, int first, int step, double cp_r,
+                                  double cq_r, double *units, ExactAcc &acc)
+{
+    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_EXACT * E;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int nit = (V + CE - 1) / CE;
+    const bool tabled = (DT == 1) && exact_rows_tabled<MODE>(x);
+    acc.tp = acc.tq = acc.near = 0.0;
+    uint4 rp[NV_EXACT], rq[NV_EXACT], np[NV_EXACT], nq[NV_EXACT];
+    if (first < nit && x.al)
+        exact_fetch<DT>(x, first, rp, rq);
+    for (int it = first; it < nit; it += step) {
+        if (it + step < nit && x.al)  // the next iteration's words, in flight meanwhile
+            exact_fetch<DT>(x, it + step, np, nq);
+#pragma unroll
+        for (int i = 0; i < NV_EXACT; ++i) {
+            acc.a[i] = 0.0;
+            acc.b[i] = 0.0;
+        }
+        bool miss = false;
+        const int last0 = it * CE + ((NV_EXACT - 1) * TAIL_WG + t) * E;  // this thread's last vector
+        if (tabled && x.al && last0 + E <= V) {
+            if constexpr (DT == 1) {
+#pragma unroll
+                for (int i = 0; i < NV_EXACT; ++i) {
+                    const uint32_t wpv[4] = {rp[i].x, rp[i].y, rp[i].z, rp[i].w};
+                    const uint32_t wqv[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
+                    double pv[8], qv[8];
+                    bool mk[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t bp = (k & 1) ? (wpv[k >> 1] >> 16) : (wpv[k >> 1] & 0xffffu);
+                        const uint32_t bq = (k & 1) ? (wqv[k >> 1] >> 16) : (wqv[k >> 1] & 0xffffu);
+                        const int kp = tab_slot(bp), kq = tab_slot(bq);
+                        qv[k] = x.tq[kq];
+                        if constexpr (MODE == SAMPLING) {
+                            pv[k] = x.tp[kp];
+                            mk[k] = false;
+                        } else {
+                            const double f = x.tp[kp], g = x.tn[kq];
+                            mk[k] = neg_zero(f) | neg_zero(g);
+                            pv[k] = (f * g) * x.kc;
+                        }
+                    }
+                    // an id with a value outside the tables adds nothing here: the loop below
+                    // adds both its terms
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        mk[k] = mk[k] | neg_zero(qv[k]);
+                        if constexpr (MODE == SAMPLING)
+                            mk[k] = mk[k] | neg_zero(pv[k]);
+                        miss = miss | mk[k];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        exact_add(acc, i, mk[k] ? 0.0 : pv[k], mk[k] ? 0.0 : qv[k], cp_r, cq_r);
+                }
+            }
+        } else {
+            // id by id (float32 unrolled, as its word index would otherwise come from memory)
+            constexpr int KU = (E == 4) ? 4 : 1;
+#pragma unroll
+            for (int i = 0; i < NV_EXACT; ++i) {
+                const int v0 = it * CE + (i * TAIL_WG + t) * E;
+                uint4 wp4, wq4;
+                if (x.al) {
+                    wp4 = rp[i];
+                    wq4 = rq[i];
+                } else {  // an unaligned row: element by element
+                    uint4 tmp[NV_EXACT];
+                    exact_load<DT>(x.p0, false, v0, V, tmp);
+                    wp4 = tmp[0];
+                    exact_load<DT>(x.p1, false, v0, V, tmp);
+                    wq4 = tmp[0];
+                }
+#pragma unroll KU
+                for (int k = 0; k < E; ++k) {
+                    const int id = v0 + k;
+                    const uint32_t wp = word_of(wp4, (E == 8) ? (k >> 1) : k);
+                    const uint32_t wq = word_of(wq4, (E == 8) ? (k >> 1) : k);
+                    uint32_t bp, bq;
+                    const float pv = word_value<DT>(wp, (E == 8) ? (k & 1) : 0, bp);
+                    const float qv = word_value<DT>(wq, (E == 8) ? (k & 1) : 0, bq);
+                    double ep = 0.0, eq = 0.0;
+                    if (id < V)
+                        exact_terms<DT, MODE>(pv, qv, bp, bq, x, ep, eq);
+                    exact_add(acc, i, ep, eq, cp_r, cq_r);
+                }
+            }
+        }
+        if constexpr (DT == 1) {
+            if (miss) {  // ids outside the tables (values near 0 or beyond 2^8): rare
+#pragma unroll
+                for (int i = 0; i < NV_EXACT; ++i)
+#pragma unroll 1
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t wp = word_of(rp[i], k >> 1), wq = word_of(rq[i], k >> 1);
+                        const uint32_t bp = (k & 1) ? (wp >> 16) : (wp & 0xffffu);
+                        const uint32_t bq = (k & 1) ? (wq >> 16) : (wq & 0xffffu);
+                        double ep, eq;
+                        if (!table_terms<MODE>(bp, bq, x, ep, eq)) {
+                            direct_terms<DT, MODE>(__uint_as_float(bp << 16),
+                                                   __uint_as_float(bq << 16), x, ep, eq);
+                            exact_add(acc, i, ep, eq, cp_r, cq_r);
+                        }
+                    }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV_EXACT; ++i) {
+            const double A = wave_sum_lds(acc.a[i]), B = wave_sum_lds(acc.b[i]);
+            if (lane == 0) {
+                const int u = (it * NV_EXACT + i) * TAIL_WAVES + w;
+                units[2 * u] = A;
+                units[2 * u + 1] = B;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NV_EXACT; ++i) {
+            rp[i] = np[i];
+            rq[i] = nq[i];
+        }
+    }
+}
+
+// the weight of one id in the fp64 draw: max(0, e_p / S_p - e_q / S_q) on the positive side of
+// the pass's side test, else 0
+template <int DT, int MODE>
+__device__ __forceinline__ double exact_weight(float pv, float qv, uint32_t bp, uint32_t bq,
+                                               const ExactRows &x, double cp_r, double cq_r,
+                                               double np_r, double nq_r)
+{
+    double ep, eq;
+    exact_terms<DT, MODE>(pv, qv, bp, bq, x, ep, eq);
+    if (!(ep * cp_r > eq * cq_r))
+        return 0.0;
+    const double d = ep * np_r - eq * nq_r;
+    return d > 0.0 ? d : 0.0;
+}
+
+// Wave 0 inside unit `unit` of the fp64 pass: lane l weighs the unit's vector l (exact_weight,
+// with the side test of the pass that produced the unit sums), a wave scan from `base` finds the
+// lane, and the lane walks its ids again with the same instructions: the first id whose running
+// weight exceeds tt (fb: the last id of positive weight).
+template <int DT, int MODE>
+__device__ inline void exact_search(const ExactRows &x, int V, double cp_r, double cq_r,
+                                    double np_r, double nq_r, int unit, double base, double tt,
+                                    bool fb, int32_t *out)
+{
+    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_EXACT * E;
+    const int lane = threadIdx.x & 63;
+    const int it = unit / (NV_EXACT * TAIL_WAVES), rem = unit - it * (NV_EXACT * TAIL_WAVES);
+    const int i = rem / TAIL_WAVES, ww = rem - i * TAIL_WAVES;
+    const int e0 = it * CE + i * TAIL_WG * E + (ww * 64 + lane) * E;
+    uint4 rp[NV_EXACT], rq[NV_EXACT];
+    exact_load<DT>(x.p0, x.al, e0, V, rp);
+    exact_load<DT>(x.p1, x.al, e0, V, rq);
+    double wv[E];
+    double vs = 0.0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const uint32_t wp = word_of(rp[0], (E == 8) ? (k >> 1) : k);
+        const uint32_t wq = word_of(rq[0], (E == 8) ? (k >> 1) : k);
+        uint32_t bp, bq;
+        const float pv = word_value<DT>(wp, (E == 8) ? (k & 1) : 0, bp);
+        const float qv = word_value<DT>(wq, (E == 8) ? (k & 1) : 0, bq);
+        wv[k] = (e0 + k < V) ? exact_weight<DT, MODE>(pv, qv, bp, bq, x, cp_r, cq_r, np_r, nq_r)
+                             : 0.0;
+        vs += wv[k];
+    }
+    const double inc = wave_incl_scan(vs);
+    const double exc = wave_excl_from_incl(inc);
+    const double bt = base + exc;
+    const unsigned long long hit = __ballot(!fb && vs > 0.0 && bt + vs > tt);
+    const unsigned long long pos = __ballot(vs > 0.0);
+    if (pos == 0) {  // a unit of positive weight has an id of positive weight: not reached
+        if (lane == 0)
+            *out = -1;
+        return;
+    }
+    const bool fb2 = fb || hit == 0;
+    const int owner = fb2 ? 63 - __builtin_clzll(pos) : __builtin_ctzll(hit);
+    if (lane != owner)
+        return;
+    double run = bt;
+    int y = -1, lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        if (wv[k] > 0.0) {
+            run += wv[k];
+            lastpos = e0 + k;
+            if (!fb2 && y < 0 && run > tt)
+                y = e0 + k;
+        }
+    }
+    *out = (y >= 0) ? y : lastpos;
+}
+
+// The block's sums of three per-thread values, in a fixed order (wave sums, then the waves in
+// order), into s_out[0..2] after the next barrier.
+__device__ inline void block_sum3(double a, double b, double c, double *s_out)
+{
+    __shared__ double s_red[3][TAIL_WAVES];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    a = wave_sum_lds(a);
+    b = wave_sum_lds(b);
+    c = wave_sum_lds(c);
+    if (lane == 0) {
+        s_red[0][w] = a;
+        s_red[1][w] = b;
+        s_red[2][w] = c;
+    }
+    __syncthreads();
+    if (t == 0) {
+        double x = 0.0, y = 0.0, z = 0.0;
+        for (int v = 0; v < TAIL_WAVES; ++v) {
+            x += s_red[0][v];
+            y += s_red[1][v];
+            z += s_red[2][v];
+        }
+        s_out[0] = x;
+        s_out[1] = y;
+        s_out[2] = z;
+    }
 }
 
 // Arguments of k_tail.
@@ -1148,6 +1651,7 @@ struct TailArgs {
     int *gcount;        // split > 1: [B] workgroups done with their share; 0 between calls
     Scale sp, sq;
     int K, V, nch, prefix, mask_probs, split, nu_stride;
+    unsigned flags;     // TestFlag bits
 };
 
 // The draw when its weights are the target law p_L alone (the bonus draw at L = K, which is
@@ -1251,23 +1755,59 @@ __device__ __forceinline__ bool chunk_draw(const TailArgs &a, const DrawRows &r,
     return s_u >= 0;
 }
 
+// The draw from p_L over the whole row L by one workgroup (the fp32 row pass with the target law):
+// after a one-chunk draw that found no weight, or when the residual is empty in fp64 as well.
+// Writes -1 (and a NaN probability) for a row without finite logits.
+template <int DT, int MODE>
+__device__ inline void target_law_draw(const DrawRows &r, const SeqInfo &si, int V, float u01,
+                                       const Scale &sp, const Scale &sq, double *units,
+                                       int32_t *out, float *out_prob)
+{
+    __shared__ int s_unit, s_fb;
+    __shared__ double s_base, s_t, s_W;
+    constexpr int E = Elt<DT>::EPV;
+    // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
+    const bool two = (MODE == CONTRASTIVE) || r.two;
+    const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
+    const int nit = (V + ce - 1) / ce, nu = nit * nv * TAIL_WAVES;
+    if (two)
+        tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, 0, 1, true, si, sp, sq, units);
+    else if constexpr (MODE == SAMPLING)
+        tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, 0, 1, true, si, sp, sq, units);
+    __syncthreads();
+    find_unit_block(units, nu, u01, &s_unit, &s_base, &s_t, &s_fb, &s_W);
+    __syncthreads();
+    if (s_unit >= 0) {
+        if ((threadIdx.x >> 6) == 0)
+            search_unit<DT, MODE>(r, si, V, nv, s_unit, s_base, s_t, s_fb != 0, true, sp, sq, out,
+                                  out_prob);
+    } else if (threadIdx.x == 0) {  // a row without finite logits: outside the contract
+        *out = -1;
+        if (out_prob)
+            *out_prob = NAN;
+    }
+}
+
 // `split` workgroups of 1024 threads per sequence, after the row statistics.  Each runs the
 // accept phase (merge, gather, accept tests, L: the same decisions in every one; the first
-// writes the outputs), then weighs its share of the pass over row L (and the draft row L),
-// iterations g, g + split, ..., into unit sums in LDS.  With one workgroup it then finds the
-// unit holding t = u_K * W and the id inside it.  With several, each copies its unit sums to
-// the workspace (device-coherent stores, waited for) and counts itself in; the last to
-// arrive reads the others' sums (device-coherent loads), resets the count and draws.  If
-// rounding left the residual empty, that workgroup repeats the whole pass with the target law
-// p_L (essentially never taken).  Dynamic LDS: the staged partials during the accept phase,
-// the unit sums afterwards.
+// writes the outputs).  A draw from p_L alone (L = K, and the sampler) is made by the first
+// workgroup from one chunk of the row (chunk_draw).  A residual draw (L < K) runs the fp64 pass
+// over row L and the draft row L, iterations g, g + split, ..., into per-unit fp64 sums in LDS.
+// With one workgroup it then forms S_p, S_q and the unit weights, finds the unit holding
+// t = u_K * W and the id inside it.  With several, each copies its unit sums to the workspace
+// (device-coherent stores, waited for) and counts itself in; the last to arrive reads the
+// others' sums (device-coherent loads), resets the count and draws.  If the residual is empty
+// in fp64, that workgroup draws from p_L over the whole row.  LDS: the fp64 tables (bfloat16,
+// static); dynamic: the staged partials during the accept phase, the unit sums afterwards.
 template <int DT, int MODE, bool SPLIT>
 __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
 {
     extern __shared__ double dyn[];
+    constexpr int NTAB = (DT == 1) ? (MODE == CONTRASTIVE ? 3 : 2) * TAB_STRIDE : 1;
+    __shared__ double s_tab[NTAB];
     __shared__ SeqInfo s_info;
     __shared__ int s_unit, s_fb, s_last;
-    __shared__ double s_base, s_t;
+    __shared__ double s_base, s_t, s_W, s_S[3];
     constexpr int E = Elt<DT>::EPV;
     // SPLIT: a.split workgroups share each sequence; else one, and this compiles to the plain
     // single-workgroup pass
@@ -1290,80 +1830,132 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     int32_t *out = a.out_tokens + (size_t)b * (K + 1) + si.L;
     float *out_prob = a.draw_probs ? a.draw_probs + b : nullptr;
     double *units = dyn;
-    // solo: this workgroup makes the whole-row pass alone (the other workgroups of a split
-    // sequence have left)
-    bool solo = false;
     if (!r.resid) {  // w = p_L: one chunk of the row is read again, not the whole row
         if (SPLIT && g != 0)
             return;
-        if (chunk_draw<DT, MODE>(a, r, si, b, u01, units, out, out_prob))
-            return;
-        solo = true;
+        if ((a.flags & TEST_CHUNK_FALLBACK) ||
+            !chunk_draw<DT, MODE>(a, r, si, b, u01, units, out, out_prob))
+            target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
+        return;
     }
-    // a draft-side row read as well: NV_TAIL vectors per row per iteration, else twice as many
-    const bool two = (MODE == CONTRASTIVE) || r.two;
-    const int nv = two ? NV_TAIL : 2 * NV_TAIL, ce = TAIL_WG * nv * E;
-    const int nit = (V + ce - 1) / ce, per_it = nv * TAIL_WAVES, nu = nit * per_it;
+
+    // ---- the residual draw, in fp64
+    ExactRows x = {r.p0, r.p1, r.b0, r.b1, r.al, si.Mp, si.Mq, a.sp.c, a.sq.c, 0.0,
+                   nullptr, nullptr, nullptr};
+    if constexpr (DT == 1) {
+        exact_tables<MODE>(x, s_tab);
+        __syncthreads();
+    }
+    constexpr int CE2 = TAIL_WG * NV_EXACT * E;
+    const int nit = (V + CE2 - 1) / CE2, nu = nit * NV_EXACT * TAIL_WAVES;
+    // sorted with the statistics' approximate sums (see the section's notes)
+    const double cp0 = 1.0 / si.Sp, cq0 = 1.0 / si.Sq;
+    ExactAcc acc;
+    exact_pass<DT, MODE>(x, V, g, G, cp0, cq0, units, acc);
+    block_sum3(acc.tp, acc.tq, acc.near, s_S);
+    __syncthreads();
+    if (SPLIT) {
+        // gunits of sequence b: 2 sums per unit, then 3 totals per workgroup
+        double *gu = a.gunits + (size_t)b * a.nu_stride;
+        if (w == 0) {
+            // The sums go out as device-coherent stores, and the wave waits until they are
+            // acknowledged before it counts in, so a workgroup that sees the count complete
+            // reads every share with device-coherent loads.  (A device fence would also write
+            // back the whole L2, which costs more than the draw.)
+            constexpr int PER_IT = 2 * NV_EXACT * TAIL_WAVES;  // doubles per iteration
+            for (int it = g; it < nit; it += G)
+                for (int k = lane; k < PER_IT; k += 64)
+                    __hip_atomic_store(gu + it * PER_IT + k, units[it * PER_IT + k],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane < 3)
+                __hip_atomic_store(gu + 2 * nu + 3 * g + lane, s_S[lane], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            int last = 0;
+            if (lane == 0)
+                last = (__hip_atomic_fetch_add(a.gcount + b, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) == G - 1);
+            last = __shfl(last, 0);
+            if (last && lane == 0)  // every share is in: ready for the next call
+                __hip_atomic_store(a.gcount + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0)
+                s_last = last;
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        constexpr int PER_IT = 2 * NV_EXACT * TAIL_WAVES;
+        for (int k = t; k < 2 * nu; k += TAIL_WG)
+            if ((k / PER_IT) % G != g)
+                units[k] = __hip_atomic_load(gu + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (t == 0) {  // the totals of every workgroup, in workgroup order
+            double tot[3] = {0.0, 0.0, 0.0};
+            for (int v = 0; v < G; ++v)
+                for (int k = 0; k < 3; ++k)
+                    tot[k] += (v == g) ? s_S[k]
+                                       : __hip_atomic_load(gu + 2 * nu + 3 * v + k, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            s_S[0] = tot[0];
+            s_S[1] = tot[1];
+            s_S[2] = tot[2];
+        }
+        __syncthreads();
+    }
+    const double Sp = s_S[0], Sq = s_S[1], near_q = s_S[2];
+    if (!(Sp > 0.0) || !(Sq > 0.0)) {  // a row without finite logits: outside the contract
+        __syncthreads();
+        target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
+        return;
+    }
+    const double np_r = 1.0 / Sp, nq_r = 1.0 / Sq;
+    // unit weights A / S_p - B / S_q, compacted to one double per unit
+    static_assert((MAX_VOCAB + TAIL_WG * NV_EXACT * 4 - 1) / (TAIL_WG * NV_EXACT * 4) * NV_EXACT *
+                          TAIL_WAVES <= 4 * TAIL_WG,
+                  "each thread converts at most four units");
+    double cp_r = cp0, cq_r = cq0;
     for (int pass = 0; pass < 2; ++pass) {
-        const bool target_law = (pass == 1);
-        // the first pass is shared by the sequence's workgroups; a repeat, or a pass after a
-        // chunk draw that found no weight, is done by one alone
-        const bool shared = pass == 0 && !solo;
-        const int first = shared ? g : 0, step = shared ? G : 1;
-        if (two)
-            tail_unit_sums<DT, MODE, NV_TAIL, true>(r, V, nit, first, step, target_law, si, a.sp,
-                                                    a.sq, units);
-        else if constexpr (MODE == SAMPLING)
-            tail_unit_sums<DT, MODE, 2 * NV_TAIL, false>(r, V, nit, first, step, target_law, si,
-                                                         a.sp, a.sq, units);
-        __syncthreads();
-        if (SPLIT && shared) {
-            double *gu = a.gunits + (size_t)b * a.nu_stride;
-            if (w == 0) {
-                // The sums go out as device-coherent stores, and the wave waits until they
-                // are acknowledged before it counts in, so a workgroup that sees the count
-                // complete reads every share with device-coherent loads.  (A device fence
-                // would also write back the whole L2, which costs more than the draw.)
-                for (int it = g; it < nit; it += G)
-                    for (int k = lane; k < per_it; k += 64)
-                        __hip_atomic_store(gu + it * per_it + k, units[it * per_it + k],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                int last = 0;
-                if (lane == 0)
-                    last = (__hip_atomic_fetch_add(a.gcount + b, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT) == G - 1);
-                last = __shfl(last, 0);
-                if (last && lane == 0)  // every share is in: ready for the next call
-                    __hip_atomic_store(a.gcount + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (lane == 0)
-                    s_last = last;
-            }
-            __syncthreads();
-            if (!s_last)
-                return;
-            for (int k = t; k < nu; k += TAIL_WG)
-                if ((k / per_it) % G != g)
-                    units[k] = __hip_atomic_load(gu + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
+        double wk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = t + j * TAIL_WG;
+            const double d = (k < nu) ? units[2 * k] * np_r - units[2 * k + 1] * nq_r : 0.0;
+            wk[j] = d > 0.0 ? d : 0.0;
         }
-        find_unit_block(units, nu, u01, &s_unit, &s_base, &s_t, &s_fb);
         __syncthreads();
-        const int us = s_unit;
-        if (us >= 0) {
-            if (w == 0)
-                search_unit<DT, MODE>(r, si, V, nv, us, s_base, s_t, s_fb != 0, target_law, a.sp,
-                                      a.sq, out, out_prob);
-            return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = t + j * TAIL_WG;
+            if (k < nu)
+                units[k] = wk[j];
         }
-        // every unit weighs 0: the residual is empty by rounding; draw from p_L instead
-        __syncthreads();  // find_unit_block has read the units the repeat overwrites
+        __syncthreads();
+        find_unit_block(units, nu, u01, &s_unit, &s_base, &s_t, &s_fb, &s_W);
+        __syncthreads();
+        // The approximate sums may sort an id differently from the exact ones only if its two
+        // sides agree within rel = |theta~/theta - 1|; each such id moves the weights by at most
+        // rel (1 + rel) e_q / S_q.  Keep the draw when those ids' draft mass bounds the error far
+        // below the decision scale, else sort again with the exact sums.
+        const double rel = fabs((si.Sp * Sq) / (si.Sq * Sp) - 1.0);
+        const bool sure = pass == 1 || (rel <= 0.5 * EXACT_NEAR &&
+                                        rel * (1.0 + rel) * near_q * nq_r <= 0x1p-24 * s_W &&
+                                        !(a.flags & TEST_EXACT_TWO_PASS));
+        if (sure)
+            break;
+        cp_r = np_r;
+        cq_r = nq_r;
+        exact_pass<DT, MODE>(x, V, 0, 1, cp_r, cq_r, units, acc);
+        __syncthreads();
     }
-    if (t == 0) {  // a row without finite logits: outside the contract
-        *out = -1;
-        if (out_prob)
-            *out_prob = NAN;
+    if (s_unit >= 0) {
+        if (w == 0)
+            exact_search<DT, MODE>(x, V, cp_r, cq_r, np_r, nq_r, s_unit, s_base, s_t, s_fb != 0,
+                                   out);
+        return;
     }
+    // every weight is 0 in fp64 as well: the residual is empty; draw from p_L
+    __syncthreads();
+    target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
 }
 
 // ------------------------------------------------------------------ early-exit verify
@@ -1905,7 +2497,7 @@ int tail_split(const Workspace &ws, int dtype, int B, int V)
 {
     if (B < 1 || B > ws.split_batch)
         return 1;
-    const int ce = TAIL_WG * NV_TAIL * elems_per_vec(dtype);
+    const int ce = TAIL_WG * NV_EXACT * elems_per_vec(dtype);  // iterations of the fp64 pass
     const int nit = (V + ce - 1) / ce;
     int g = ws.num_cus / B;
     g = g < TAIL_MAX_SPLIT ? g : TAIL_MAX_SPLIT;
@@ -1940,6 +2532,7 @@ TailArgs tail_args(const Workspace &ws, int dtype, int B, int K, int V, int nch,
     a.mask_probs = mask_probs;
     a.split = tail_split(ws, dtype, B, V);
     a.nu_stride = ws.nu_stride;
+    a.flags = ws.test_flags;
     return a;
 }
 

@@ -251,6 +251,51 @@ def make_sampling(B: int, K: int, V: int, dtype: int, temperature: float, seed: 
                     tokens=np.ascontiguousarray(tokens.reshape(B, K)), uniforms=uniforms, seed=seed)
 
 
+def make_small_residual(B: int, V: int, dtype: int, temperature: float, seed: int, *,
+                        target_sigma: float = 4.0, n_peaks: int = 20, peak_height: float = 8.0,
+                        noise_lo: float = 1e-4, noise_hi: float = 3e-2, top: int = 100,
+                        name: str = "small residual") -> Workload:
+    """Sampling-verify workload (K = 1) shaped so that position 0 rejects with a small residual
+    mass: a draft that is the target plus very little noise.
+
+    Target rows are N(0, target_sigma^2) plus ``peak_height`` at ``n_peaks`` distinct positions,
+    as in the large-vocabulary workload.  The draft row of position 0 is the float32 target row
+    plus N(0, s_b^2) noise, s_b log-uniform in [noise_lo, noise_hi] per sequence, then stored in
+    the logit type (a bfloat16 draft differs from its target only where the noise crosses a
+    rounding boundary, by one bfloat16 step).  The draft token is, among the ``top`` largest
+    target logits of the row (by value, with numpy's sort), the id whose stored draft logit rose
+    the most over its stored target logit, so that the draft favours it; the accept uniform is
+    1 - 2^-13 and the draw uniform a lattice value.  Nothing here evaluates a probability: the
+    workload only shapes logits.
+    """
+    s_logits, s_noise, s_peaks, _s_tokens, s_unif = _streams(seed)
+    t = normal_rows(s_logits, B * 2, V, target_sigma).reshape(B, 2, V)
+    if n_peaks:
+        rng = np.random.Generator(np.random.PCG64(s_peaks))
+        pos = _distinct_positions(rng, B * 2, n_peaks, V)
+        flat = t.reshape(B * 2, V)
+        flat[np.repeat(np.arange(B * 2), n_peaks), pos.reshape(-1)] += np.float32(peak_height)
+    noise = normal_rows(s_noise, B, V, 1.0)
+    rng = np.random.Generator(np.random.PCG64(s_unif))
+    sb = np.exp(rng.uniform(np.log(noise_lo), np.log(noise_hi), size=B)).astype(np.float32)
+    noise *= sb[:, None]
+    noise += t[:, 0, :]
+    target = _store(t, dtype)
+    draft = _store(noise.reshape(B, 1, V), dtype)
+    del t, noise
+    tv = decode(target[:, 0, :], dtype)
+    dv = decode(draft[:, 0, :], dtype)
+    idx = np.argsort(-tv, axis=1, kind="stable")[:, :top]
+    rise = np.take_along_axis(dv, idx, 1) - np.take_along_axis(tv, idx, 1)
+    tokens = np.take_along_axis(idx, np.argmax(rise, axis=1)[:, None], 1).astype(np.int32)
+    k_acc = (1 << _U_BITS) - (1 << (_U_BITS - 13))
+    u_acc = np.full((B, 1), (k_acc + 0.5) * _U_SCALE, dtype=np.float32)
+    uniforms = np.concatenate([u_acc, lattice_uniforms(rng, (B, 1))], axis=1)
+    return Workload(name=name, mode=SAMPLING, dtype=dtype, B=B, K=1, V=V,
+                    temperature=_f32(temperature), target=target, draft=draft,
+                    tokens=np.ascontiguousarray(tokens), uniforms=uniforms, seed=seed)
+
+
 def make_greedy(B: int, K: int, V: int, dtype: int, seed: int, *, sigma: float = 4.0,
                 match_prob: float = 0.7, name: str = "greedy") -> Workload:
     """Greedy blockwise workload: l ~ N(0, sigma^2); proposal j equals the row's first

@@ -64,6 +64,7 @@ def test_null_context_is_rejected_on_the_host():
     assert lib.specverify_profile_end(None, None, None) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_profile_launches(None, 0, None, 0) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_workspace_bytes(None) == 0
+    assert lib.specverify_set_test_flags(None, 0) == sv.SPECVERIFY_EINVAL
     h = ctypes.c_void_p()
     assert lib.specverify_create(None, 0, 1, 1, 1) == sv.SPECVERIFY_EINVAL
     assert lib.specverify_create(ctypes.byref(h), 0, 0, 1, 1) == sv.SPECVERIFY_EINVAL
@@ -93,6 +94,8 @@ def test_binding_constants_match_the_header():
     assert eval(defs["SPECVERIFY_MAX_K"]) == sv.SPECVERIFY_MAX_K
     assert eval(defs["SPECVERIFY_MAX_VOCAB"]) == sv.SPECVERIFY_MAX_VOCAB
     assert eval(defs["SPECVERIFY_NUM_KERNELS"]) == sv.SPECVERIFY_NUM_KERNELS == len(sv.KERNEL_NAMES)
+    for k in ("SPECVERIFY_TEST_CHUNK_FALLBACK", "SPECVERIFY_TEST_EXACT_TWO_PASS"):
+        assert int(defs[k].rstrip("u")) == getattr(sv, k), k
     enums = dict((k, int(v)) for k, v in re.findall(r"\b(SPECVERIFY_[A-Z0-9]+) = (-?\d+)", text))
     for k, v in enums.items():
         assert getattr(sv, k) == v, k
@@ -137,6 +140,7 @@ int main(void)
     EXPECT(specverify_profile_launches(NULL, 0, NULL, 0), SPECVERIFY_EINVAL);
     EXPECT(specverify_profile_end(NULL, NULL, NULL), SPECVERIFY_EINVAL);
     EXPECT(specverify_workspace_bytes(NULL), 0);
+    EXPECT(specverify_set_test_flags(NULL, SPECVERIFY_TEST_EXACT_TWO_PASS), SPECVERIFY_EINVAL);
     EXPECT(specverify_destroy(NULL), SPECVERIFY_OK);
     if (specverify_strerror(SPECVERIFY_EINVAL) == NULL || ctx != NULL)
         bad |= 1 << k;
