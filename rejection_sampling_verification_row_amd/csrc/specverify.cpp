@@ -185,9 +185,8 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     const int split_batch = std::min(max_batch, cus / 2);
     // per sequence of a shared draw: the fp64 pass's two sums per unit and three totals per
     // workgroup
-    const int nu_stride =
-        2 * std::max(sv::exact_units(0, max_vocab), sv::exact_units(1, max_vocab)) +
-        3 * sv::TAIL_MAX_SPLIT;
+    // per sequence: two fp64 sums per segment, three totals per workgroup
+    const int nu_stride = 2 * sv::EXACT_MAX_SEGS + 3 * sv::TAIL_MAX_SPLIT;
     const size_t b_part = align_up(rows * nch * sv::WAVES * sizeof(float2));
     const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
     const size_t b_gu = align_up((size_t)split_batch * nu_stride * sizeof(double));

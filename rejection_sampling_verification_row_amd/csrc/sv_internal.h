@@ -27,7 +27,7 @@ constexpr int MAX_ROWS = 2 * 63 + 1;  // rows per sequence at the largest K
 constexpr int TAIL_WG = 1024;
 constexpr int TAIL_WAVES = TAIL_WG / 64;
 constexpr int NV_TAIL = 2;
-constexpr int ACCEPT_STAGE = 4096;    // float2 partials staged in LDS by the accept phase
+constexpr int ACCEPT_STAGE = 3072;    // float2 partials staged in LDS by the accept phase
 constexpr int MAX_VOCAB = 1 << 20;    // keeps the unit sums within 32 KiB of LDS
 constexpr int MAX_CUT_N = 8192;       // scores per prompt of the quantile cut (32 KiB of LDS)
 constexpr int EARLY_PREFIX = 2;       // positions every sequence reads before early exit
@@ -36,8 +36,9 @@ constexpr int EARLY_PREFIX_GREEDY = 3; // the same for greedy verify (B=512 K=8 
 constexpr int TAIL_MAX_SPLIT = 8;     // most workgroups that share one sequence's draw
 
 // The residual draw (L < K) is made in fp64 from the logits of row L (see exact_pass in the
-// kernels), in iterations of TAIL_WG * NV_EXACT vectors per row laid out as the fp32 row pass's;
-// its unit is one wave's vector slot, 64 * EPV contiguous ids, with two fp64 sums per unit.
+// kernels): the row's wave vectors (64 lanes x 16 bytes) go to 16 contiguous segments per
+// workgroup sharing the draw, a wave streams its segment NV_EXACT wave vectors per step, and a
+// segment's unit sums are two fp64 values.  bfloat16 kernels also hold two 64 KiB tables in LDS.
 constexpr int NV_EXACT = 2;
 
 // test-only switches (specverify_set_test_flags): reach draw paths that data rarely reaches
@@ -67,20 +68,24 @@ inline int tail_units(int dtype, int V)
     }
     return most;
 }
-// units of the fp64 residual pass: one per wave and vector slot of each iteration
-inline int exact_units(int dtype, int V)
+// segments of the fp64 residual pass of one sequence (16 per workgroup sharing the draw)
+constexpr int EXACT_MAX_SEGS = TAIL_WAVES * TAIL_MAX_SPLIT;
+// wave vectors per segment of the fp64 residual pass with one workgroup (the most)
+inline int exact_seg_vectors(int dtype, int V)
 {
-    const int ce = TAIL_WG * NV_EXACT * elems_per_vec(dtype);
-    return (V + ce - 1) / ce * NV_EXACT * TAIL_WAVES;
+    const int wv = 64 * elems_per_vec(dtype), nwv = (V + wv - 1) / wv;
+    const int per = TAIL_WAVES * NV_EXACT;
+    return (nwv + per - 1) / per * NV_EXACT;
 }
 // dynamic LDS of the tail kernel: the staged partials, then (reusing it) the unit sums of the
-// fp32 pass of a draw from p_L, or the two fp64 sums per unit of the residual pass
+// fp32 pass of a draw from p_L, or the residual pass's two fp64 sums per segment and one
+// weight per wave vector of a segment
 inline size_t tail_lds_bytes(int dtype, int K, int V, int nch)
 {
     const size_t parts = (size_t)(2 * K + 1) * nch * WAVES;
     const size_t stage = parts <= (size_t)ACCEPT_STAGE ? parts * 8 : 0;
     const size_t units = (size_t)tail_units(dtype, V) * 8;
-    const size_t exact = (size_t)exact_units(dtype, V) * 16;
+    const size_t exact = (size_t)(2 * EXACT_MAX_SEGS + exact_seg_vectors(dtype, V)) * 8;
     size_t m = stage > units ? stage : units;
     return m > exact ? m : exact;
 }

@@ -705,7 +705,7 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
                                                        const char *__restrict__ drf, int K, int V,
                                                        int nch, Scale sc, float2 *part)
 {
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    constexpr int BY = Elt<DT>::BYTES;
     const int R = 2 * K + 1;
     const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
     const int b = row / R, r = row - b * R;
@@ -1149,47 +1149,90 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
 // carry about 1e-7 of p each, and the fp32 row statistics put a common error of the same order
 // on every p (or q) of a row, which max(0, p - q) does not cancel; at W of 1e-3 that is far
 // above the 1e-6 decision margins.  So the residual draw is computed in fp64 from the logits of
-// row L: e_p(v) = 2^((z_p(v) - M_p) log2(e)/T_p) and e_q(v) = 2^((x_q(v) - M_q) log2(e)/T_q)
-// (z_p the target-side logit, or the expert-minus-amateur difference formed exactly in fp64),
-// and the normalising sums S_p = sum e_p, S_q = sum e_q recomputed in fp64 in the same pass.
-// Which side of the residual an id is on, e_p / S_p > e_q / S_q, is needed before the sums are
-// known, so the pass sorts ids with the statistics' approximate sums; each unit keeps A = sum e_p
-// and B = sum e_q over its ids on the positive side, and afterwards its weight is
-// A / S_p - B / S_q with the exact sums.  An id can be sorted differently by the approximate and
-// the exact sums only if its ratio of the two sides lies between theirs, so the error of the
-// unit weights is at most |theta~/theta - 1| times the draft mass of the ids whose sides agree
-// within that (theta the ratio of the sums); the pass sums the draft mass of the ids within
-// EXACT_NEAR, and when the bound is not far below the decision scale (2^-24 W) it is repeated
-// with the exact sums.
+// row L.  Per id v it forms a(v) = 2^((z_p(v) - M_p) log2(e)/T_p) * r and
+// b(v) = 2^((x_q(v) - M_q) log2(e)/T_q) (z_p the target-side logit, or the expert-minus-amateur
+// difference formed exactly in fp64; r a scale), and the sums S_a = sum a, S_b = sum b, so
+// that p(v) = a(v) / S_a and q(v) = b(v) / S_b.  Which side of the residual an id is on,
+// a / S_a > b / S_b, is needed before the sums are known; with r = S~_q / S~_p from the
+// statistics' approximate sums the pass sorts an id to the positive side when a > b, keeps
+// per unit A = sum a and B = sum b over its positive-side ids, and afterwards takes the unit's
+// weight A / S_a - B / S_b with the exact sums.  The exact side test is a > b * theta,
+// theta = S_a / S_b, so an id can be sorted differently only if a / b lies between 1 and
+// theta; each such id moves the weights by at most rel (1 + rel) b / S_b, rel = |theta - 1|.
+// The pass sums the draft mass b of the ids whose a and b agree to about 2^-16 (their upper
+// 32 bits differ by at most NEAR_HI), which holds every such id while rel <= 2^-17; when that
+// bound is not far below the decision scale (2^-24 W) the pass is repeated with r from the
+// exact sums.
 //
-// For bfloat16 rows the fp64 exps come from LDS tables: a bfloat16 value is one of at most
-// 65536 bit patterns, and the 5120 with 2^-12 <= |x| < 2^8 (both signs) cover the logits of a
-// language model's head; each table holds 2^((x - M) c) for them, computed once per row with
-// fp64 exp2, and ids outside the table take fp64 exp2 directly.
+// The row is cut into 16 G contiguous segments, one per wave of the G workgroups that share
+// the draw; a wave streams its segment (1 KiB per load) and keeps its sums in registers, so a
+// unit is a segment.  The draw then finds the segment holding t, weighs its vectors one per
+// wave to find the vector, and one wave finds the lane and the id in it.
+//
+// For bfloat16 rows a and b come from LDS tables: a bfloat16 value is one of 65536 bit
+// patterns, and the 7168 with 2^-20 <= |x| < 2^8 cover the logits of a language model's head.
+// A slot is found from the bit pattern with packed 16-bit integer operations, two ids at a
+// time; values outside the tables read a NaN sentinel (or +0.0 for values below -2^8 whose
+// term is negligible), which spoils the lane's sums for that step, and the lane weighs the
+// step again id by id with fp64 exp2 for those ids.
 
-constexpr int TAB_E0 = 115;               // bfloat16 exponent field of 2^-12
-constexpr int TAB_NE = 20;                // fields 115..134: 2^-12 <= |x| < 2^8
-constexpr int TAB_HALF = TAB_NE * 128;    // tabulated values per sign
-// Each sign's block is [below, TAB_HALF values, above]: the two sentinel slots take the
-// magnitudes below and above the tabulated ones.  A slot is found with one clamp, no branch.
-constexpr int TAB_BLOCK = TAB_HALF + 2;
-constexpr int TAB_STRIDE = 2 * TAB_BLOCK; // doubles per table (41 KiB)
-constexpr double TAB_TINY = 0x1p-60;      // a term this far below the row's largest counts as 0
+constexpr int TAB_E0 = 107;               // bfloat16 exponent field of 2^-20
+constexpr int TAB_NE = 28;                // fields 107..134: 2^-20 <= |x| < 2^8
+constexpr int TAB_LO = TAB_E0 << 7;       // the smallest tabulated magnitude's 15 low bits
+constexpr int TAB_HALF = TAB_NE * 128;    // tabulated magnitudes per sign
+// Each sign's block is 4096 doubles: slot 0 takes magnitudes below the tabulated ones, slots
+// 1..TAB_HALF the tabulated ones, slot TAB_HALF + 1 those above; the sign is bit 15 of the
+// slot's byte offset and table 1 lies 64 KiB after table 0.
+constexpr int TAB_SIGN = 4096;
+constexpr int TAB_DOUBLES = 2 * TAB_SIGN;  // one table: 64 KiB
+static_assert(TAB_HALF + 2 <= TAB_SIGN && TAB_SIGN * 8 == 0x8000, "slot byte offsets are 15 bits");
+constexpr double TAB_TINY = 0x1p-80;      // a term this far below the row's largest counts as 0
+// the ids whose a and b have upper words at most this far apart count as near the threshold
+constexpr uint32_t NEAR_HI = 32;
+constexpr double NEAR_REL = 0x1p-17;      // the largest rel for which NEAR_HI holds every such id
 
-// the slot of a bfloat16 bit pattern: the tabulated value, or a sentinel of its sign
-__device__ __forceinline__ int tab_slot(uint32_t b)
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// byte offset of the slot of one bfloat16 pattern b (16 bits) within a table: the magnitude's
+// 15 bits less TAB_LO - 1, clamped to [0, TAB_HALF + 1], times 8, and the sign in bit 15
+__device__ __forceinline__ uint32_t tab_offset(uint32_t b)
 {
-    const int t = (int)(b & 0x7fffu) - (TAB_E0 << 7);
-    const int c = min(max(t, -1), TAB_HALF);   // clamp to [-1, TAB_HALF] (one v_med3_i32)
-    return (int)((b >> 15) & 1u) * TAB_BLOCK + 1 + c;
+    const int d = (int)(b & 0x7fffu) - (TAB_LO - 1);
+    const int s = min(max(d, 0), TAB_HALF + 1);
+    return (uint32_t)(s * 8) | (b & 0x8000u);
 }
 
-// the bfloat16 value of tabulated slot k (a slot of neither sentinel)
-__device__ __forceinline__ double tab_value(int k)
+// the same for the two patterns of a 32-bit word, in its two halves (packed 16-bit operations:
+// a saturating subtract takes magnitudes below TAB_LO - 1 to slot 0, a minimum the rest)
+__device__ __forceinline__ uint32_t tab_offsets2(uint32_t w)
 {
-    const int sign = k / TAB_BLOCK, j = k - sign * TAB_BLOCK - 1;
-    const uint32_t b = ((uint32_t)sign << 15) | (uint32_t)((TAB_E0 << 7) + j);
-    return (double)__uint_as_float(b << 16);
+    const u16x2 m = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+    const u16x2 d = __builtin_elementwise_sub_sat(m, (u16x2)(unsigned short)(TAB_LO - 1));
+    const u16x2 c = __builtin_elementwise_min(d, (u16x2)(unsigned short)(TAB_HALF + 1));
+    const u16x2 o = c << (u16x2)(unsigned short)3;
+    return __builtin_bit_cast(uint32_t, o) | (w & 0x80008000u);
+}
+
+// The tables live at LDS address 0 (the kernel's first LDS variable, see k_tail), so a slot's
+// byte offset is its address and the loads need no base register.
+__device__ __forceinline__ double tab_at(const char *tab, uint32_t off)
+{
+    return *reinterpret_cast<const double *>(tab + off);
+}
+// table 0 (the target side) and table 1 (the draft side) at the low or high half's offset of a
+// packed pair (one byte permute each)
+__device__ __forceinline__ uint32_t t0_lo(uint32_t o2) { return __builtin_amdgcn_perm(0u, o2, 0x0c0c0100u); }
+__device__ __forceinline__ uint32_t t0_hi(uint32_t o2) { return __builtin_amdgcn_perm(0u, o2, 0x0c0c0302u); }
+__device__ __forceinline__ uint32_t t1_lo(uint32_t o2) { return __builtin_amdgcn_perm(0x10000u, o2, 0x0c060100u); }
+__device__ __forceinline__ uint32_t t1_hi(uint32_t o2) { return __builtin_amdgcn_perm(0x10000u, o2, 0x0c060302u); }
+
+// |x - y| of two 32-bit words (v_sad_u32)
+__device__ __forceinline__ uint32_t absdiff(uint32_t x, uint32_t y)
+{
+    uint32_t d;
+    asm("v_sad_u32 %0, %1, %2, 0" : "=v"(d) : "v"(x), "v"(y));
+    return d;
 }
 
 // fp64 exp2 for the ids outside the tables: out of line, so that its constants do not take
@@ -1201,140 +1244,242 @@ struct ExactRows {
     const char *p0, *p1;     // target (expert) row L, draft (amateur) row L
     __amdgpu_buffer_rsrc_t b0, b1;  // the same rows as buffer resources (see DrawRows)
     bool al;                 // both rows 16-byte aligned
+    bool tabled;             // bfloat16 rows with tables built
     float Mp, Mq;            // the rows' maxima from the statistics (the exps' reference points)
     double cp, cq;           // log2(e) / T of each law
-    double kc;               // contrastive bfloat16: 2^(-M_p cp)
-    const double *tp, *tq, *tn;  // bfloat16 tables (LDS), see exact_tables
+    double r;                // the target-side scale
+    const char *tab;         // LDS: table 0 at +0, table 1 at +64 KiB
 };
 
-// The LDS tables of the two rows (bfloat16 only), by the whole workgroup.  Sampling: tp[k] =
-// 2^((x_k - M_p) cp), tq[k] = 2^((x_k - M_q) cq).  Contrastive: tq as sampling for the amateur
-// law, and for p = 2^((x_e - x_a - M_p) cp) = tp[k_e] * tn[k_a] * kc the factors tp[k] =
-// 2^(x_k cp) and tn[k] = 2^(-x_k cp), left NaN where |x_k cp| > 1000 (their product could leave
-// the fp64 range): such ids take exp2 directly.
+// Whether the tables serve this row pair.  Sampling: while one group's span of 16 mantissa
+// steps, at most 2^4 c in the exponent, keeps its largest value finite (c <= 60).  Contrastive:
+// the target-side table holds factors 2^(v c_p) * sqrt(2^(-M_p c_p) r) with a = f(z_e) f(-z_a);
+// both factors and their product stay inside the fp64 range while 512 c_p <= 1000 and
+// |M_p| <= 512.
 template <int MODE>
-__device__ inline void exact_tables(ExactRows &x, double *tab)
+__device__ __forceinline__ bool exact_tabled(float Mp, double cp, double cq)
 {
-    double *tp = tab, *tq = tab + TAB_STRIDE, *tn = tab + 2 * TAB_STRIDE;
-    // Sentinels hold -0.0 (the id's term comes from exp2) or +0.0 (the term is taken as 0):
-    // below -2^8 (and -inf) the term is at most 2^((-2^8 - M) c), +0.0 when that is below
-    // TAB_TINY (sampling, and the amateur law of contrastive verify).
+    if (MODE == SAMPLING)
+        return cp <= 60.0 && cq <= 60.0;
+    return 512.0 * cp <= 1000.0 && fabsf(Mp) <= 512.0f && cq <= 60.0;
+}
+
+// The LDS tables (bfloat16), by the whole workgroup.  Table 0: sampling a = 2^((x - M_p) c_p) r;
+// contrastive the factors 2^(x c_p) sqrt(2^(-M_p c_p) r).  Table 1: b = 2^((x - M_q) c_q).
+// which: 1 table 0, 2 table 1, 3 both.  A slot's value v = +-(128 + 16 jb + j) 2^(E - 134)
+// (exponent field E = TAB_E0 + e, mantissa 16 jb + j) is the product of its group's largest
+// value (j = 15 for +, j = 0 for -) and 2^(-d c 2^(E - 134)), d its mantissa steps below it,
+// each by fp64 exp2 (a few ulps for the product).  Phase 1 computes those group values and
+// step powers into the unused slots past TAB_HALF + 1 (group (s, e, jb) at TAB_SPARE0 +
+// 8 e + jb of sign block s; power (e, d) at TAB_SPARE0 + 224 + 8 e + d % 8 of sign block
+// d / 8); phase 2 writes every slot, consecutive threads consecutive slots.  The caller's
+// barrier (LDS only suffices) follows.
+constexpr int TAB_SPARE0 = TAB_HALF + 2;      // the first unused slot of a sign block
+constexpr int TAB_GRP = TAB_NE * 8;           // groups per sign
+static_assert(TAB_SPARE0 + 2 * TAB_GRP <= TAB_SIGN, "the phase-1 values fit in the unused slots");
+
+// A workgroup barrier that orders LDS only: unlike __syncthreads() it does not wait for the
+// wave's global loads, so loads issued before it stay in flight across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 2^(E - 134) for exponent field E = TAB_E0 + e: one mantissa step of that binade
+__device__ __forceinline__ double tab_unit(int e)
+{
+    return __hiloint2double((TAB_E0 + e - 134 + 1023) << 20, 0);
+}
+
+template <int MODE>
+__device__ inline void exact_tables(const ExactRows &x, double *tab, int which)
+{
+    const int t = threadIdx.x;
     const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
-    const double neg_p = (exp2((-top - (double)x.Mp) * x.cp) <= TAB_TINY) ? 0.0 : -0.0;
-    const double neg_q = (exp2((-top - (double)x.Mq) * x.cq) <= TAB_TINY) ? 0.0 : -0.0;
-    for (int k = threadIdx.x; k < TAB_STRIDE; k += TAIL_WG) {
-        const int sign = k / TAB_BLOCK, j = k - sign * TAB_BLOCK;
-        if (j == 0 || j == TAB_BLOCK - 1) {
-            const bool neg_above = sign == 1 && j == TAB_BLOCK - 1;
-            tq[k] = neg_above ? neg_q : -0.0;
-            tp[k] = (MODE == SAMPLING && neg_above) ? neg_p : -0.0;
-            if (MODE == CONTRASTIVE)
-                tn[k] = -0.0;
+    // phase 1: per table 2 * TAB_GRP group values and TAB_NE * 16 step powers (as many); then
+    // the sentinels (below and above, per sign and table)
+    constexpr int P1 = 4 * TAB_GRP;
+    for (int k1 = t; k1 < 2 * P1 + 8; k1 += TAIL_WG) {
+        if (k1 >= 2 * P1) {
+            const int k = k1 - 2 * P1, tb = k >> 2, s = (k >> 1) & 1, above = k & 1;
+            if ((which >> tb) & 1) {
+                double v = __builtin_nan("");
+                if (above && s == 1 && !(MODE == CONTRASTIVE && tb == 0)) {
+                    // values below -2^8: the term is at most 2^((-2^8 - M) c) * scale
+                    const float M = tb ? x.Mq : x.Mp;
+                    const double c = tb ? x.cq : x.cp, sc = tb ? 1.0 : x.r;
+                    if (exp2((-top - (double)M) * c) * sc <= TAB_TINY)
+                        v = 0.0;
+                }
+                tab[tb * TAB_DOUBLES + s * TAB_SIGN + (above ? TAB_HALF + 1 : 0)] = v;
+            }
             continue;
         }
-        const double v = tab_value(k);
-        tq[k] = exp2((v - (double)x.Mq) * x.cq);
-        if (MODE == SAMPLING) {
-            tp[k] = exp2((v - (double)x.Mp) * x.cp);
-        } else {
-            // factors 2^(v cp) and 2^(-v cp); exact_rows_tabled() keeps them in range
-            tp[k] = exp2(v * x.cp);
-            tn[k] = exp2(-v * x.cp);
+        const int tb = k1 >= P1 ? 1 : 0, r = k1 - tb * P1;
+        if (!((which >> tb) & 1))
+            continue;
+        const double c = tb ? x.cq : x.cp;
+        double *T = tab + tb * TAB_DOUBLES;
+        if (r < 2 * TAB_GRP) {  // group value: sign s, exponent e, mantissas 16 jb ..
+            const int s = r >= TAB_GRP ? 1 : 0, g = r - s * TAB_GRP, e = g >> 3, jb = g & 7;
+            const double xv = (s ? -1.0 : 1.0) * (double)(128 + 16 * jb + (s ? 0 : 15)) *
+                              tab_unit(e);
+            double v;
+            if (tb == 0 && MODE == CONTRASTIVE)
+                v = exp2(xv * c) * (exp2(-(double)x.Mp * c * 0.5) * sqrt(x.r));
+            else
+                v = exp2((xv - (double)(tb ? x.Mq : x.Mp)) * c) * (tb ? 1.0 : x.r);
+            T[s * TAB_SIGN + TAB_SPARE0 + g] = v;
+        } else {  // step power: exponent e, d steps
+            const int q = r - 2 * TAB_GRP, e = q >> 4, d = q & 15;
+            T[(d >> 3) * TAB_SIGN + TAB_SPARE0 + TAB_GRP + 8 * e + (d & 7)] =
+                exp2(-(double)d * tab_unit(e) * c);
         }
     }
-    x.tp = tp;
-    x.tq = tq;
-    x.tn = tn;
-    x.kc = exp2(-(double)x.Mp * x.cp);
+    lds_barrier();
+    // phase 2: slot 1 + m of sign s, m = 128 e + 16 jb + j
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+        const int tb = ts >> 1, s = ts & 1;
+        if (!((which >> tb) & 1))
+            continue;
+        double *T = tab + tb * TAB_DOUBLES;
+        for (int m = t; m < TAB_HALF; m += TAIL_WG) {
+            const int e = m >> 7, jb = (m >> 4) & 7, j = m & 15, d = s ? j : 15 - j;
+            const double gv = T[s * TAB_SIGN + TAB_SPARE0 + 8 * e + jb];
+            const double pw = T[(d >> 3) * TAB_SIGN + TAB_SPARE0 + TAB_GRP + 8 * e + (d & 7)];
+            T[s * TAB_SIGN + 1 + m] = gv * pw;
+        }
+    }
 }
 
-// Whether the tables serve this row pair: always for sampling; for contrastive verify while the
-// factors 2^(+-x cp) of every tabulated x (|x| < 2^8) and their products stay far inside the
-// fp64 range (|x cp| <= 2^8 cp <= 1000), else every id takes exp2.
-template <int MODE> __device__ __forceinline__ bool exact_rows_tabled(const ExactRows &x)
+// One id's a and b from its bit patterns (bfloat16: bp, bq; float32: the float bits): the
+// tables where they hold its values, else fp64 exp2.  The pass's slow path and the search use
+// this; the pass's fast path reads the same table entries with the same products.
+template <int DT, int MODE>
+__device__ __forceinline__ void exact_terms(uint32_t bp, uint32_t bq, const ExactRows &x,
+                                            double &a, double &b)
 {
-    return MODE == SAMPLING || (double)(1 << (TAB_E0 + TAB_NE - 127)) * x.cp <= 1000.0;
+    bool da = true, db = true;
+    if (DT == 1 && x.tabled) {
+        const uint32_t op = tab_offset(bp), oq = tab_offset(bq);
+        b = tab_at(x.tab, 0x10000u | oq);
+        a = tab_at(x.tab, op);
+        if (MODE == CONTRASTIVE)
+            a *= tab_at(x.tab, oq ^ 0x8000u);
+        da = __builtin_isnan(a);
+        db = __builtin_isnan(b);
+    }
+    const double pv = (DT == 1) ? (double)__uint_as_float(bp << 16) : (double)__uint_as_float(bp);
+    const double qv = (DT == 1) ? (double)__uint_as_float(bq << 16) : (double)__uint_as_float(bq);
+    const double ap = ((MODE == SAMPLING ? pv : pv - qv) - (double)x.Mp) * x.cp;
+    const double aq = (qv - (double)x.Mq) * x.cq;
+    if (DT == 1) {
+        if (da)
+            a = exp2_cold(ap) * x.r;
+        if (db)
+            b = exp2_cold(aq);
+    } else {
+        a = exp2(ap) * x.r;
+        b = exp2(aq);
+    }
 }
 
-// -0.0: a sentinel whose id takes exp2 (see exact_tables)
-__device__ __forceinline__ bool neg_zero(double v) { return __builtin_amdgcn_class(v, 0x20); }
+// A lane's sums over one step of its segment: A, B over the positive side (a > b), the totals
+// of a and b, and the draft mass of the ids near the threshold.
+struct ExactLoc {
+    double A, B, tp, tq, near;
+};
 
-// One id's fp64 terms from the bfloat16 tables: returns false (with e_p, e_q of 0) if a value
-// lies outside them; such ids take direct_terms.
+__device__ __forceinline__ void exact_acc(double a, double b, ExactLoc &l)
+{
+    const double mv = (a > b) ? 1.0 : 0.0;
+    l.A = __builtin_fma(a, mv, l.A);
+    l.B = __builtin_fma(b, mv, l.B);
+    l.tp += a;
+    l.tq += b;
+    const uint32_t dh = absdiff((uint32_t)__double2hiint(a), (uint32_t)__double2hiint(b));
+    l.near = __builtin_fma(b, dh <= NEAR_HI ? 1.0 : 0.0, l.near);
+}
+
+// One 16-byte vector of each row (bfloat16, tables): eight ids, two per word.
 template <int MODE>
-__device__ __forceinline__ bool table_terms(uint32_t bp, uint32_t bq, const ExactRows &x,
-                                            double &ep, double &eq)
+__device__ __forceinline__ void exact_fast_vec(const uint4 &vp, const uint4 &vq, const char *tab,
+                                               ExactLoc &l)
 {
-    const int kp = tab_slot(bp), kq = tab_slot(bq);
-    const double q = x.tq[kq];
-    bool miss = neg_zero(q);
-    double p;
-    if constexpr (MODE == SAMPLING) {
-        p = x.tp[kp];
-        miss = miss | neg_zero(p);
-    } else {
-        const double f = x.tp[kp], g = x.tn[kq];
-        miss = miss | neg_zero(f) | neg_zero(g);
-        p = (f * g) * x.kc;
-    }
-    ep = miss ? 0.0 : p;
-    eq = miss ? 0.0 : q;
-    return !miss;
-}
-
-// One id's fp64 terms by exp2 from its target-side and draft-side values.
-template <int DT, int MODE>
-__device__ __forceinline__ void direct_terms(float pv, float qv, const ExactRows &x, double &ep,
-                                             double &eq)
-{
-    const double zp = (MODE == SAMPLING) ? (double)pv : (double)pv - (double)qv;
-    const double ap = (zp - (double)x.Mp) * x.cp, aq = ((double)qv - (double)x.Mq) * x.cq;
-    if constexpr (DT == 1) {
-        ep = exp2_cold(ap);
-        eq = exp2_cold(aq);
-    } else {
-        ep = exp2(ap);
-        eq = exp2(aq);
+    const uint32_t P[4] = {vp.x, vp.y, vp.z, vp.w}, Q[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t op = tab_offsets2(P[k]), oq = tab_offsets2(Q[k]);
+        const double b0 = tab_at(tab, t1_lo(oq)), b1 = tab_at(tab, t1_hi(oq));
+        double a0 = tab_at(tab, t0_lo(op)), a1 = tab_at(tab, t0_hi(op));
+        if (MODE == CONTRASTIVE) {
+            const uint32_t on = oq ^ 0x80008000u;  // the amateur value negated
+            a0 *= tab_at(tab, t0_lo(on));
+            a1 *= tab_at(tab, t0_hi(on));
+        }
+        exact_acc(a0, b0, l);
+        exact_acc(a1, b1, l);
     }
 }
 
-// One id's fp64 terms e_p, e_q: from the tables (bfloat16) where they hold its values, else by
-// exp2.  The pass and the search compute every id's terms with these same instructions.
-template <int DT, int MODE>
-__device__ __forceinline__ void exact_terms(float pv, float qv, uint32_t bp, uint32_t bq,
-                                            const ExactRows &x, double &ep, double &eq)
+// Geometry of the fp64 pass: the row's wave vectors (64 lanes x one 16-byte vector, WV ids)
+// go to nseg = 16 G segments of nsub = nst * NV_EXACT consecutive wave vectors; a wave takes
+// NV_EXACT of them per step.
+struct ExactGeom {
+    int nst, nsub, nseg;
+};
+
+template <int DT> __device__ __forceinline__ ExactGeom exact_geom(int V, int G)
 {
-    if constexpr (DT == 1) {
-        if (exact_rows_tabled<MODE>(x) && table_terms<MODE>(bp, bq, x, ep, eq))
-            return;
-    }
-    direct_terms<DT, MODE>(pv, qv, x, ep, eq);
+    constexpr int WV = 64 * Elt<DT>::EPV;
+    const int nwv = (V + WV - 1) / WV, per = TAIL_WAVES * G * NV_EXACT;
+    ExactGeom gm;
+    gm.nst = (nwv + per - 1) / per;
+    gm.nsub = gm.nst * NV_EXACT;
+    gm.nseg = TAIL_WAVES * G;
+    return gm;
 }
 
-// NV_EXACT consecutive vectors of a row from id e0 as raw 16-byte words (bfloat16: two ids per
-// 32-bit word, the lower id in the low half): whole vectors of an aligned row as 16-byte loads,
-// the rest (and every vector of an unaligned row) element by element; words of ids >= V are
-// filled with anything and never used
+// Wave vector vw of the two rows, this lane's 16 bytes, loaded nontemporally through the
+// rows' buffer resources (past V they read zeros, which the caller does not use).
 template <int DT>
-__device__ __forceinline__ void exact_load(const char *row, bool al, int e0, int V,
-                                           uint4 (&raw)[NV_EXACT])
+__device__ __forceinline__ void exact_fetch(const ExactRows &x, int vw0, uint4 (&rp)[NV_EXACT],
+                                            uint4 (&rq)[NV_EXACT])
 {
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES;
+    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, WV = 64 * E;
+    const int vo = (vw0 * WV + (int)(threadIdx.x & 63) * E) * BY;
 #pragma unroll
     for (int i = 0; i < NV_EXACT; ++i) {
-        const int v0 = e0 + i * E;
-        if (al && v0 + E <= V) {
-            raw[i] = load_plain(row + (size_t)v0 * BY);
-        } else if constexpr (E == 8) {
-            raw[i] = pack_bf16(row, v0, V);
-        } else {
-            uint32_t wd[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                wd[k] = (v0 + k < V) ? __float_as_uint(Elt<DT>::one(row, (size_t)(v0 + k))) : 0u;
-            raw[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        }
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(x.b0, vo + i * WV * BY, 0, 2);
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(x.b1, vo + i * WV * BY, 0, 2);
+        rp[i] = make_uint4(v.x, v.y, v.z, v.w);
+        rq[i] = make_uint4(u.x, u.y, u.z, u.w);
     }
+}
+
+// the lane's E ids of wave vector vw as raw words: the fetched words when the vector is whole
+// and the rows aligned, else element loads (bfloat16: two ids per word, the lower in the low
+// half; ids >= V are filled with anything and never used)
+template <int DT>
+__device__ __forceinline__ uint4 exact_words(const char *row, bool al, int e0, int V)
+{
+    constexpr int E = Elt<DT>::EPV;
+    uint4 raw[1];
+    if (al && e0 + E <= V) {
+        raw[0] = load_plain(row + (size_t)e0 * Elt<DT>::BYTES);
+    } else if constexpr (E == 8) {
+        raw[0] = pack_bf16(row, e0, V);
+    } else {
+        uint32_t wd[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wd[k] = (e0 + k < V) ? __float_as_uint(Elt<DT>::one(row, (size_t)(e0 + k))) : 0u;
+        raw[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    return raw[0];
 }
 
 // 32-bit word q (0..3) of a 16-byte vector
@@ -1343,270 +1488,327 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int q)
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// id h of a word: its float value and (bfloat16) its 16-bit pattern
-template <int DT>
-__device__ __forceinline__ float word_value(uint32_t wd, int h, uint32_t &bits)
+// id k (0..E-1) of a vector: its bit pattern (bfloat16 16 bits, float32 32 bits)
+template <int DT> __device__ __forceinline__ uint32_t id_bits(const uint4 &v, int k)
 {
     if constexpr (Elt<DT>::EPV == 8) {
-        bits = h ? (wd >> 16) : (wd & 0xffffu);
-        return __uint_as_float(bits << 16);
+        const uint32_t wd = word_of(v, k >> 1);
+        return (k & 1) ? (wd >> 16) : (wd & 0xffffu);
     } else {
-        bits = 0;
-        return __uint_as_float(wd);
+        return word_of(v, k);
     }
 }
 
-// The side test of the fp64 pass: id v is on the residual's positive side when
-// e_p(v) cp_r > e_q(v) cq_r, with cp_r, cq_r the reciprocal sums it sorts with (the statistics'
-// approximate ones, or in a second pass the exact ones).  An id whose two sides agree within
-// EXACT_NEAR (|x - y| <= EXACT_NEAR y) may be sorted differently by the exact sums; its draft
-// mass e_q is summed so that the error of such ids can be bounded once the exact sums are known.
-constexpr double EXACT_NEAR = 1.0 / 65536.0;
-
-// What one thread accumulates in the fp64 pass: per vector slot (unit) the sums A, B of e_p and
-// e_q over its ids on the positive side; over all its ids the sums of e_p, e_q, and the draft
-// mass of the ids near the threshold.
-struct ExactAcc {
-    double a[NV_EXACT], b[NV_EXACT];
-    double tp, tq, near;
-};
-
-__device__ __forceinline__ void exact_add(ExactAcc &acc, int i, double ep, double eq, double cp_r,
-                                          double cq_r)
+// One id of the lane by the general path (ids >= V add nothing).
+template <int DT, int MODE>
+__device__ __forceinline__ void exact_slow_vec(const ExactRows &x, int V, int e0, const uint4 &vp,
+                                               const uint4 &vq, ExactLoc &l)
 {
-    const double xp = ep * cp_r, yq = eq * cq_r;
-    const double m = xp > yq ? 1.0 : 0.0;
-    const double nr = fabs(xp - yq) <= EXACT_NEAR * yq ? 1.0 : 0.0;
-    acc.a[i] = __builtin_fma(ep, m, acc.a[i]);
-    acc.b[i] = __builtin_fma(eq, m, acc.b[i]);
-    acc.near = __builtin_fma(eq, nr, acc.near);
-    acc.tp += ep;
-    acc.tq += eq;
+    constexpr int E = Elt<DT>::EPV;
+    constexpr int KU = (E == 4) ? 4 : 1;  // float32 unrolled: its word index would come from memory
+#pragma unroll KU
+    for (int k = 0; k < E; ++k) {
+        if (e0 + k < V) {
+            double a, b;
+            exact_terms<DT, MODE>(id_bits<DT>(vp, k), id_bits<DT>(vq, k), x, a, b);
+            exact_acc(a, b, l);
+        }
+    }
 }
 
-// Vector i of this thread in iteration it: ids it * CE + (i * TAIL_WG + t) * E + [0, E), the
-// fp32 row pass's layout (a wave's loads 1 KiB contiguous), loaded nontemporally through the
-// rows' buffer resources (past V they read zeros, which the caller never uses).
-template <int DT>
-__device__ __forceinline__ void exact_fetch(const ExactRows &x, int it, uint4 (&rp)[NV_EXACT],
-                                            uint4 (&rq)[NV_EXACT])
+// A step weighed id by id, for one lane: the wave vectors vw0 .. vw0 + NV_EXACT - 1 (ids >= V
+// add nothing), from the fetched words when the step is whole, else by element loads.  Out of
+// line for bfloat16 rows, where only a step with a value outside the tables (or the row's end,
+// or an unaligned row) takes it: the fast path then keeps its registers.
+template <int DT, int MODE>
+__device__ __forceinline__ ExactLoc exact_step_ids(const ExactRows &x, int V, int vw0, bool whole,
+                                                   const uint4 (&rp)[NV_EXACT],
+                                                   const uint4 (&rq)[NV_EXACT])
 {
-    constexpr int E = Elt<DT>::EPV, BY = Elt<DT>::BYTES, CE = TAIL_WG * NV_EXACT * E;
-    const int vo = (it * CE + (int)threadIdx.x * E) * BY;
+    constexpr int E = Elt<DT>::EPV, WV = 64 * E;
+    const int lane = threadIdx.x & 63;
+    ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < NV_EXACT; ++i) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(x.b0, vo + i * TAIL_WG * E * BY, 0, 2);
-        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(x.b1, vo + i * TAIL_WG * E * BY, 0, 2);
-        rp[i] = make_uint4(v.x, v.y, v.z, v.w);
-        rq[i] = make_uint4(u.x, u.y, u.z, u.w);
+        const int e0 = (vw0 + i) * WV + lane * E;
+        if (e0 >= V)
+            continue;
+        const uint4 vp = whole ? rp[i] : exact_words<DT>(x.p0, x.al, e0, V);
+        const uint4 vq = whole ? rq[i] : exact_words<DT>(x.p1, x.al, e0, V);
+        exact_slow_vec<DT, MODE>(x, V, e0, vp, vq, l);
     }
+    return l;
 }
 
-// One fp64 pass over iterations first, first + step, ... of row L and the draft row L.  Unit
-// u = (it * NV_EXACT + i) * TAIL_WAVES + w (wave w's vector slot i of iteration it, 64 * EPV
-// contiguous ids; unit order is id order) gets units[2u] = A, units[2u+1] = B; acc holds this
-// thread's totals.  Whole vectors of bfloat16 rows whose tables serve are formed without
-// branches (every table lookup of the vector, then the arithmetic; an id outside the tables reads
-// a -0.0 sentinel and adds nothing there, and a loop that a lane enters only if it holds such an
-// id adds it by exp2); float32 rows, unaligned rows and the vectors at the end of the row go id
-// by id.  The next iteration's rows are loaded while this one is weighed.
-template <int DT, int MODE>
-__device__ inline void exact_pass(const ExactRows &x, int V, int first, int step, double cp_r,
-                                  double cq_r, double *units, ExactAcc &acc)
+__device__ __forceinline__ void exact_merge(const ExactLoc &l, double &A, double &B, ExactLoc &tot)
 {
-    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_EXACT * E;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int nit = (V + CE - 1) / CE;
-    const bool tabled = (DT == 1) && exact_rows_tabled<MODE>(x);
-    acc.tp = acc.tq = acc.near = 0.0;
-    uint4 rp[NV_EXACT], rq[NV_EXACT], np[NV_EXACT], nq[NV_EXACT];
-    if (first < nit && x.al)
-        exact_fetch<DT>(x, first, rp, rq);
-    for (int it = first; it < nit; it += step) {
-        if (it + step < nit && x.al)  // the next iteration's words, in flight meanwhile
-            exact_fetch<DT>(x, it + step, np, nq);
+    A += l.A;
+    B += l.B;
+    tot.tp += l.tp;
+    tot.tq += l.tq;
+    tot.near += l.near;
+}
+
+// steps of a segment whose words are in registers at once: EXACT_BUFS - 1 in flight while one
+// is weighed (float32 rows, whose exp2 needs more registers per id, keep one in flight)
+template <int DT> constexpr int exact_bufs() { return 2; }
+static_assert((MAX_VOCAB + 64 * 8 - 1) / (64 * 8) <= 64 * TAIL_WAVES * NV_EXACT,
+              "a bfloat16 segment has at most 64 steps (one bit each)");
+
+// One segment s by one wave: the lane's positive-side sums (A, B) of the segment, and its
+// totals added to tot.  float32 rows weigh every id with exp2.  For bfloat16 rows with tables a
+// whole step runs without branches; a step in which the lane read a sentinel (its sums turned
+// NaN), and the steps at the row's end or of an unaligned row, only set the step's bit, and
+// after the segment the lane weighs those steps id by id (out of the loop, so that the loop
+// keeps its registers for words in flight).  The buffers rotate through an unrolled loop.
+template <int DT, int MODE>
+__device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom &gm, int s,
+                                     double &A, double &B, ExactLoc &tot,
+                                     const uint4 (&p0)[NV_EXACT], const uint4 (&q0)[NV_EXACT],
+                                     bool pre)
+{
+    constexpr int WV = 64 * Elt<DT>::EPV;
+    const int vbase = s * gm.nsub, nst = gm.nst;
+    A = 0.0;
+    B = 0.0;
+    uint64_t redo = 0;  // bfloat16: steps to weigh id by id
+    constexpr int EXACT_BUFS = exact_bufs<DT>();
+    uint4 bp[EXACT_BUFS][NV_EXACT], bq[EXACT_BUFS][NV_EXACT];
+    if (x.al) {
 #pragma unroll
-        for (int i = 0; i < NV_EXACT; ++i) {
-            acc.a[i] = 0.0;
-            acc.b[i] = 0.0;
-        }
-        bool miss = false;
-        const int last0 = it * CE + ((NV_EXACT - 1) * TAIL_WG + t) * E;  // this thread's last vector
-        if (tabled && x.al && last0 + E <= V) {
-            if constexpr (DT == 1) {
+        for (int k = 0; k < EXACT_BUFS - 1; ++k) {
+            if (k == 0 && pre) {  // the caller's early fetch of step 0
 #pragma unroll
                 for (int i = 0; i < NV_EXACT; ++i) {
-                    const uint32_t wpv[4] = {rp[i].x, rp[i].y, rp[i].z, rp[i].w};
-                    const uint32_t wqv[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
-                    double pv[8], qv[8];
-                    bool mk[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const uint32_t bp = (k & 1) ? (wpv[k >> 1] >> 16) : (wpv[k >> 1] & 0xffffu);
-                        const uint32_t bq = (k & 1) ? (wqv[k >> 1] >> 16) : (wqv[k >> 1] & 0xffffu);
-                        const int kp = tab_slot(bp), kq = tab_slot(bq);
-                        qv[k] = x.tq[kq];
-                        if constexpr (MODE == SAMPLING) {
-                            pv[k] = x.tp[kp];
-                            mk[k] = false;
-                        } else {
-                            const double f = x.tp[kp], g = x.tn[kq];
-                            mk[k] = neg_zero(f) | neg_zero(g);
-                            pv[k] = (f * g) * x.kc;
-                        }
-                    }
-                    // an id with a value outside the tables adds nothing here: the loop below
-                    // adds both its terms
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        mk[k] = mk[k] | neg_zero(qv[k]);
-                        if constexpr (MODE == SAMPLING)
-                            mk[k] = mk[k] | neg_zero(pv[k]);
-                        miss = miss | mk[k];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        exact_add(acc, i, mk[k] ? 0.0 : pv[k], mk[k] ? 0.0 : qv[k], cp_r, cq_r);
+                    bp[0][i] = p0[i];
+                    bq[0][i] = q0[i];
                 }
+            } else if (k < nst) {
+                exact_fetch<DT>(x, vbase + k * NV_EXACT, bp[k], bq[k]);
             }
-        } else {
-            // id by id (float32 unrolled, as its word index would otherwise come from memory)
-            constexpr int KU = (E == 4) ? 4 : 1;
+        }
+    }
+    for (int j0 = 0; j0 < nst; j0 += EXACT_BUFS) {
 #pragma unroll
-            for (int i = 0; i < NV_EXACT; ++i) {
-                const int v0 = it * CE + (i * TAIL_WG + t) * E;
-                uint4 wp4, wq4;
-                if (x.al) {
-                    wp4 = rp[i];
-                    wq4 = rq[i];
-                } else {  // an unaligned row: element by element
-                    uint4 tmp[NV_EXACT];
-                    exact_load<DT>(x.p0, false, v0, V, tmp);
-                    wp4 = tmp[0];
-                    exact_load<DT>(x.p1, false, v0, V, tmp);
-                    wq4 = tmp[0];
-                }
-#pragma unroll KU
-                for (int k = 0; k < E; ++k) {
-                    const int id = v0 + k;
-                    const uint32_t wp = word_of(wp4, (E == 8) ? (k >> 1) : k);
-                    const uint32_t wq = word_of(wq4, (E == 8) ? (k >> 1) : k);
-                    uint32_t bp, bq;
-                    const float pv = word_value<DT>(wp, (E == 8) ? (k & 1) : 0, bp);
-                    const float qv = word_value<DT>(wq, (E == 8) ? (k & 1) : 0, bq);
-                    double ep = 0.0, eq = 0.0;
-                    if (id < V)
-                        exact_terms<DT, MODE>(pv, qv, bp, bq, x, ep, eq);
-                    exact_add(acc, i, ep, eq, cp_r, cq_r);
+        for (int k = 0; k < EXACT_BUFS; ++k) {
+            const int j = j0 + k;
+            if (j < nst) {
+                // step j + EXACT_BUFS - 1 goes to the buffer that step j - 1 has freed
+                const int kf = (k + EXACT_BUFS - 1) % EXACT_BUFS;  // constant once unrolled
+                if (j + EXACT_BUFS - 1 < nst && x.al)
+                    exact_fetch<DT>(x, vbase + (j + EXACT_BUFS - 1) * NV_EXACT, bp[kf], bq[kf]);
+                const int vw0 = vbase + j * NV_EXACT;
+                const bool whole = x.al && (vw0 + NV_EXACT) * WV <= V;
+                if constexpr (DT == 1) {
+                    bool ok = false;
+                    if (x.tabled && whole) {
+                        ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                        for (int i = 0; i < NV_EXACT; ++i)
+                            exact_fast_vec<MODE>(bp[k][i], bq[k][i], x.tab, l);
+                        ok = !__builtin_isnan(l.tp) && !__builtin_isnan(l.tq);
+                        // selects, not a branch: a branch would let the compiler defer the
+                        // sums it guards and keep every looked-up term live until the test
+                        A = ok ? A + l.A : A;
+                        B = ok ? B + l.B : B;
+                        tot.tp = ok ? tot.tp + l.tp : tot.tp;
+                        tot.tq = ok ? tot.tq + l.tq : tot.tq;
+                        tot.near = ok ? tot.near + l.near : tot.near;
+                    }
+                    if (!ok)
+                        redo |= 1ull << j;
+                } else {
+                    exact_merge(exact_step_ids<DT, MODE>(x, V, vw0, whole, bp[k], bq[k]), A, B,
+                                tot);
                 }
             }
         }
-        if constexpr (DT == 1) {
-            if (miss) {  // ids outside the tables (values near 0 or beyond 2^8): rare
-#pragma unroll
-                for (int i = 0; i < NV_EXACT; ++i)
-#pragma unroll 1
-                    for (int k = 0; k < 8; ++k) {
-                        const uint32_t wp = word_of(rp[i], k >> 1), wq = word_of(rq[i], k >> 1);
-                        const uint32_t bp = (k & 1) ? (wp >> 16) : (wp & 0xffffu);
-                        const uint32_t bq = (k & 1) ? (wq >> 16) : (wq & 0xffffu);
-                        double ep, eq;
-                        if (!table_terms<MODE>(bp, bq, x, ep, eq)) {
-                            direct_terms<DT, MODE>(__uint_as_float(bp << 16),
-                                                   __uint_as_float(bq << 16), x, ep, eq);
-                            exact_add(acc, i, ep, eq, cp_r, cq_r);
-                        }
-                    }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NV_EXACT; ++i) {
-            const double A = wave_sum_lds(acc.a[i]), B = wave_sum_lds(acc.b[i]);
-            if (lane == 0) {
-                const int u = (it * NV_EXACT + i) * TAIL_WAVES + w;
-                units[2 * u] = A;
-                units[2 * u + 1] = B;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NV_EXACT; ++i) {
-            rp[i] = np[i];
-            rq[i] = nq[i];
+    }
+    if constexpr (DT == 1) {
+        while (redo) {  // rare: values outside the tables, the row's end, an unaligned row
+            const int j = __builtin_ctzll(redo);
+            redo &= redo - 1;
+            const uint4 none[NV_EXACT] = {};
+            exact_merge(exact_step_ids<DT, MODE>(x, V, vbase + j * NV_EXACT, false, none, none),
+                        A, B, tot);
         }
     }
 }
 
-// the weight of one id in the fp64 draw: max(0, e_p / S_p - e_q / S_q) on the positive side of
-// the pass's side test, else 0
+// The fp64 pass over segments s_first + w, s_first + w + 16, ... below s_end (w the wave):
+// units[2 s] = A, units[2 s + 1] = B of each, and the thread's totals in tot.  pre: p0, q0
+// hold the first segment's step 0, fetched by the caller.
 template <int DT, int MODE>
-__device__ __forceinline__ double exact_weight(float pv, float qv, uint32_t bp, uint32_t bq,
-                                               const ExactRows &x, double cp_r, double cq_r,
-                                               double np_r, double nq_r)
+__device__ inline void exact_pass(const ExactRows &x, int V, const ExactGeom &gm, int s_first,
+                                  int s_end, double *units, ExactLoc &tot,
+                                  const uint4 (&p0)[NV_EXACT], const uint4 (&q0)[NV_EXACT],
+                                  bool pre)
 {
-    double ep, eq;
-    exact_terms<DT, MODE>(pv, qv, bp, bq, x, ep, eq);
-    if (!(ep * cp_r > eq * cq_r))
-        return 0.0;
-    const double d = ep * np_r - eq * nq_r;
-    return d > 0.0 ? d : 0.0;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    tot = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int s = s_first + w; s < s_end; s += TAIL_WAVES) {
+        double A, B;
+        exact_segment<DT, MODE>(x, V, gm, s, A, B, tot, p0, q0, pre && s == s_first + w);
+        A = wave_sum(A);
+        B = wave_sum(B);
+        if (lane == 0) {
+            units[2 * s] = A;
+            units[2 * s + 1] = B;
+        }
+    }
 }
 
-// Wave 0 inside unit `unit` of the fp64 pass: lane l weighs the unit's vector l (exact_weight,
-// with the side test of the pass that produced the unit sums), a wave scan from `base` finds the
-// lane, and the lane walks its ids again with the same instructions: the first id whose running
-// weight exceeds tt (fb: the last id of positive weight).
+// The draw weights of the lane's E ids of wave vector vw: max(0, a / S_a - b / S_b) for ids
+// on the positive side of the pass's side test (a > b), else 0; ids >= V weigh 0.
 template <int DT, int MODE>
-__device__ inline void exact_search(const ExactRows &x, int V, double cp_r, double cq_r,
-                                    double np_r, double nq_r, int unit, double base, double tt,
-                                    bool fb, int32_t *out)
+__device__ __forceinline__ void exact_vec_weights(const ExactRows &x, int V, int vw, double ia,
+                                                  double ib, double (&wv)[Elt<DT>::EPV])
 {
-    constexpr int E = Elt<DT>::EPV, CE = TAIL_WG * NV_EXACT * E;
-    const int lane = threadIdx.x & 63;
-    const int it = unit / (NV_EXACT * TAIL_WAVES), rem = unit - it * (NV_EXACT * TAIL_WAVES);
-    const int i = rem / TAIL_WAVES, ww = rem - i * TAIL_WAVES;
-    const int e0 = it * CE + i * TAIL_WG * E + (ww * 64 + lane) * E;
-    uint4 rp[NV_EXACT], rq[NV_EXACT];
-    exact_load<DT>(x.p0, x.al, e0, V, rp);
-    exact_load<DT>(x.p1, x.al, e0, V, rq);
-    double wv[E];
-    double vs = 0.0;
+    constexpr int E = Elt<DT>::EPV;
+    const int e0 = vw * 64 * E + (int)(threadIdx.x & 63) * E;
+    const uint4 vp = exact_words<DT>(x.p0, x.al, e0, V), vq = exact_words<DT>(x.p1, x.al, e0, V);
 #pragma unroll
     for (int k = 0; k < E; ++k) {
-        const uint32_t wp = word_of(rp[0], (E == 8) ? (k >> 1) : k);
-        const uint32_t wq = word_of(rq[0], (E == 8) ? (k >> 1) : k);
-        uint32_t bp, bq;
-        const float pv = word_value<DT>(wp, (E == 8) ? (k & 1) : 0, bp);
-        const float qv = word_value<DT>(wq, (E == 8) ? (k & 1) : 0, bq);
-        wv[k] = (e0 + k < V) ? exact_weight<DT, MODE>(pv, qv, bp, bq, x, cp_r, cq_r, np_r, nq_r)
-                             : 0.0;
-        vs += wv[k];
+        wv[k] = 0.0;
+        if (e0 + k < V) {
+            double a, b;
+            exact_terms<DT, MODE>(id_bits<DT>(vp, k), id_bits<DT>(vq, k), x, a, b);
+            const double d = a * ia - b * ib;
+            wv[k] = (a > b && d > 0.0) ? d : 0.0;
+        }
     }
-    const double inc = wave_incl_scan(vs);
-    const double exc = wave_excl_from_incl(inc);
-    const double bt = base + exc;
-    const unsigned long long hit = __ballot(!fb && vs > 0.0 && bt + vs > tt);
-    const unsigned long long pos = __ballot(vs > 0.0);
-    if (pos == 0) {  // a unit of positive weight has an id of positive weight: not reached
+}
+
+// The weights of the wave vectors of segment s, by the waves in turn: sub[j] = the sum over
+// wave vector s * nsub + j.  Wave w keeps its lanes' id weights of vector w in wv.
+template <int DT, int MODE>
+__device__ inline void exact_sub_sums(const ExactRows &x, int V, const ExactGeom &gm, int s,
+                                      double ia, double ib, double *sub,
+                                      double (&wv)[Elt<DT>::EPV])
+{
+    constexpr int E = Elt<DT>::EPV;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+        wv[k] = 0.0;
+    for (int j = w; j < gm.nsub; j += TAIL_WAVES) {
+        double wt[E];
+        exact_vec_weights<DT, MODE>(x, V, s * gm.nsub + j, ia, ib, wt);
+        double vs = 0.0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            vs += wt[k];
+            if (j == w)
+                wv[k] = wt[k];
+        }
+        vs = wave_sum(vs);
         if (lane == 0)
-            *out = -1;
-        return;
+            sub[j] = vs;
     }
-    const bool fb2 = fb || hit == 0;
-    const int owner = fb2 ? 63 - __builtin_clzll(pos) : __builtin_ctzll(hit);
+}
+
+// One wave, for at most 64 segments: the weights A / S_a - B / S_b (clamped at 0) from the
+// unit sums, their running totals, W, tt = u01 * W and the first segment whose running total
+// exceeds tt (else, rounding at u near 1, the last of positive weight: fb = 1; -1 if W = 0),
+// as find_unit_block leaves them; readable after the next barrier.
+__device__ inline void find_segment_wave(const double *units, int nseg, double ia, double ib,
+                                         float u01, int *s_unit, double *s_base, double *s_t,
+                                         int *s_fb, double *s_W)
+{
+    const int lane = threadIdx.x & 63;
+    double wk = 0.0;
+    if (lane < nseg) {
+        const double d = units[2 * lane] * ia - units[2 * lane + 1] * ib;
+        wk = d > 0.0 ? d : 0.0;
+    }
+    const double inc = wave_incl_scan(wk);
+    const double exc = wave_excl_from_incl(inc);
+    const double W = lane_value(inc, 63), tt = (double)u01 * W;
+    const unsigned long long hm = __ballot(W > 0.0 && wk > 0.0 && exc + wk > tt);
+    const unsigned long long pm = __ballot(wk > 0.0);
+    const int lh = hm ? __builtin_ctzll(hm) : 0, lp = pm ? 63 - __builtin_clzll(pm) : 0;
+    const double bh = lane_value(exc, lh), bl = lane_value(exc, lp);
+    if (lane == 0) {
+        *s_unit = hm ? lh : (pm ? lp : -1);
+        *s_base = hm ? bh : (pm ? bl : 0.0);
+        *s_t = tt;
+        *s_fb = hm ? 0 : 1;
+        *s_W = W;
+    }
+}
+
+// Wave 0: among the nsub vector weights of the chosen segment (from `base`), the first whose
+// running total exceeds tt (unless fb), else the last of positive weight: its index, starting
+// total and whether it is a fallback go to s_pick (-1: no vector of the segment has weight, a
+// segment whose weight is rounding alone, misclassified ids only, about 1e-16 of W).
+__device__ inline void exact_pick_vector(const double *sub, int nsub, double base, double tt,
+                                         bool fb, int *s_j, double *s_b, int *s_f)
+{
+    const int lane = threadIdx.x & 63;
+    double carry = base, hb = 0.0, lb = 0.0;
+    int hit = -1, lastp = -1;
+    for (int j0 = 0; j0 < nsub; j0 += 64) {
+        const int j = j0 + lane;
+        const double wj = (j < nsub) ? sub[j] : 0.0;
+        const double sc = wave_incl_scan(wj);
+        const double inc = sc + carry, exc = wave_excl_from_incl(sc) + carry;
+        const unsigned long long hm = __ballot(!fb && wj > 0.0 && inc > tt);
+        const unsigned long long pm = __ballot(wj > 0.0);
+        if (hit < 0 && hm) {
+            const int l = __builtin_ctzll(hm);
+            hit = j0 + l;
+            hb = lane_value(exc, l);
+        }
+        if (pm) {
+            const int l = 63 - __builtin_clzll(pm);
+            lastp = j0 + l;
+            lb = lane_value(exc, l);
+        }
+        carry = lane_value(inc, 63);
+    }
+    if (lane == 0) {
+        const bool f = fb || hit < 0;
+        *s_j = f ? lastp : hit;
+        *s_b = f ? lb : hb;
+        *s_f = f ? 1 : 0;
+    }
+}
+
+// One wave inside wave vector vw with its lanes' id weights wv: the lane by a wave scan from
+// `base`, and the id by the lane's walk (the first id whose running weight exceeds tt; fb: the
+// last id of positive weight).
+template <int DT>
+__device__ inline void exact_pick_id(const double (&wv)[Elt<DT>::EPV], int vw, double base,
+                                     double tt, bool fb, int32_t *out)
+{
+    constexpr int E = Elt<DT>::EPV;
+    const int lane = threadIdx.x & 63;
+    double vs = 0.0;
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+        vs += wv[k];
+    const double inc = wave_incl_scan(vs);
+    const double bt = base + wave_excl_from_incl(inc);
+    const unsigned long long hl = __ballot(!fb && vs > 0.0 && bt + vs > tt);
+    const unsigned long long pl = __ballot(vs > 0.0);
+    const bool fb3 = fb || hl == 0;
+    // the vector's weight is the sum of these lane sums, so some lane has weight
+    const int owner = fb3 ? (pl ? 63 - __builtin_clzll(pl) : 63) : __builtin_ctzll(hl);
     if (lane != owner)
         return;
+    const int e0 = vw * 64 * E + lane * E;
     double run = bt;
-    int y = -1, lastpos = -1;
+    int y = -1, lastid = -1;
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         if (wv[k] > 0.0) {
             run += wv[k];
-            lastpos = e0 + k;
-            if (!fb2 && y < 0 && run > tt)
+            lastid = e0 + k;
+            if (!fb3 && y < 0 && run > tt)
                 y = e0 + k;
         }
     }
-    *out = (y >= 0) ? y : lastpos;
+    *out = (y >= 0) ? y : lastid;
 }
 
 // The block's sums of three per-thread values, in a fixed order (wave sums, then the waves in
@@ -1792,23 +1994,25 @@ __device__ inline void target_law_draw(const DrawRows &r, const SeqInfo &si, int
 // accept phase (merge, gather, accept tests, L: the same decisions in every one; the first
 // writes the outputs).  A draw from p_L alone (L = K, and the sampler) is made by the first
 // workgroup from one chunk of the row (chunk_draw).  A residual draw (L < K) runs the fp64 pass
-// over row L and the draft row L, iterations g, g + split, ..., into per-unit fp64 sums in LDS.
-// With one workgroup it then forms S_p, S_q and the unit weights, finds the unit holding
-// t = u_K * W and the id inside it.  With several, each copies its unit sums to the workspace
-// (device-coherent stores, waited for) and counts itself in; the last to arrive reads the
-// others' sums (device-coherent loads), resets the count and draws.  If the residual is empty
-// in fp64, that workgroup draws from p_L over the whole row.  LDS: the fp64 tables (bfloat16,
-// static); dynamic: the staged partials during the accept phase, the unit sums afterwards.
+// over row L and the draft row L, workgroup g's waves taking segments 16 g .. 16 g + 15, into
+// per-segment fp64 sums.  With one workgroup it then forms the sums S_a, S_b and the segment
+// weights, finds the segment holding t = u_K * W, the wave vector in it and the id.  With
+// several, each copies its segment sums to the workspace (device-coherent stores, waited for)
+// and counts itself in; the last to arrive reads the others' sums (device-coherent loads),
+// resets the count and draws.  If the residual is empty in fp64, that workgroup draws from p_L
+// over the whole row.  LDS: the fp64 tables (bfloat16, static, at address 0); dynamic: the
+// staged partials during the accept phase, then the unit sums of a draw from p_L or the
+// segment sums of the residual draw.
 template <int DT, int MODE, bool SPLIT>
 __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
 {
+    // the fp64 tables first, at LDS address 0 (see tab_at); then the dynamic LDS
+    constexpr int NTAB = (DT == 1) ? 2 * TAB_DOUBLES : 1;
+    __shared__ __attribute__((aligned(65536))) double s_tab[NTAB];
     extern __shared__ double dyn[];
-    constexpr int NTAB = (DT == 1) ? (MODE == CONTRASTIVE ? 3 : 2) * TAB_STRIDE : 1;
-    __shared__ double s_tab[NTAB];
     __shared__ SeqInfo s_info;
     __shared__ int s_unit, s_fb, s_last;
     __shared__ double s_base, s_t, s_W, s_S[3];
-    constexpr int E = Elt<DT>::EPV;
     // SPLIT: a.split workgroups share each sequence; else one, and this compiles to the plain
     // single-workgroup pass
     const int G = SPLIT ? a.split : 1, K = a.K, V = a.V;
@@ -1829,46 +2033,61 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     const float u01 = a.unif[(size_t)b * (K + 1) + K];
     int32_t *out = a.out_tokens + (size_t)b * (K + 1) + si.L;
     float *out_prob = a.draw_probs ? a.draw_probs + b : nullptr;
-    double *units = dyn;
     if (!r.resid) {  // w = p_L: one chunk of the row is read again, not the whole row
         if (SPLIT && g != 0)
             return;
         if ((a.flags & TEST_CHUNK_FALLBACK) ||
-            !chunk_draw<DT, MODE>(a, r, si, b, u01, units, out, out_prob))
-            target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
+            !chunk_draw<DT, MODE>(a, r, si, b, u01, dyn, out, out_prob))
+            target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, dyn, out, out_prob);
         return;
     }
 
     // ---- the residual draw, in fp64
-    ExactRows x = {r.p0, r.p1, r.b0, r.b1, r.al, si.Mp, si.Mq, a.sp.c, a.sq.c, 0.0,
-                   nullptr, nullptr, nullptr};
-    if constexpr (DT == 1) {
-        exact_tables<MODE>(x, s_tab);
-        __syncthreads();
+    const ExactGeom gm = exact_geom<DT>(V, G);
+    // LDS (dynamic): 2 nseg unit sums, then nsub vector weights
+    double *units = dyn;
+    ExactRows x;
+    x.p0 = r.p0;
+    x.p1 = r.p1;
+    x.b0 = r.b0;
+    x.b1 = r.b1;
+    x.al = r.al;
+    x.Mp = si.Mp;
+    x.Mq = si.Mq;
+    x.cp = a.sp.c;
+    x.cq = a.sq.c;
+    x.r = si.Sq / si.Sp;  // sorted with the statistics' approximate sums
+    x.tabled = (DT == 1) && exact_tabled<MODE>(si.Mp, x.cp, x.cq);
+    x.tab = reinterpret_cast<const char *>(s_tab);
+    // this wave's first step, loaded while the tables are built
+    uint4 p0[NV_EXACT], q0[NV_EXACT];
+    const bool pre = x.al && g * TAIL_WAVES + w < gm.nseg;
+    if (pre)
+        exact_fetch<DT>(x, (g * TAIL_WAVES + w) * gm.nsub, p0, q0);
+    if (DT == 1 && x.tabled) {
+        exact_tables<MODE>(x, s_tab, 3);
+        lds_barrier();
     }
-    constexpr int CE2 = TAIL_WG * NV_EXACT * E;
-    const int nit = (V + CE2 - 1) / CE2, nu = nit * NV_EXACT * TAIL_WAVES;
-    // sorted with the statistics' approximate sums (see the section's notes)
-    const double cp0 = 1.0 / si.Sp, cq0 = 1.0 / si.Sq;
-    ExactAcc acc;
-    exact_pass<DT, MODE>(x, V, g, G, cp0, cq0, units, acc);
-    block_sum3(acc.tp, acc.tq, acc.near, s_S);
+    ExactLoc tot;
+    exact_pass<DT, MODE>(x, V, gm, g * TAIL_WAVES, (g + 1) * TAIL_WAVES, units, tot, p0, q0,
+                         pre);
+    block_sum3(tot.tp, tot.tq, tot.near, s_S);
     __syncthreads();
+    const int nseg = gm.nseg;
     if (SPLIT) {
-        // gunits of sequence b: 2 sums per unit, then 3 totals per workgroup
+        // gunits of sequence b: 2 sums per segment, then 3 totals per workgroup
         double *gu = a.gunits + (size_t)b * a.nu_stride;
+        constexpr int OWN = 2 * TAIL_WAVES;  // this workgroup's segment sums
         if (w == 0) {
             // The sums go out as device-coherent stores, and the wave waits until they are
             // acknowledged before it counts in, so a workgroup that sees the count complete
             // reads every share with device-coherent loads.  (A device fence would also write
             // back the whole L2, which costs more than the draw.)
-            constexpr int PER_IT = 2 * NV_EXACT * TAIL_WAVES;  // doubles per iteration
-            for (int it = g; it < nit; it += G)
-                for (int k = lane; k < PER_IT; k += 64)
-                    __hip_atomic_store(gu + it * PER_IT + k, units[it * PER_IT + k],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane < OWN)
+                __hip_atomic_store(gu + g * OWN + lane, units[g * OWN + lane], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             if (lane < 3)
-                __hip_atomic_store(gu + 2 * nu + 3 * g + lane, s_S[lane], __ATOMIC_RELAXED,
+                __hip_atomic_store(gu + 2 * nseg + 3 * g + lane, s_S[lane], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             int last = 0;
@@ -1884,79 +2103,104 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
         __syncthreads();
         if (!s_last)
             return;
-        constexpr int PER_IT = 2 * NV_EXACT * TAIL_WAVES;
-        for (int k = t; k < 2 * nu; k += TAIL_WG)
-            if ((k / PER_IT) % G != g)
+        for (int k = t; k < 2 * nseg; k += TAIL_WG)
+            if (k / OWN != g)
                 units[k] = __hip_atomic_load(gu + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (t == 0) {  // the totals of every workgroup, in workgroup order
-            double tot[3] = {0.0, 0.0, 0.0};
+            double tt3[3] = {0.0, 0.0, 0.0};
             for (int v = 0; v < G; ++v)
                 for (int k = 0; k < 3; ++k)
-                    tot[k] += (v == g) ? s_S[k]
-                                       : __hip_atomic_load(gu + 2 * nu + 3 * v + k, __ATOMIC_RELAXED,
+                    tt3[k] += (v == g) ? s_S[k]
+                                       : __hip_atomic_load(gu + 2 * nseg + 3 * v + k,
+                                                           __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);
-            s_S[0] = tot[0];
-            s_S[1] = tot[1];
-            s_S[2] = tot[2];
+            s_S[0] = tt3[0];
+            s_S[1] = tt3[1];
+            s_S[2] = tt3[2];
         }
         __syncthreads();
     }
-    const double Sp = s_S[0], Sq = s_S[1], near_q = s_S[2];
-    if (!(Sp > 0.0) || !(Sq > 0.0)) {  // a row without finite logits: outside the contract
+    double Sa = s_S[0], Sb = s_S[1];
+    const double near_b = s_S[2];
+    if (!(Sa > 0.0) || !(Sb > 0.0)) {  // a row without finite logits: outside the contract
         __syncthreads();
-        target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
+        target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, dyn, out, out_prob);
         return;
     }
-    const double np_r = 1.0 / Sp, nq_r = 1.0 / Sq;
-    // unit weights A / S_p - B / S_q, compacted to one double per unit
-    static_assert((MAX_VOCAB + TAIL_WG * NV_EXACT * 4 - 1) / (TAIL_WG * NV_EXACT * 4) * NV_EXACT *
-                          TAIL_WAVES <= 4 * TAIL_WG,
-                  "each thread converts at most four units");
-    double cp_r = cp0, cq_r = cq0;
+    static_assert(16 * TAIL_MAX_SPLIT <= TAIL_WG, "one thread per segment");
+    double ia = 1.0 / Sa, ib = 1.0 / Sb;
     for (int pass = 0; pass < 2; ++pass) {
-        double wk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = t + j * TAIL_WG;
-            const double d = (k < nu) ? units[2 * k] * np_r - units[2 * k + 1] * nq_r : 0.0;
-            wk[j] = d > 0.0 ? d : 0.0;
+        // the segment weights A / S_a - B / S_b and the segment holding t
+        if (nseg <= 64) {
+            if (w == 0)
+                find_segment_wave(units, nseg, ia, ib, u01, &s_unit, &s_base, &s_t, &s_fb, &s_W);
+        } else {  // compacted to one double per segment, then the whole workgroup's search
+            double wk = 0.0;
+            if (t < nseg) {
+                const double d = units[2 * t] * ia - units[2 * t + 1] * ib;
+                wk = d > 0.0 ? d : 0.0;
+            }
+            __syncthreads();
+            if (t < nseg)
+                units[t] = wk;
+            __syncthreads();
+            find_unit_block(units, nseg, u01, &s_unit, &s_base, &s_t, &s_fb, &s_W);
         }
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = t + j * TAIL_WG;
-            if (k < nu)
-                units[k] = wk[j];
-        }
-        __syncthreads();
-        find_unit_block(units, nu, u01, &s_unit, &s_base, &s_t, &s_fb, &s_W);
-        __syncthreads();
-        // The approximate sums may sort an id differently from the exact ones only if its two
-        // sides agree within rel = |theta~/theta - 1|; each such id moves the weights by at most
-        // rel (1 + rel) e_q / S_q.  Keep the draw when those ids' draft mass bounds the error far
-        // below the decision scale, else sort again with the exact sums.
-        const double rel = fabs((si.Sp * Sq) / (si.Sq * Sp) - 1.0);
-        const bool sure = pass == 1 || (rel <= 0.5 * EXACT_NEAR &&
-                                        rel * (1.0 + rel) * near_q * nq_r <= 0x1p-24 * s_W &&
+        // An id may be sorted differently by the exact sums only if a / b lies between 1 and
+        // theta = S_a / S_b; each such id moves the weights by at most rel (1 + rel) b / S_b.
+        // Keep the draw when the near ids' draft mass bounds that far below the decision scale,
+        // else sort again with r from the exact sums (a' = a S_b / S_a against b).
+        const double rel = fabs(Sa * ib - 1.0);
+        const bool sure = pass == 1 || (rel <= NEAR_REL &&
+                                        rel * (1.0 + rel) * near_b * ib <= 0x1p-24 * s_W &&
                                         !(a.flags & TEST_EXACT_TWO_PASS));
         if (sure)
             break;
-        cp_r = np_r;
-        cq_r = nq_r;
-        exact_pass<DT, MODE>(x, V, 0, 1, cp_r, cq_r, units, acc);
+        x.r *= Sb * ia;
+        if (DT == 1 && x.tabled) {
+            exact_tables<MODE>(x, s_tab, 1);
+            __syncthreads();
+        }
+        exact_pass<DT, MODE>(x, V, gm, 0, nseg, units, tot, p0, q0, false);
+        block_sum3(tot.tp, tot.tq, tot.near, s_S);
         __syncthreads();
+        Sa = s_S[0];
+        Sb = s_S[1];
+        ia = 1.0 / Sa;
+        ib = 1.0 / Sb;
     }
     if (s_unit >= 0) {
+        // the segment holding t, then its wave vector (each wave weighs one and keeps its
+        // lanes' id weights), then the lane and the id
+        const int s = s_unit;
+        const double tt = s_t;
+        double *sub = units + 2 * nseg;
+        double wv[Elt<DT>::EPV];
+        exact_sub_sums<DT, MODE>(x, V, gm, s, ia, ib, sub, wv);
+        __syncthreads();
         if (w == 0)
-            exact_search<DT, MODE>(x, V, cp_r, cq_r, np_r, nq_r, s_unit, s_base, s_t, s_fb != 0,
-                                   out);
+            exact_pick_vector(sub, gm.nsub, s_base, tt, s_fb != 0, &s_unit, &s_base, &s_fb);
+        __syncthreads();
+        const int jv = s_unit;
+        if (jv < 0) {  // see exact_pick_vector: the segment's first id
+            if (t == 0)
+                *out = min(s * gm.nsub * 64 * Elt<DT>::EPV, V - 1);
+            return;
+        }
+        if (w == (jv < TAIL_WAVES ? jv : 0)) {
+            if (jv >= TAIL_WAVES)  // a vector no wave kept: weigh it again
+                exact_vec_weights<DT, MODE>(x, V, s * gm.nsub + jv, ia, ib, wv);
+            exact_pick_id<DT>(wv, s * gm.nsub + jv, s_base, tt, s_fb != 0, out);
+        }
         return;
     }
     // every weight is 0 in fp64 as well: the residual is empty; draw from p_L
     __syncthreads();
-    target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, units, out, out_prob);
+    target_law_draw<DT, MODE>(r, si, V, u01, a.sp, a.sq, dyn, out, out_prob);
 }
+
 
 // ------------------------------------------------------------------ early-exit verify
 //
@@ -2491,17 +2735,18 @@ __global__ __launch_bounds__(TAIL_WG) void k_quantile_cut(const float *__restric
 namespace {
 
 // Workgroups per sequence for the tail: enough to give every compute unit a share of the
-// draws when the batch is small (at most TAIL_MAX_SPLIT, at most one per pass iteration, and
-// only for batches the workspace's unit-sum buffer holds).
+// draws when the batch is small (at most TAIL_MAX_SPLIT, at most one per step of the fp64
+// pass, and only for batches the workspace's unit-sum buffer holds).
 int tail_split(const Workspace &ws, int dtype, int B, int V)
 {
     if (B < 1 || B > ws.split_batch)
         return 1;
-    const int ce = TAIL_WG * NV_EXACT * elems_per_vec(dtype);  // iterations of the fp64 pass
-    const int nit = (V + ce - 1) / ce;
+    // steps of NV_EXACT wave vectors of a workgroup's 16 waves in the fp64 pass
+    const int wv = 64 * elems_per_vec(dtype), per = TAIL_WAVES * NV_EXACT;
+    const int nst = ((V + wv - 1) / wv + per - 1) / per;
     int g = ws.num_cus / B;
     g = g < TAIL_MAX_SPLIT ? g : TAIL_MAX_SPLIT;
-    g = g < nit ? g : nit;
+    g = g < nst ? g : nst;
     return g > 1 ? g : 1;
 }
 
