@@ -122,6 +122,28 @@ int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, in
                             float *out_probs);
 
 /*
+ * Sampling verify that allocates nothing, for callers that cannot call hipMalloc: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layouts, arithmetic and results as specverify_run_sampling, without a context: it runs on
+ * the calling thread's current device, and its workspace is a file-scope device array of
+ * SPECVERIFY_STATIC_SCRATCH_BYTES per device (held until the process ends; its address is
+ * taken on the first call on each device).  A call needs B * (2K+1) * ceil(V / chunk) * 32
+ * bytes of it for the row statistics (chunk = 8192 bfloat16 or 4096 float32 ids), plus about
+ * 2.3 KB per sequence when B is at most half the device's compute units; larger inputs
+ * return SPECVERIFY_ECAPACITY before any GPU work.  Every call on a device shares its array:
+ * calls that overlap on one device (other streams, other threads) race and must be ordered
+ * by the caller.  The statistics partials are rewritten and the arrival counts cleared by
+ * each call (a kernel, not a memset, so a captured graph replays it).  Errors as
+ * specverify_run_sampling (capacity: the array's size, SPECVERIFY_MAX_K, SPECVERIFY_MAX_VOCAB).
+ */
+#define SPECVERIFY_STATIC_SCRATCH_BYTES (4 << 20)
+int specverify_run_sampling_static(void *hip_stream, int dtype, int B, int K, int V,
+                                   float temperature, const void *target_logits,
+                                   const void *draft_logits, const int32_t *draft_tokens,
+                                   const float *uniforms, int32_t *accepted_len,
+                                   int32_t *out_tokens, float *out_probs);
+
+/*
  * Sampling verify with early exit: accepted_len and out_tokens exactly as
  * specverify_run_sampling (same arithmetic, same decisions), but a sequence's rows after its
  * first rejection are not read, since the tokens after that rejection are discarded

@@ -26,6 +26,7 @@ SPECVERIFY_ECAPACITY = -5
 
 SPECVERIFY_MAX_K = 63
 SPECVERIFY_MAX_VOCAB = 1 << 20
+SPECVERIFY_STATIC_SCRATCH_BYTES = 4 << 20
 SPECVERIFY_MAX_CUT_N = 8192
 SPECVERIFY_NUM_KERNELS = 7
 SPECVERIFY_TEST_CHUNK_FALLBACK = 1
@@ -65,6 +66,9 @@ def load():
         lib.specverify_run_sampling.restype = i
         lib.specverify_run_sampling_early_exit.argtypes = lib.specverify_run_sampling.argtypes
         lib.specverify_run_sampling_early_exit.restype = i
+        lib.specverify_run_sampling_static.argtypes = [vp, i, i, i, i, f, vp, vp, vp, vp, vp, vp,
+                                                       vp]
+        lib.specverify_run_sampling_static.restype = i
         lib.specverify_run_contrastive.argtypes = [vp, vp, i, i, i, i, f, vp, vp, vp, vp, vp, vp,
                                                    vp]
         lib.specverify_run_contrastive.restype = i
@@ -148,6 +152,15 @@ def specverify_run_sampling(ctx, stream, dtype, B, K, V, temperature, target_log
         ctx, _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
         _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
         _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling")
+
+
+def specverify_run_sampling_static(stream, dtype, B, K, V, temperature, target_logits,
+                                   draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
+                                   out_probs=None) -> None:
+    _check(load().specverify_run_sampling_static(
+        _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
+        _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling_static")
 
 
 def specverify_run_sampling_early_exit(ctx, stream, dtype, B, K, V, temperature, target_logits,

@@ -35,6 +35,8 @@ constexpr int NK = SPECVERIFY_NUM_KERNELS;
 static_assert(NK == sv::NUM_KINDS, "kernel kinds out of step with the header");
 static_assert(SPECVERIFY_MAX_CUT_N == sv::MAX_CUT_N, "cut capacity out of step with the header");
 static_assert(SPECVERIFY_MAX_VOCAB == sv::MAX_VOCAB, "vocabulary cap out of step with the header");
+static_assert(SPECVERIFY_STATIC_SCRATCH_BYTES == sv::STATIC_SCRATCH_BYTES,
+              "scratch size out of step with the header");
 static_assert(SPECVERIFY_TEST_CHUNK_FALLBACK == sv::TEST_CHUNK_FALLBACK &&
                   SPECVERIFY_TEST_EXACT_TWO_PASS == sv::TEST_EXACT_TWO_PASS,
               "test flags out of step with the header");
@@ -245,6 +247,72 @@ int specverify_run_sampling(specverify_ctx *ctx, void *hip_stream, int dtype, in
     return run_sampling_like(ctx, hip_stream, sv::SAMPLING, dtype, B, K, V, temperature,
                              target_logits, draft_logits, draft_tokens, uniforms, accepted_len,
                              out_tokens, out_probs, false);
+}
+
+int specverify_run_sampling_static(void *hip_stream, int dtype, int B, int K, int V,
+                                   float temperature, const void *target_logits,
+                                   const void *draft_logits, const int32_t *draft_tokens,
+                                   const float *uniforms, int32_t *accepted_len,
+                                   int32_t *out_tokens, float *out_probs)
+{
+    // the checks of specverify_run_sampling, with the scratch array's size as the capacity
+    if (dtype != SPECVERIFY_F32 && dtype != SPECVERIFY_BF16)
+        return SPECVERIFY_EUNSUPPORTED;
+    if (B < 0 || K < 0 || V < 1 || bad_temperature(temperature))
+        return SPECVERIFY_EINVAL;
+    if (K > SPECVERIFY_MAX_K || V > SPECVERIFY_MAX_VOCAB ||
+        (B > 0 && largest_launch(B, K, V) > MAX_ITEMS))
+        return SPECVERIFY_ECAPACITY;
+    if (B > 0 && (!target_logits || !uniforms || !accepted_len || !out_tokens ||
+                  (K > 0 && (!draft_logits || !draft_tokens))))
+        return SPECVERIFY_EINVAL;
+    const size_t es = dtype == SPECVERIFY_BF16 ? 2 : 4;
+    if (!aligned_to(target_logits, es) || (draft_logits && !aligned_to(draft_logits, es)) ||
+        (draft_tokens && !aligned_to(draft_tokens, 4)) || !aligned_to(uniforms, 4) ||
+        !aligned_to(accepted_len, 4) || !aligned_to(out_tokens, 4) ||
+        (out_probs && !aligned_to(out_probs, 4)))
+        return SPECVERIFY_EINVAL;
+    // the scratch layout: the statistics' partials, then (a draw shared by several workgroups,
+    // B <= compute units / 2) the segment sums and arrival counts of each sequence
+    const size_t nch = (size_t)sv::num_chunks(sv::NV_STATS, dtype, V);
+    const size_t b_part = align_up((size_t)B * (2 * (size_t)K + 1) * nch * sv::WAVES * sizeof(float2));
+    const int nu_stride = 2 * sv::EXACT_MAX_SEGS + 3 * sv::TAIL_MAX_SPLIT;
+    if (b_part > sv::STATIC_SCRATCH_BYTES)
+        return SPECVERIFY_ECAPACITY;
+    if (B == 0)
+        return SPECVERIFY_OK;
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return SPECVERIFY_EHIP;
+    const bool split = B <= cus / 2;
+    const size_t b_gu = split ? align_up((size_t)B * nu_stride * sizeof(double)) : 0;
+    const size_t b_gc = split ? align_up((size_t)B * sizeof(int)) : 0;
+    if (b_part + b_gu + b_gc > sv::STATIC_SCRATCH_BYTES)
+        return SPECVERIFY_ECAPACITY;
+    void *base = nullptr;
+    if (sv::static_scratch(dev, &base) != hipSuccess)
+        return SPECVERIFY_EHIP;
+    char *p = static_cast<char *>(base);
+    sv::Workspace ws = {};
+    ws.part = reinterpret_cast<float2 *>(p);
+    ws.gunits = split ? reinterpret_cast<double *>(p + b_part) : nullptr;
+    ws.gcount = split ? reinterpret_cast<int *>(p + b_part + b_gu) : nullptr;
+    ws.split_batch = split ? B : 0;
+    ws.nu_stride = nu_stride;
+    ws.num_cus = cus;
+    ws.test_flags = 0;
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    // the arrival counts must start at 0; the array keeps whatever the last call left
+    if (split && sv::launch_zero_ints(st, ws.gcount, B) != hipSuccess)
+        return SPECVERIFY_EHIP;
+    const sv::Scale sc = sv::make_scale((double)temperature);
+    sv::Launch ln{st, nullptr, 0u};
+    const hipError_t e = sv::launch_sampling(ln, ws, sv::SAMPLING, dtype, B, K, V, sc, sc,
+                                             target_logits, draft_logits, draft_tokens, uniforms,
+                                             accepted_len, out_tokens, out_probs, nullptr);
+    return e == hipSuccess ? SPECVERIFY_OK : SPECVERIFY_EHIP;
 }
 
 int specverify_run_contrastive(specverify_ctx *ctx, void *hip_stream, int dtype, int B, int K,

@@ -175,6 +175,16 @@ hipError_t launch_greedy_heads(const Launch &ln, const Workspace &ws, int dtype,
 hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const float *scores,
                                float *r_cut, uint8_t *keep, int32_t *n_keep);
 
+// The workspace of the entry point that allocates nothing: a file-scope device array of
+// STATIC_SCRATCH_BYTES per device (see static_scratch in the kernels' source).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(4) << 20;
+constexpr int STATIC_SCRATCH_DEVICES = 64;
+// The device address of the current device's scratch array, taken once per device with
+// hipGetSymbolAddress (device: the current device's index).
+hipError_t static_scratch(int device, void **ptr);
+// n ints from p set to 0 by a small kernel (capturable in a HIP graph, unlike a memset node)
+hipError_t launch_zero_ints(hipStream_t stream, int *p, int n);
+
 hipError_t launch_greedy(const Launch &ln, const Workspace &ws, int dtype, int B, int K, int V,
                          const void *tgt, const int32_t *props, int32_t *acc_len,
                          int32_t *out_tokens);

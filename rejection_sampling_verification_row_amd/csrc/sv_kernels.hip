@@ -30,6 +30,9 @@
 #include <math.h>
 #include <hip/hip_ext.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -2962,6 +2965,53 @@ hipError_t launch_quantile_cut(const Launch &ln, int P, int N, int k, const floa
 {
     SV_LAUNCH(ln, KIND_CUT, k_quantile_cut, dim3(P), dim3(TAIL_WG), (size_t)N * sizeof(uint32_t),
               scores, N, k, r_cut, keep, n_keep);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ static scratch
+//
+// The workspace of specverify_run_sampling_static, for callers that cannot allocate: one
+// array per device, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory, so host code uses only the address hipGetSymbolAddress returns
+// for the current device, taken once per device and kept.
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex scratch_mu;
+std::atomic<void *> scratch_at[STATIC_SCRATCH_DEVICES];
+}  // namespace
+
+hipError_t static_scratch(int device, void **ptr)
+{
+    if (device < 0 || device >= STATIC_SCRATCH_DEVICES)
+        return hipErrorInvalidDevice;
+    void *p = scratch_at[device].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_at[device].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (!p)
+                return hipErrorInvalidSymbol;
+            scratch_at[device].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+__global__ __launch_bounds__(WG) void k_zero_ints(int *p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += WG)
+        p[i] = 0;
+}
+
+hipError_t launch_zero_ints(hipStream_t stream, int *p, int n)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(WG), 0, stream, p, n);
     return hipGetLastError();
 }
 

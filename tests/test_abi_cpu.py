@@ -88,11 +88,33 @@ def test_capacity_beyond_one_dispatch_is_rejected_on_the_host():
         lib.specverify_destroy(h)
 
 
+def test_static_entry_point_checks_on_the_host():
+    """The sampling verify that allocates nothing checks its arguments, and whether its
+    partials fit the scratch array, before it asks for a device: without a GPU these return
+    their codes.  No call here passes every check: the stand-in addresses must never reach a
+    kernel, on this machine or on one with a GPU."""
+    lib = sv.load()
+    f = lib.specverify_run_sampling_static
+    ok_ptr = 256  # aligned stand-in addresses: never dereferenced on these paths
+    args = lambda dtype, B, K, V, t=1.0: (None, dtype, B, K, V, t) + (ok_ptr,) * 6 + (None,)
+    assert f(*args(sv.SPECVERIFY_BF16, -1, 1, 8)) == sv.SPECVERIFY_EINVAL
+    assert f(*args(sv.SPECVERIFY_BF16, 1, 1, 8, 0.0)) == sv.SPECVERIFY_EINVAL
+    assert f(*args(5, 1, 1, 8)) == sv.SPECVERIFY_EUNSUPPORTED
+    assert f(*args(sv.SPECVERIFY_BF16, 1, 64, 8)) == sv.SPECVERIFY_ECAPACITY
+    assert f(*args(sv.SPECVERIFY_BF16, 1, 1, sv.SPECVERIFY_MAX_VOCAB + 1)) == sv.SPECVERIFY_ECAPACITY
+    # partials: B * (2K+1) * chunks * 32 bytes; 4096 x 17 x 16 chunks of bfloat16 ids > 4 MiB
+    assert f(*args(sv.SPECVERIFY_BF16, 4096, 8, 128256)) == sv.SPECVERIFY_ECAPACITY
+    assert f(*args(sv.SPECVERIFY_BF16, 0, 8, 128256)) == sv.SPECVERIFY_OK   # nothing to do
+    assert f(None, sv.SPECVERIFY_BF16, 2, 1, 8, 1.0, ok_ptr + 1, *((ok_ptr,) * 5), None) == \
+        sv.SPECVERIFY_EINVAL                                                   # misaligned
+
+
 def test_binding_constants_match_the_header():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (SPECVERIFY_\w+) (.+)", text))
     assert eval(defs["SPECVERIFY_MAX_K"]) == sv.SPECVERIFY_MAX_K
     assert eval(defs["SPECVERIFY_MAX_VOCAB"]) == sv.SPECVERIFY_MAX_VOCAB
+    assert eval(defs["SPECVERIFY_STATIC_SCRATCH_BYTES"]) == sv.SPECVERIFY_STATIC_SCRATCH_BYTES
     assert eval(defs["SPECVERIFY_NUM_KERNELS"]) == sv.SPECVERIFY_NUM_KERNELS == len(sv.KERNEL_NAMES)
     for k in ("SPECVERIFY_TEST_CHUNK_FALLBACK", "SPECVERIFY_TEST_EXACT_TWO_PASS"):
         assert int(defs[k].rstrip("u")) == getattr(sv, k), k
@@ -141,6 +163,11 @@ int main(void)
     EXPECT(specverify_profile_end(NULL, NULL, NULL), SPECVERIFY_EINVAL);
     EXPECT(specverify_workspace_bytes(NULL), 0);
     EXPECT(specverify_set_test_flags(NULL, SPECVERIFY_TEST_EXACT_TWO_PASS), SPECVERIFY_EINVAL);
+    /* the context-free entry point: its argument checks come before any device call */
+    EXPECT(specverify_run_sampling_static(NULL, SPECVERIFY_BF16, 1, 1, 8, 1.0f, NULL, NULL, NULL,
+                                          NULL, NULL, NULL, NULL), SPECVERIFY_EINVAL);
+    EXPECT(specverify_run_sampling_static(NULL, 7, 1, 1, 8, 1.0f, NULL, NULL, NULL, NULL, NULL,
+                                          NULL, NULL), SPECVERIFY_EUNSUPPORTED);
     EXPECT(specverify_destroy(NULL), SPECVERIFY_OK);
     if (specverify_strerror(SPECVERIFY_EINVAL) == NULL || ctx != NULL)
         bad |= 1 << k;
