@@ -8,9 +8,11 @@ call over the whole batch (row statistics, then accept + first-reject scan + res
 draw).  Inputs sit in HBM before timing starts and alternate between two copies so that no
 step reads logits the previous one left in the 256 MB last-level cache.
 
-Prints one JSON line: verified draft positions/s (B*K per step), the dominant kernel's
-bytes/s against the 8 TB/s HBM peak (HIP events attached to that kernel's dispatch on the
-call's stream, in about 25 steps spread over the timed loop: every 40th of the default 1000),
+Prints one JSON line: verified draft positions/s (B*K per step, from the wall clock over
+back-to-back calls with no events in them), per-call p10 / median / p90 (HIP events around
+each call, in a pass of its own), the dominant kernel's bytes/s against the 8 TB/s HBM peak
+(HIP events attached to that kernel's dispatch on the call's stream, at least 25 launches in
+a pass of their own: every 40th of 1000 calls by default),
 the fp64 CPU oracle timed on a bounded sample of the same batch (on one thread, then on all
 host threads up to 16), and a check of the GPU's outputs for the whole batch against that
 oracle run.
@@ -66,8 +68,8 @@ WORKLOADS = {
                  "row_stats", "k_pairs_prefix<bf16> (row pairs 0-1 of every sequence)",
                  "prefix_pairs_bf16_B128_K4_V152064_traffic.md"),
 }
-TIMING_STRIDE = 8   # the dominant kernel is timed in steps 0, 8, 16, ... of the timed loop
-TIMED_LAUNCHES = 25  # ... or, in longer runs, in about this many steps spread over the loop
+TIMING_STRIDE = 8   # the dominant kernel is timed in calls 0, 8, 16, ... of its pass
+TIMED_LAUNCHES = 25  # ... at least this many launches (spread further in longer runs)
 
 
 def timing_stride(steps: int) -> int:
@@ -96,6 +98,50 @@ def preheat(step, sync, seconds: float = PREHEAT_SECONDS) -> int:
         sync()
         if time.perf_counter() >= t_end:
             return n
+
+
+def timed_passes(args, step, ctx, kind, sv, torch):
+    """The passes after the wall-clock loop, each after a preheat that brings the clocks back
+    up from the idle wait at the end of the previous one:
+    - the dominant kernel's durations: HIP events attached to its dispatch, on the call's
+      stream, in every stride-th of max(steps, 25 * stride) calls (at least 25 launches; a
+      timed dispatch costs the call a few microseconds, so the events stay out of the
+      wall-clock loop);
+    - per-call times: a pair of events around each of max(steps, 100) calls (their marker
+      packets sit between calls, not between a call's kernels), for p10 / median / p90;
+    - the per-kernel breakdown: every kernel of every 8th of 160 calls.
+    Returns (dominant-kernel durations ms, per-kind sums ms, per-kind counts, stride,
+    per-call ms, breakdown sums ms, breakdown counts)."""
+    stride = timing_stride(args.steps)
+    n_k = max(args.steps, TIMED_LAUNCHES * stride)
+    preheat(step, torch.cuda.synchronize)
+    sv.specverify_profile_begin(ctx, n_k, [kind], stride=stride)
+    for i in range(n_k):
+        step(i)
+    torch.cuda.synchronize()
+    kdur = sv.specverify_profile_launches(ctx, kind)
+    kms, kn = sv.specverify_profile_end(ctx)
+
+    n_c = max(args.steps, 100)
+    preheat(step, torch.cuda.synchronize)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_c)]
+    for i in range(n_c):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+
+    nb = 20 * TIMING_STRIDE
+    preheat(step, torch.cuda.synchronize)
+    sv.specverify_profile_begin(ctx, (nb + TIMING_STRIDE - 1) // TIMING_STRIDE,
+                                stride=TIMING_STRIDE)
+    for i in range(nb):
+        step(i)
+    torch.cuda.synchronize()
+    bms, bn = sv.specverify_profile_end(ctx)
+    return kdur, kms, kn, stride, call_ms, bms, bn
 
 
 def log(msg):
@@ -130,7 +176,7 @@ def measured_traffic(name):
 
 
 def percentiles(ms: list) -> dict:
-    """p10, median and p90 of the timed launches' durations (ms), by linear interpolation."""
+    """p10, median and p90 of durations (ms), by linear interpolation."""
     if not ms:
         return {"p10_ms": None, "median_ms": None, "p90_ms": None}
     xs = sorted(ms)
@@ -378,31 +424,15 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
-    # HIP events on the dominant kernel's dispatch, on the call's stream, in every
-    # timing_stride-th timed step (a timed dispatch costs a few microseconds more)
-    stride = timing_stride(args.steps)
-    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=stride)
+    # the headline: wall clock over back-to-back calls with no events anywhere
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kdur = sv.specverify_profile_launches(ctx, kind)
-    kms, kn = sv.specverify_profile_end(ctx)
     mean_L = float(acc.float().mean().item())
-    # per-kernel breakdown from a separate pass that times every kernel of every 8th call, as
-    # the timed loop times the dominant one (events on every call slow the kernels down), after
-    # calls that bring the clocks back up from the idle wait at the end of the timed loop
-    nb = min(args.steps, 20 * TIMING_STRIDE)
-    for i in range(min(args.warmup, 60)):
-        step(i)
-    sv.specverify_profile_begin(ctx, (nb + TIMING_STRIDE - 1) // TIMING_STRIDE,
-                                stride=TIMING_STRIDE)
-    for i in range(nb):
-        step(i)
-    torch.cuda.synchronize()
-    bms, bn = sv.specverify_profile_end(ctx)
+    kdur, kms, kn, stride, call_ms, bms, bn = timed_passes(args, step, ctx, kind, sv, torch)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -451,8 +481,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic type of the dominant kernel (bfloat16 logits are widened to fp32);
+        # the accept tests and the draw compute in fp64; config.logits is the input type
         "dtype": "f32",
         "data": "synthetic",
+        "per_call_ms": {**percentiles(call_ms), "calls": len(call_ms),
+                        "how": "HIP events around each call in a pass of its own"},
         "config": {"workload": desc, "mode": w.mode, "B": B, "K": K, "V": V,
                    "logits": synth.DTYPE_NAMES[w.dtype], "temperature": w.temperature,
                    "seed": w.seed},
@@ -505,16 +539,13 @@ def bench_cut(args, desc, kind, kname):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    stride = timing_stride(args.steps)
-    sv.specverify_profile_begin(ctx, args.steps, [kind], stride=stride)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kdur = sv.specverify_profile_launches(ctx, kind)
-    kms, kn = sv.specverify_profile_end(ctx)
+    kdur, kms, kn, stride, call_ms, _, _ = timed_passes(args, step, ctx, kind, sv, torch)
     sv.specverify_destroy(ctx)
     gcut, gkeep, gn = cut.cpu().numpy(), keep.cpu().numpy(), n.cpu().numpy()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -525,6 +556,8 @@ def bench_cut(args, desc, kind, kname):
         "unit": "prompts/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "per_call_ms": {**percentiles(call_ms), "calls": len(call_ms),
+                        "how": "HIP events around each call in a pass of its own"},
         "config": {"workload": desc, "P": P, "N": N, "alpha": w.alpha, "seed": w.seed},
         "roofline": {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

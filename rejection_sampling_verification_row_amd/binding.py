@@ -44,8 +44,13 @@ class SpecVerifyError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, specverify_strerror(status), status))
 
 
+# Another build of the same sources may be loaded instead (the sanitizer run of the CPU tests
+# builds the host code with AddressSanitizer and UndefinedBehaviorSanitizer).
+_LIB_OVERRIDE = os.environ.get("SPECVERIFY_LIB")
+
+
 def library_path() -> str:
-    return _build.LIB
+    return _LIB_OVERRIDE or _build.LIB
 
 
 def load():
@@ -54,9 +59,9 @@ def load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_build.LIB):
+        if not _LIB_OVERRIDE and not os.path.exists(_build.LIB):
             _build.build(force=True)
-        lib = ctypes.CDLL(_build.LIB)
+        lib = ctypes.CDLL(library_path())
         vp, i, f, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
         lib.specverify_create.argtypes = [ctypes.POINTER(vp), i, i, i, i]
         lib.specverify_create.restype = i
@@ -115,6 +120,51 @@ def _ptr(x):
     raise TypeError("expected a torch tensor, an int device address or None, got %r" % type(x))
 
 
+_ITEMSIZE = {"i32": 4, "f32": 4, "u8": 1}
+
+
+def _ptrs(*specs):
+    """The pointers of a call's array arguments, each spec (x, count, kind, name): every tensor
+    is first checked against the call's shape (_arr), then converted (_ptr)."""
+    for x, count, kind, name in specs:
+        _arr(x, count, kind, name)
+    return tuple(_ptr(x) for x, _, _, _ in specs)
+
+
+def _arr(x, count: int, kind, name: str):
+    """Check a tensor argument against the call's shape: its element type (kind: "i32", "f32",
+    "u8", or a logits dtype SPECVERIFY_F32 / SPECVERIFY_BF16) and at least `count` elements,
+    so that no kernel reads or writes past it.  Plain integer addresses are not checked: their
+    extent is the caller's to guarantee."""
+    if x is None or isinstance(x, int) or not hasattr(x, "data_ptr"):
+        return
+    import torch
+    if kind in (SPECVERIFY_F32, SPECVERIFY_BF16):
+        ok = ({torch.float32} if kind == SPECVERIFY_F32
+              else {torch.bfloat16, torch.int16, torch.uint16})
+        what = "float32" if kind == SPECVERIFY_F32 else "bfloat16 (or its 16-bit patterns)"
+    else:
+        ok = {"i32": {torch.int32}, "f32": {torch.float32}, "u8": {torch.uint8, torch.bool}}[kind]
+        what = {"i32": "int32", "f32": "float32", "u8": "uint8"}[kind]
+    if x.dtype not in ok:
+        raise ValueError("%s: expected %s elements, got %s" % (name, what, x.dtype))
+    if x.numel() < max(int(count), 0):
+        raise ValueError("%s: needs at least %d elements for this call, has %d"
+                         % (name, count, x.numel()))
+
+
+def _verify_args(dtype, B, K, V, target, draft, tokens, uniforms, acc, out, probs, draft_rows):
+    """The pointers of a sampling or contrastive verify call, checked against B, K and V
+    (draft_rows: K for sampling, K + 1 for contrastive)."""
+    return _ptrs((target, B * (K + 1) * V, dtype, "target/expert logits"),
+                 (draft, B * draft_rows * V, dtype, "draft/amateur logits"),
+                 (tokens, B * K, "i32", "draft_tokens"),
+                 (uniforms, B * (K + 1), "f32", "uniforms"),
+                 (acc, B, "i32", "accepted_len"),
+                 (out, B * (K + 1), "i32", "out_tokens"),
+                 (probs, B * K * 2, "f32", "out_probs"))
+
+
 def _stream(s):
     if isinstance(s, int):
         return s
@@ -148,81 +198,96 @@ def specverify_workspace_bytes(ctx: int) -> int:
 def specverify_run_sampling(ctx, stream, dtype, B, K, V, temperature, target_logits,
                             draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
                             out_probs=None) -> None:
-    _check(load().specverify_run_sampling(
-        ctx, _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
-        _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling")
+    ptrs = _verify_args(dtype, B, K, V, target_logits, draft_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, out_probs, K)
+    _check(load().specverify_run_sampling(ctx, _stream(stream), dtype, B, K, V,
+                                          float(temperature), *ptrs), "specverify_run_sampling")
 
 
 def specverify_run_sampling_static(stream, dtype, B, K, V, temperature, target_logits,
                                    draft_logits, draft_tokens, uniforms, accepted_len, out_tokens,
                                    out_probs=None) -> None:
-    _check(load().specverify_run_sampling_static(
-        _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
-        _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling_static")
+    ptrs = _verify_args(dtype, B, K, V, target_logits, draft_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, out_probs, K)
+    _check(load().specverify_run_sampling_static(_stream(stream), dtype, B, K, V,
+                                                 float(temperature), *ptrs),
+           "specverify_run_sampling_static")
 
 
 def specverify_run_sampling_early_exit(ctx, stream, dtype, B, K, V, temperature, target_logits,
                                        draft_logits, draft_tokens, uniforms, accepted_len,
                                        out_tokens, out_probs=None) -> None:
-    _check(load().specverify_run_sampling_early_exit(
-        ctx, _stream(stream), dtype, B, K, V, float(temperature), _ptr(target_logits),
-        _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_sampling_early_exit")
+    ptrs = _verify_args(dtype, B, K, V, target_logits, draft_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, out_probs, K)
+    _check(load().specverify_run_sampling_early_exit(ctx, _stream(stream), dtype, B, K, V,
+                                                     float(temperature), *ptrs),
+           "specverify_run_sampling_early_exit")
 
 
 def specverify_run_contrastive(ctx, stream, dtype, B, K, V, tau, expert_logits, amateur_logits,
                                draft_tokens, uniforms, accepted_len, out_tokens,
                                out_probs=None) -> None:
-    _check(load().specverify_run_contrastive(
-        ctx, _stream(stream), dtype, B, K, V, float(tau), _ptr(expert_logits),
-        _ptr(amateur_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_contrastive")
+    ptrs = _verify_args(dtype, B, K, V, expert_logits, amateur_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, out_probs, K + 1)
+    _check(load().specverify_run_contrastive(ctx, _stream(stream), dtype, B, K, V, float(tau),
+                                             *ptrs), "specverify_run_contrastive")
 
 
 def specverify_run_contrastive_early_exit(ctx, stream, dtype, B, K, V, tau, expert_logits,
                                           amateur_logits, draft_tokens, uniforms, accepted_len,
                                           out_tokens, out_probs=None) -> None:
-    _check(load().specverify_run_contrastive_early_exit(
-        ctx, _stream(stream), dtype, B, K, V, float(tau), _ptr(expert_logits),
-        _ptr(amateur_logits), _ptr(draft_tokens), _ptr(uniforms), _ptr(accepted_len),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_run_contrastive_early_exit")
+    ptrs = _verify_args(dtype, B, K, V, expert_logits, amateur_logits, draft_tokens, uniforms,
+                        accepted_len, out_tokens, out_probs, K + 1)
+    _check(load().specverify_run_contrastive_early_exit(ctx, _stream(stream), dtype, B, K, V,
+                                                        float(tau), *ptrs),
+           "specverify_run_contrastive_early_exit")
 
 
 def specverify_run_greedy(ctx, stream, dtype, B, K, V, target_logits, proposals, accepted_len,
                           out_tokens) -> None:
     _check(load().specverify_run_greedy(
-        ctx, _stream(stream), dtype, B, K, V, _ptr(target_logits), _ptr(proposals),
-        _ptr(accepted_len), _ptr(out_tokens)), "specverify_run_greedy")
+        ctx, _stream(stream), dtype, B, K, V,
+        *_ptrs((target_logits, B * (K + 1) * V, dtype, "target_logits"),
+               (proposals, B * K, "i32", "proposals"), (accepted_len, B, "i32", "accepted_len"),
+               (out_tokens, B * (K + 1), "i32", "out_tokens"))), "specverify_run_greedy")
 
 
 def specverify_run_greedy_early_exit(ctx, stream, dtype, B, K, V, target_logits, proposals,
                                      accepted_len, out_tokens) -> None:
     _check(load().specverify_run_greedy_early_exit(
-        ctx, _stream(stream), dtype, B, K, V, _ptr(target_logits), _ptr(proposals),
-        _ptr(accepted_len), _ptr(out_tokens)), "specverify_run_greedy_early_exit")
+        ctx, _stream(stream), dtype, B, K, V,
+        *_ptrs((target_logits, B * (K + 1) * V, dtype, "target_logits"),
+               (proposals, B * K, "i32", "proposals"), (accepted_len, B, "i32", "accepted_len"),
+               (out_tokens, B * (K + 1), "i32", "out_tokens"))),
+        "specverify_run_greedy_early_exit")
 
 
 def specverify_sample(ctx, stream, dtype, N, V, temperature, logits, uniforms, out_tokens,
                       out_probs=None) -> None:
     _check(load().specverify_sample(
-        ctx, _stream(stream), dtype, N, V, float(temperature), _ptr(logits), _ptr(uniforms),
-        _ptr(out_tokens), _ptr(out_probs)), "specverify_sample")
+        ctx, _stream(stream), dtype, N, V, float(temperature),
+        *_ptrs((logits, N * V, dtype, "logits"), (uniforms, N, "f32", "uniforms"),
+               (out_tokens, N, "i32", "out_tokens"), (out_probs, N, "f32", "out_probs"))),
+        "specverify_sample")
 
 
 def specverify_run_greedy_heads(ctx, stream, dtype, B, K, H, V, logits, proposals, accepted_len,
                                 out_tokens, next_proposals=None) -> None:
     _check(load().specverify_run_greedy_heads(
-        ctx, _stream(stream), dtype, B, K, H, V, _ptr(logits), _ptr(proposals),
-        _ptr(accepted_len), _ptr(out_tokens), _ptr(next_proposals)),
+        ctx, _stream(stream), dtype, B, K, H, V,
+        *_ptrs((logits, B * (K + 1) * max(H, 0) * V, dtype, "logits"),
+               (proposals, B * K, "i32", "proposals"), (accepted_len, B, "i32", "accepted_len"),
+               (out_tokens, B * (K + 1), "i32", "out_tokens"),
+               (next_proposals, B * max(H - 1, 0), "i32", "next_proposals"))),
         "specverify_run_greedy_heads")
 
 
 def specverify_quantile_cut(ctx, stream, P, N, alpha, scores, r_cut, keep, n_keep) -> None:
     _check(load().specverify_quantile_cut(
-        ctx, _stream(stream), P, N, float(alpha), _ptr(scores), _ptr(r_cut), _ptr(keep),
-        _ptr(n_keep)), "specverify_quantile_cut")
+        ctx, _stream(stream), P, N, float(alpha),
+        *_ptrs((scores, P * N, "f32", "scores"), (r_cut, P, "f32", "r_cut"),
+               (keep, P * N, "u8", "keep"), (n_keep, P, "i32", "n_keep"))),
+        "specverify_quantile_cut")
 
 
 def specverify_set_test_flags(ctx, flags: int) -> None:

@@ -191,3 +191,43 @@ def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
                     "-L" + libdir, "-lspecverify", "-Wl,-rpath," + libdir], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr)
+
+
+def test_binding_checks_tensor_types_and_sizes_before_any_call():
+    """The Python wrappers check each tensor's element type and size against B, K and V (a
+    short or mistyped tensor would let a kernel read or write past it) and raise ValueError
+    before calling into the library; on this machine the tensors are on the CPU, so a call
+    whose shapes are right stops at the device check instead."""
+    import torch
+    B, K, V = 2, 3, 10
+    ok = dict(tgt=torch.zeros(B * (K + 1) * V, dtype=torch.bfloat16),
+              drf=torch.zeros(B * K * V, dtype=torch.int16),
+              tok=torch.zeros(B * K, dtype=torch.int32),
+              unif=torch.zeros(B * (K + 1), dtype=torch.float32),
+              acc=torch.zeros(B, dtype=torch.int32),
+              out=torch.zeros(B * (K + 1), dtype=torch.int32),
+              probs=torch.zeros(B * K * 2, dtype=torch.float32))
+
+    def call(fn=sv.specverify_run_sampling, **bad):
+        a = dict(ok, **bad)
+        fn(0, 0, sv.SPECVERIFY_BF16, B, K, V, 1.0, a["tgt"], a["drf"], a["tok"], a["unif"],
+           a["acc"], a["out"], a["probs"])
+
+    with pytest.raises(ValueError, match="target"):
+        call(tgt=torch.zeros(B * (K + 1) * V - 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="target"):
+        call(tgt=torch.zeros(B * (K + 1) * V, dtype=torch.float32))   # f32 under dtype bf16
+    with pytest.raises(ValueError, match="draft_tokens"):
+        call(tok=torch.zeros(B * K, dtype=torch.int64))
+    with pytest.raises(ValueError, match="uniforms"):
+        call(unif=torch.zeros(B * K, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_probs"):
+        call(probs=torch.zeros(B * K, dtype=torch.float32))
+    with pytest.raises(ValueError, match="draft/amateur"):   # contrastive: K + 1 amateur rows
+        call(fn=sv.specverify_run_contrastive)
+    with pytest.raises(ValueError, match="device tensor"):   # right shapes, but on the CPU
+        call()
+    with pytest.raises(ValueError, match="keep"):
+        sv.specverify_quantile_cut(0, 0, 2, 5, 0.5, torch.zeros(10), torch.zeros(2),
+                                   torch.zeros(9, dtype=torch.uint8),
+                                   torch.zeros(2, dtype=torch.int32))

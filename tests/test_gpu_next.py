@@ -97,16 +97,26 @@ def test_sampler_matches_verify_with_no_draft(ctx):
     assert np.array_equal(tok, out.cpu().numpy()[:, 0])
 
 
+def _raw(*xs):
+    """Device addresses as plain integers: the binding passes them unchecked, so these tests
+    reach the library's own host-side checks (they refuse before any launch)."""
+    return tuple(x if x is None or isinstance(x, int) else x.data_ptr() for x in xs)
+
+
 def test_sampler_errors(ctx):
     w = synth.make_sampler(2, 10, F32, 1.0, seed=1)
     lg, u = dev(w.target), dev(w.uniforms.reshape(2))
     tok = torch.full((2,), 9, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="logits"):   # the binding: N x V beyond the tensor
+        sv.specverify_sample(ctx, None, F32, 2000, 10, 1.0, lg, u, tok)
+    lg, u, tok_p = _raw(lg, u, tok)
     E = sv.SpecVerifyError
     for args, want in [((F32, 2, 10, 0.0, lg, u, tok), sv.SPECVERIFY_EINVAL),
                        ((F32, 2, 10, 1.0, None, u, tok), sv.SPECVERIFY_EINVAL),
                        ((F32, 2000, 10, 1.0, lg, u, tok), sv.SPECVERIFY_ECAPACITY),
                        ((F32, 2, 200000, 1.0, lg, u, tok), sv.SPECVERIFY_ECAPACITY),
                        ((5, 2, 10, 1.0, lg, u, tok), sv.SPECVERIFY_EUNSUPPORTED)]:
+        args = args[:-1] + (tok_p,)
         with pytest.raises(E) as ei:
             sv.specverify_sample(ctx, None, *args)
         assert ei.value.status == want
@@ -164,6 +174,9 @@ def test_heads_errors(ctx):
     acc = torch.empty(2, dtype=torch.int32, device="cuda")
     tok = torch.empty((2, 3), dtype=torch.int32, device="cuda")
     nxt = torch.empty((2, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="logits"):   # the binding: 17 positions beyond the tensor
+        sv.specverify_run_greedy_heads(ctx, None, F32, 2, 17, 3, 10, lg, x, acc, tok, nxt)
+    lg, x, acc, tok, nxt = _raw(lg, x, acc, tok, nxt)
     E = sv.SpecVerifyError
     for args, want in [((F32, 2, 2, 0, 10, lg, x, acc, tok, nxt), sv.SPECVERIFY_EINVAL),
                        ((F32, 2, 2, 3, 10, lg, x, acc, tok, None), sv.SPECVERIFY_EINVAL),
@@ -218,6 +231,9 @@ def test_cut_errors(ctx):
     cut = torch.empty(2, dtype=torch.float32, device="cuda")
     keep = torch.empty((2, 8), dtype=torch.uint8, device="cuda")
     n = torch.empty(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="scores"):   # the binding: P x N beyond the tensor
+        sv.specverify_quantile_cut(ctx, None, 1 << 22, 8, 0.5, s, cut, keep, n)
+    s, cut, keep, n = _raw(s, cut, keep, n)
     E = sv.SpecVerifyError
     for args, want in [((2, 8, 1.5, s, cut, keep, n), sv.SPECVERIFY_EINVAL),
                        ((2, 8, float("nan"), s, cut, keep, n), sv.SPECVERIFY_EINVAL),

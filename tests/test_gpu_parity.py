@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C-ABI against the CPU oracle (needs an MI355X).
 
-Full-size workloads run exactly as the benchmark launches them; at the two largest sizes
-the oracle checks a seeded sample of sequences (it computes each sequence on its own).
+Full-size workloads run exactly as the benchmark launches them, and the oracle checks every
+sequence of them (one sequence per oracle call, on a pool of threads).
 Smaller shapes span several chunks, ragged tails, misaligned rows and the degenerate cases.
 """
 import json
@@ -271,9 +271,17 @@ def test_capacity_at_the_one_dispatch_limit_is_accepted():
 
 def test_host_side_errors(ctx):
     w = synth.c1_sampling_tiny(B=2, seed=3)
-    t, d, x, u = dev(w.target), dev(w.draft), dev(w.tokens), dev(w.uniforms)
-    acc = torch.empty(2, dtype=torch.int32, device="cuda")
-    tok = torch.full((2, 5), 9, dtype=torch.int32, device="cuda")
+    t_, d_, x_, u_ = dev(w.target), dev(w.draft), dev(w.tokens), dev(w.uniforms)
+    acc_ = torch.empty(2, dtype=torch.int32, device="cuda")
+    tok_ = torch.full((2, 5), 9, dtype=torch.int32, device="cuda")
+    # the binding checks tensors against B, K and V before the library sees them
+    with pytest.raises(ValueError, match="target"):
+        sv.specverify_run_sampling(ctx, None, F32, 2, 17, 1000, 1.0, t_, d_, x_, u_, acc_, tok_)
+    with pytest.raises(ValueError, match="draft_tokens"):
+        sv.specverify_run_sampling(ctx, None, F32, 2, 4, 1000, 1.0, t_, d_, x_.float(), u_, acc_,
+                                   tok_)
+    # plain integer addresses reach the library's own host-side checks
+    t, d, x, u, acc, tok = (a.data_ptr() for a in (t_, d_, x_, u_, acc_, tok_))
     E = sv.SpecVerifyError
 
     def status(fn):
@@ -292,13 +300,13 @@ def test_host_side_errors(ctx):
     assert status(lambda: run_s(ctx, None, F32, 2000, 4, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_ECAPACITY
     assert status(lambda: run_s(ctx, None, F32, -1, 4, 1000, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: run_s(ctx, None, F32, 2, 4, 0, 1.0, t, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
-    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 1.0, t.data_ptr() + 2, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
+    assert status(lambda: run_s(ctx, None, F32, 2, 4, 1000, 1.0, t + 2, d, x, u, acc, tok)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_run_greedy(ctx, None, BF16, 2, 4, 1000, t, None, acc, tok)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_create(0, 0, 4, 10)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_create(0, 4, 64, 10)) == sv.SPECVERIFY_EINVAL
     assert status(lambda: sv.specverify_create(0, 4, 4, sv.SPECVERIFY_MAX_VOCAB + 1)) == sv.SPECVERIFY_EINVAL
     torch.cuda.synchronize()
-    assert torch.all(tok == 9)  # nothing was written by any rejected call
+    assert torch.all(tok_ == 9)  # nothing was written by any rejected call
 
 
 def test_profile_api(ctx):
