@@ -520,16 +520,23 @@ __device__ __forceinline__ Draft gather_draft(const char *tgt, const char *drf,
 // s * 2^((m - M) log2(e)/T).  The NT threads stage the partials in LDS in one coalesced pass
 // when they fit; one wave merges each row, always with the same instructions, so every
 // kernel that merges a row gets the same bits.
-template <int NT>
+// nothing to do while the partials are in flight (see merge_rows)
+struct NoWork {
+    __device__ void operator()() const {}
+};
+
+template <int NT, class Mid = NoWork>
 __device__ __forceinline__ void merge_rows(const float2 *part, int b, int K, int nch, int npos,
                                            const Scale &sp, const Scale &sq, float2 *stage,
-                                           float *sM, double *sS)
+                                           float *sM, double *sS, const Mid &mid = Mid())
 {
     constexpr int NW = NT / 64;
     const int R = 2 * K + 1, np = nch * WAVES, total = R * np;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float2 *pb = part + (size_t)b * total;
     const bool staged = total <= ACCEPT_STAGE;
+    // mid() runs once, by every thread, while the first staging loads are in flight
+    bool done_mid = false;
     if (staged) {
         for (int i0 = 0; i0 < total; i0 += 4 * NT) {
             float2 v[4];
@@ -538,6 +545,10 @@ __device__ __forceinline__ void merge_rows(const float2 *part, int b, int K, int
                 const int i = i0 + k * NT + t;
                 v[k] = (i < total) ? pb[i] : make_float2(0.0f, 0.0f);
             }
+            if (!done_mid) {
+                mid();
+                done_mid = true;
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int i = i0 + k * NT + t;
@@ -545,8 +556,11 @@ __device__ __forceinline__ void merge_rows(const float2 *part, int b, int K, int
                     stage[i] = v[k];
             }
         }
-        __syncthreads();
     }
+    if (!done_mid)
+        mid();
+    if (staged)
+        __syncthreads();
     // A row with at most 32 partials is merged by half a wave, so that each wave takes two
     // rows at a time; the reductions then run over the half's 32 lanes, which gives the
     // same values as the 64-lane ones (there the other half only adds zeros and -inf).
@@ -596,14 +610,16 @@ __device__ __forceinline__ bool accept_test(const Draft &d, int j, int K, const 
 // Positions at or past npos are only reached by a sequence that rejects before them.
 // mask_probs: out_probs only for j <= L, NaN after (the rows after L may not have been read).
 // write: whether this workgroup writes the outputs (one of the workgroups of a split draw).
-template <int DT, int MODE>
+// mid: work for every thread while the partials load (see merge_rows).
+template <int DT, int MODE, class Mid = NoWork>
 __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
                                              const int32_t *tokens, const float *unif, int b,
                                              int K, int V, int nch, int npos, bool mask_probs,
                                              bool write, const Scale &sp, const Scale &sq,
                                              const float2 *part, float2 *stage,
                                              int32_t *acc_len, int32_t *out_tokens,
-                                             float *out_probs, SeqInfo *info)
+                                             float *out_probs, SeqInfo *info,
+                                             const Mid &mid = Mid())
 {
     __shared__ float sM[MAX_ROWS];
     __shared__ double sS[MAX_ROWS];
@@ -616,7 +632,7 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
     Draft d = {0, 0.0f, 0.0f, 0.0f, false};
     if (w == GW)
         d = gather_draft<DT, MODE>(tgt, drf, tokens, unif, b, K, V, lane);
-    merge_rows<TAIL_WG>(part, b, K, nch, npos, sp, sq, stage, sM, sS);
+    merge_rows<TAIL_WG>(part, b, K, nch, npos, sp, sq, stage, sM, sS, mid);
     if (w != GW)
         return;
 
@@ -1296,28 +1312,36 @@ __device__ __forceinline__ double tab_unit(int e)
     return __hiloint2double((TAB_E0 + e - 134 + 1023) << 20, 0);
 }
 
+// Sentinel k (0..7: table k / 4, sign (k / 2) % 2, below or above) of the tables in `which`:
+// NaN (the id takes exp2), or +0.0 above in magnitude for negative values (below -2^8) when
+// such a term is at most 2^((-2^8 - M) c) * scale <= TAB_TINY (not for contrastive factors).
+template <int MODE>
+__device__ inline void tab_sentinel(const ExactRows &x, double *tab, int which, int k)
+{
+    const int tb = k >> 2, s = (k >> 1) & 1, above = k & 1;
+    if (!((which >> tb) & 1))
+        return;
+    double v = __builtin_nan("");
+    if (above && s == 1 && !(MODE == CONTRASTIVE && tb == 0)) {
+        const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
+        const float M = tb ? x.Mq : x.Mp;
+        const double c = tb ? x.cq : x.cp, sc = tb ? 1.0 : x.r;
+        if (exp2((-top - (double)M) * c) * sc <= TAB_TINY)
+            v = 0.0;
+    }
+    tab[tb * TAB_DOUBLES + s * TAB_SIGN + (above ? TAB_HALF + 1 : 0)] = v;
+}
+
 template <int MODE>
 __device__ inline void exact_tables(const ExactRows &x, double *tab, int which)
 {
     const int t = threadIdx.x;
-    const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
     // phase 1: per table 2 * TAB_GRP group values and TAB_NE * 16 step powers (as many); then
     // the sentinels (below and above, per sign and table)
     constexpr int P1 = 4 * TAB_GRP;
     for (int k1 = t; k1 < 2 * P1 + 8; k1 += TAIL_WG) {
         if (k1 >= 2 * P1) {
-            const int k = k1 - 2 * P1, tb = k >> 2, s = (k >> 1) & 1, above = k & 1;
-            if ((which >> tb) & 1) {
-                double v = __builtin_nan("");
-                if (above && s == 1 && !(MODE == CONTRASTIVE && tb == 0)) {
-                    // values below -2^8: the term is at most 2^((-2^8 - M) c) * scale
-                    const float M = tb ? x.Mq : x.Mp;
-                    const double c = tb ? x.cq : x.cp, sc = tb ? 1.0 : x.r;
-                    if (exp2((-top - (double)M) * c) * sc <= TAB_TINY)
-                        v = 0.0;
-                }
-                tab[tb * TAB_DOUBLES + s * TAB_SIGN + (above ? TAB_HALF + 1 : 0)] = v;
-            }
+            tab_sentinel<MODE>(x, tab, which, k1 - 2 * P1);
             continue;
         }
         const int tb = k1 >= P1 ? 1 : 0, r = k1 - tb * P1;
@@ -1356,6 +1380,38 @@ __device__ inline void exact_tables(const ExactRows &x, double *tab, int which)
             T[s * TAB_SIGN + 1 + m] = gv * pw;
         }
     }
+}
+
+// Whether tables of 2^(x c) alone (no row maximum, no scale) stay inside the fp64 range, so
+// that they can be built before the accept tests have named row L: |x| < 2^8 with 256 c <= 1000
+// (contrastive factors: their products reach 512 c_p).
+template <int MODE> __device__ __forceinline__ bool tables_before_rows(double cp, double cq)
+{
+    return (MODE == SAMPLING ? 256.0 * cp : 512.0 * cp) <= 1000.0 && 256.0 * cq <= 1000.0;
+}
+
+// The tables of 2^(x c) (built with M_p = M_q = 0 and r = 1) turned into row L's: every slot
+// of table 0 times k0 = 2^(-M_p c_p) r (contrastive factors: its square root), of table 1
+// times k1 = 2^(-M_q c_q), and the sentinels for the rows' maxima.  One rounding more than
+// building them for the row.  Also rescales table 0 alone by k0 (k1 = 1, which = 1) when the
+// side-test scale changes.  The caller's barrier (LDS only suffices) follows.
+template <int MODE>
+__device__ inline void exact_rescale(const ExactRows &x, double *tab, double k0, double k1,
+                                     int which)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+        const int tb = ts >> 1, s = ts & 1;
+        if (!((which >> tb) & 1))
+            continue;
+        double *T = tab + tb * TAB_DOUBLES + s * TAB_SIGN + 1;
+        const double k = tb ? k1 : k0;
+        for (int m = t; m < TAB_HALF; m += TAIL_WG)
+            T[m] *= k;
+    }
+    if (t >= TAIL_WG - 8)
+        tab_sentinel<MODE>(x, tab, which, t - (TAIL_WG - 8));
 }
 
 // One id's a and b from its bit patterns (bfloat16: bp, bq; float32: the float bits): the
@@ -2024,10 +2080,29 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     // rows read by this call: every position, or with early exit the first `prefix` ones for
     // a sequence that was not alive after them
     const int npos = (a.alive == nullptr || a.alive[b]) ? K + 1 : a.prefix;
+    // bfloat16 verify: the tables of 2^(x c), which depend on the temperatures alone, are built
+    // while the partials load; row L's maxima and scale are multiplied in once L is known
+    const bool pre_tab = DT == 1 && K > 0 && tables_before_rows<MODE>(a.sp.c, a.sq.c);
+    struct {
+        bool on;
+        ExactRows x0;
+        double *tab;
+        __device__ void operator()() const
+        {
+            if (on)
+                exact_tables<MODE>(x0, tab, 3);
+        }
+    } build;
+    build.on = pre_tab;
+    build.x0 = {};
+    build.x0.cp = a.sp.c;
+    build.x0.cq = a.sq.c;
+    build.x0.r = 1.0;
+    build.tab = s_tab;
     accept_phase<DT, MODE>(a.tgt, a.drf, a.tokens, a.unif, b, K, V, a.nch, npos,
                            a.mask_probs != 0, g == 0, a.sp, a.sq, a.part,
                            reinterpret_cast<float2 *>(dyn), a.acc_len, a.out_tokens, a.out_probs,
-                           &s_info);
+                           &s_info, build);
     __syncthreads();
     const SeqInfo si = s_info;
     if (si.L < 0)
@@ -2068,7 +2143,14 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     if (pre)
         exact_fetch<DT>(x, (g * TAIL_WAVES + w) * gm.nsub, p0, q0);
     if (DT == 1 && x.tabled) {
-        exact_tables<MODE>(x, s_tab, 3);
+        if (pre_tab && fabs((double)si.Mp * x.cp) <= 900.0 &&
+            fabs((double)si.Mq * x.cq) <= 900.0) {
+            const double k0 = exp2(-(double)si.Mp * x.cp) * x.r;
+            exact_rescale<MODE>(x, s_tab, MODE == SAMPLING ? k0 : sqrt(k0),
+                                exp2(-(double)si.Mq * x.cq), 3);
+        } else {
+            exact_tables<MODE>(x, s_tab, 3);
+        }
         lds_barrier();
     }
     ExactLoc tot;
@@ -2161,9 +2243,10 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
                                         !(a.flags & TEST_EXACT_TWO_PASS));
         if (sure)
             break;
-        x.r *= Sb * ia;
+        const double rho = Sb * ia;  // the new side-test scale over the old one
+        x.r *= rho;
         if (DT == 1 && x.tabled) {
-            exact_tables<MODE>(x, s_tab, 1);
+            exact_rescale<MODE>(x, s_tab, MODE == SAMPLING ? rho : sqrt(rho), 1.0, 1);
             __syncthreads();
         }
         exact_pass<DT, MODE>(x, V, gm, 0, nseg, units, tot, p0, q0, false);
