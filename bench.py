@@ -44,9 +44,9 @@ WORKLOADS = {
     "c3": ("sampling verify B=256 K=8 V=128256 bf16 logits T=0.7", "row_stats",
            "k_stats_sampling<bf16>", "row_stats_bf16_B256_K8_V128256_traffic.md"),
     "c1": ("sampling verify B=1 K=4 V=1000 f32 logits T=1", "row_stats",
-           "k_stats_sampling<f32>", None),
+           "k_stats_sampling<f32>", "row_stats_f32_B1_K4_V1000_traffic.md"),
     "c2": ("sampling verify B=64 K=5 V=32000 f32 logits T=1", "row_stats",
-           "k_stats_sampling<f32>", None),
+           "k_stats_sampling<f32>", "row_stats_f32_B64_K5_V32000_traffic.md"),
     "c4": ("greedy blockwise verify B=512 K=8 V=32000 bf16 logits", "row_argmax",
            "k_argmax<bf16>", "row_argmax_bf16_B512_K8_V32000_traffic.md"),
     "c5": ("contrastive verify B=128 K=4 V=152064 bf16 logits tau=1", "row_stats",
