@@ -84,12 +84,14 @@ constexpr size_t MAX_ITEMS = 0xffffffffull;
 
 // work-items of the largest launch a context of this capacity can make, over both dtypes: the
 // row statistics and the greedy argmax (at most 2K+1 rows of float32 chunks of 8 vectors per
-// thread), the contrastive pairs (K+1 rows of the smaller pair chunks) and the draw (one
-// workgroup per sequence)
+// thread; the statistics take two chunks per workgroup, so a row of an odd number of chunks
+// launches one chunk's threads more), the contrastive pairs (K+1 rows of the smaller pair
+// chunks) and the draw (one workgroup per sequence)
 size_t largest_launch(int max_batch, int max_k, int max_vocab)
 {
     const size_t k = (size_t)max_k;
-    const size_t stats = (2 * k + 1) * (size_t)sv::num_chunks(sv::NV_STATS, 0, max_vocab);
+    const size_t nch = (size_t)sv::num_chunks(sv::NV_STATS, 0, max_vocab);
+    const size_t stats = (2 * k + 1) * (nch >= 2 ? (nch + 1) / 2 * 2 : nch);
     const size_t pairs = (k + 1) * (size_t)sv::max_chunks(max_vocab);
     const size_t per_seq = std::max(std::max(stats, pairs) * sv::WG, (size_t)sv::TAIL_WG);
     return (size_t)max_batch * per_seq;

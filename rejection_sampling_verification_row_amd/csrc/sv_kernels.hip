@@ -388,6 +388,9 @@ __device__ inline void store_wave_partials(float2 v, float2 *dst)
     }
 }
 
+// A chunk is read by 256 threads; a workgroup of 2 * WG threads reads two chunks, one per half.
+__device__ __forceinline__ int chunk_thread() { return (int)(threadIdx.x & (WG - 1)); }
+
 // Load NV vectors per thread of chunk `cbase` of a row, ids >= V as -inf.  In an aligned row
 // every vector that lies wholly below V is one streamed 16-byte load, all issued before any
 // use (a chunk at the end of the row only masks some of them off); only the vector that
@@ -402,7 +405,7 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
         uint4 raw[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY);
+            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + chunk_thread()) * E) * BY);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -412,7 +415,7 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
         uint4 raw[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int e0 = cbase + (i * WG + threadIdx.x) * E;
+            const int e0 = cbase + (i * WG + chunk_thread()) * E;
             if (e0 + E <= V)
                 raw[i] = load_stream(rp + (size_t)e0 * BY);
             else
@@ -424,7 +427,7 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
         if (V % E != 0) {
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const int e0 = cbase + (i * WG + threadIdx.x) * E;
+                const int e0 = cbase + (i * WG + chunk_thread()) * E;
                 if (e0 < V && e0 + E > V)
 #pragma unroll
                     for (int k = 0; k < E; ++k)
@@ -434,7 +437,7 @@ __device__ inline void load_chunk(const char *rp, bool al, int cbase, int V,
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            load_elems<DT>(rp, al, cbase + (i * WG + threadIdx.x) * E, V, -INFINITY, x[i]);
+            load_elems<DT>(rp, al, cbase + (i * WG + chunk_thread()) * E, V, -INFINITY, x[i]);
     }
 }
 
@@ -466,11 +469,11 @@ __device__ inline void load_chunk_words(const char *rp, bool al, int cbase, int 
     if (al && cbase + WG * NV * E <= V) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + threadIdx.x) * E) * BY);
+            raw[i] = load_stream(rp + (size_t)(cbase + (i * WG + chunk_thread()) * E) * BY);
     } else {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int e0 = cbase + (i * WG + threadIdx.x) * E;
+            const int e0 = cbase + (i * WG + chunk_thread()) * E;
             if (al && e0 + E <= V)
                 raw[i] = load_stream(rp + (size_t)e0 * BY);
             else if (e0 >= V)
@@ -717,16 +720,24 @@ __device__ __forceinline__ void sampling_chunk_stats(const char *rp, int V, int 
     }
 }
 
-// rows b*(2K+1)+r: r <= K target row (b, r), else draft row (b, r-K-1); each wave stores its
-// (max, sum) partial at part[blockIdx.x * WAVES + wave]
-template <int DT>
-__global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ tgt,
-                                                       const char *__restrict__ drf, int K, int V,
-                                                       int nch, Scale sc, float2 *part)
+// rows b*(2K+1)+r: r <= K target row (b, r), else draft row (b, r-K-1).  A workgroup of Q * WG
+// threads reads Q consecutive chunks of one row (quarter, or half, q of the workgroup reads chunk
+// Q g + q); each wave stores its (max, sum) partial at part[(row * nch + chunk) * WAVES + wave].
+// Two chunks per 512-thread workgroup: 205.3-205.6 us per call at B=256, K=8, V=128256 against
+// 210.2-211.2 with one chunk per 256-thread workgroup and 212.7-213.9 with four per 1024 (the
+// same partials, bit for bit).
+template <int DT, int Q>
+__global__ __launch_bounds__(WG * Q) void k_stats_sampling(const char *__restrict__ tgt,
+                                                           const char *__restrict__ drf, int K,
+                                                           int V, int nch, Scale sc, float2 *part)
 {
     constexpr int BY = Elt<DT>::BYTES;
     const int R = 2 * K + 1;
-    const int row = blockIdx.x / nch, c = blockIdx.x - row * nch;
+    const int ngrp = (nch + Q - 1) / Q;
+    const int row = blockIdx.x / ngrp;
+    const int c = (blockIdx.x - row * ngrp) * Q + (int)(threadIdx.x / WG);
+    if (c >= nch)
+        return;  // the row's last group has fewer than Q chunks (whole waves leave)
     const int b = row / R, r = row - b * R;
     const char *rp = (r <= K) ? tgt + ((size_t)b * (K + 1) + r) * (size_t)V * BY
                               : drf + ((size_t)b * K + (r - K - 1)) * (size_t)V * BY;
@@ -736,7 +747,7 @@ __global__ __launch_bounds__(WG) void k_stats_sampling(const char *__restrict__ 
     // 1-2.5 us faster per launch at B=256, K=8, V=128256 than one 32-byte store after a barrier)
     const float2 ws = wave_stats(m, s, sc);
     if ((threadIdx.x & 63) == 0)
-        part[(size_t)blockIdx.x * WAVES + (threadIdx.x >> 6)] = ws;
+        part[((size_t)row * nch + c) * WAVES + ((threadIdx.x >> 6) & (WAVES - 1))] = ws;
 }
 
 // One chunk of the row pair (b, j): target values l_e - l_a (fp32), draft values l_a.  The
@@ -1447,11 +1458,22 @@ __device__ __forceinline__ void exact_terms(uint32_t bp, uint32_t bq, const Exac
 }
 
 // A lane's sums over one step of its segment: A, B over the positive side (a > b), the totals
-// of a and b, and the draft mass of the ids near the threshold.
+// of a and b, and the draft mass of the ids near the threshold.  The table path only flags a
+// step with a near id (nf) and leaves its near mass to near_mass_vec, after the segment.
 struct ExactLoc {
     double A, B, tp, tq, near;
+    bool nf;
 };
 
+// whether a and b are near the threshold: upper 32 bits at most NEAR_HI apart
+__device__ __forceinline__ bool exact_near(double a, double b)
+{
+    return absdiff((uint32_t)__double2hiint(a), (uint32_t)__double2hiint(b)) <= NEAR_HI;
+}
+
+// the sums of one id, its near flag in l.nf (the table path) or its near mass in l.near (ids
+// weighed one by one)
+template <bool FLAG>
 __device__ __forceinline__ void exact_acc(double a, double b, ExactLoc &l)
 {
     const double mv = (a > b) ? 1.0 : 0.0;
@@ -1459,14 +1481,17 @@ __device__ __forceinline__ void exact_acc(double a, double b, ExactLoc &l)
     l.B = __builtin_fma(b, mv, l.B);
     l.tp += a;
     l.tq += b;
-    const uint32_t dh = absdiff((uint32_t)__double2hiint(a), (uint32_t)__double2hiint(b));
-    l.near = __builtin_fma(b, dh <= NEAR_HI ? 1.0 : 0.0, l.near);
+    if (FLAG)
+        l.nf = l.nf | exact_near(a, b);
+    else
+        l.near = __builtin_fma(b, exact_near(a, b) ? 1.0 : 0.0, l.near);
 }
 
-// One 16-byte vector of each row (bfloat16, tables): eight ids, two per word.
-template <int MODE>
-__device__ __forceinline__ void exact_fast_vec(const uint4 &vp, const uint4 &vq, const char *tab,
-                                               ExactLoc &l)
+// The terms of one 16-byte vector of each row (bfloat16, tables): eight ids, two per word, in
+// id order; f(k, a, b) takes each.
+template <int MODE, class F>
+__device__ __forceinline__ void exact_vec_terms(const uint4 &vp, const uint4 &vq, const char *tab,
+                                                const F &f)
 {
     const uint32_t P[4] = {vp.x, vp.y, vp.z, vp.w}, Q[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
@@ -1479,9 +1504,27 @@ __device__ __forceinline__ void exact_fast_vec(const uint4 &vp, const uint4 &vq,
             a0 *= tab_at(tab, t0_lo(on));
             a1 *= tab_at(tab, t0_hi(on));
         }
-        exact_acc(a0, b0, l);
-        exact_acc(a1, b1, l);
+        f(2 * k, a0, b0);
+        f(2 * k + 1, a1, b1);
     }
+}
+
+template <int MODE>
+__device__ __forceinline__ void exact_fast_vec(const uint4 &vp, const uint4 &vq, const char *tab,
+                                               ExactLoc &l)
+{
+    exact_vec_terms<MODE>(vp, vq, tab, [&](int, double a, double b) { exact_acc<true>(a, b, l); });
+}
+
+// the draft mass of the near ids of one vector pair (a flagged step, weighed again)
+template <int MODE>
+__device__ __forceinline__ double near_mass_vec(const uint4 &vp, const uint4 &vq, const char *tab)
+{
+    double n = 0.0;
+    exact_vec_terms<MODE>(vp, vq, tab, [&](int, double a, double b) {
+        n = __builtin_fma(b, exact_near(a, b) ? 1.0 : 0.0, n);
+    });
+    return n;
 }
 
 // Geometry of the fp64 pass: the row's wave vectors (64 lanes x one 16-byte vector, WV ids)
@@ -1570,7 +1613,7 @@ __device__ __forceinline__ void exact_slow_vec(const ExactRows &x, int V, int e0
         if (e0 + k < V) {
             double a, b;
             exact_terms<DT, MODE>(id_bits<DT>(vp, k), id_bits<DT>(vq, k), x, a, b);
-            exact_acc(a, b, l);
+            exact_acc<false>(a, b, l);
         }
     }
 }
@@ -1586,7 +1629,7 @@ __device__ __forceinline__ ExactLoc exact_step_ids(const ExactRows &x, int V, in
 {
     constexpr int E = Elt<DT>::EPV, WV = 64 * E;
     const int lane = threadIdx.x & 63;
-    ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0};
+    ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0, false};
 #pragma unroll
     for (int i = 0; i < NV_EXACT; ++i) {
         const int e0 = (vw0 + i) * WV + lane * E;
@@ -1631,6 +1674,7 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
     A = 0.0;
     B = 0.0;
     uint64_t redo = 0;  // bfloat16: steps to weigh id by id
+    uint64_t nearm = 0; // bfloat16: steps weighed by the tables that hold a near id
     constexpr int EXACT_BUFS = exact_bufs<DT>();
     uint4 bp[EXACT_BUFS][NV_EXACT], bq[EXACT_BUFS][NV_EXACT];
     if (x.al) {
@@ -1661,7 +1705,7 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
                 if constexpr (DT == 1) {
                     bool ok = false;
                     if (x.tabled && whole) {
-                        ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0};
+                        ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0, false};
 #pragma unroll
                         for (int i = 0; i < NV_EXACT; ++i)
                             exact_fast_vec<MODE>(bp[k][i], bq[k][i], x.tab, l);
@@ -1672,7 +1716,8 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
                         B = ok ? B + l.B : B;
                         tot.tp = ok ? tot.tp + l.tp : tot.tp;
                         tot.tq = ok ? tot.tq + l.tq : tot.tq;
-                        tot.near = ok ? tot.near + l.near : tot.near;
+                        if (ok && l.nf)
+                            nearm |= 1ull << j;
                     }
                     if (!ok)
                         redo |= 1ull << j;
@@ -1684,6 +1729,21 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
         }
     }
     if constexpr (DT == 1) {
+        // The near mass of the steps with a near id, read and looked up again: a near id is rare
+        // (a and b within ~2^-15 of each other), and keeping it out of the loop saves two
+        // instructions per id there (24.1-24.8 us against 26.0-26.2 for the pass at B=256,
+        // K=8, V=128256).
+        while (nearm) {
+            const int j = __builtin_ctzll(nearm);
+            nearm &= nearm - 1;
+            uint4 rp[NV_EXACT], rq[NV_EXACT];
+            exact_fetch<DT>(x, vbase + j * NV_EXACT, rp, rq);
+            double n = 0.0;
+#pragma unroll
+            for (int i = 0; i < NV_EXACT; ++i)
+                n += near_mass_vec<MODE>(rp[i], rq[i], x.tab);
+            tot.near += n;
+        }
         while (redo) {  // rare: values outside the tables, the row's end, an unaligned row
             const int j = __builtin_ctzll(redo);
             redo &= redo - 1;
@@ -1704,7 +1764,7 @@ __device__ inline void exact_pass(const ExactRows &x, int V, const ExactGeom &gm
                                   bool pre)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    tot = {0.0, 0.0, 0.0, 0.0, 0.0};
+    tot = {0.0, 0.0, 0.0, 0.0, 0.0, false};
     for (int s = s_first + w; s < s_end; s += TAIL_WAVES) {
         double A, B;
         exact_segment<DT, MODE>(x, V, gm, s, A, B, tot, p0, q0, pre && s == s_first + w);
@@ -2882,6 +2942,22 @@ inline bool timed(const Launch &ln, int kind) { return ln.ev && ((ln.mask >> kin
             hipLaunchKernelGGL(kernel, (grid), (block), (lds), (ln).stream, __VA_ARGS__);         \
     } while (0)
 
+// The sampling statistics over every row of B sequences (2K+1 rows each): two chunks per
+// 512-thread workgroup when a row has more than one.
+template <int DT>
+void launch_stats_sampling(const Launch &ln, int B, int K, int V, int nch, const Scale &sc,
+                           const char *t, const char *d, float2 *part)
+{
+    const size_t rows = (size_t)B * (2 * K + 1);
+    if (nch >= 2)
+        SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 2>),
+                  dim3((unsigned)(rows * (size_t)((nch + 1) / 2))), dim3(2 * WG), 0, t, d, K, V,
+                  nch, sc, part);
+    else
+        SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 1>), dim3((unsigned)rows), dim3(WG), 0,
+                  t, d, K, V, nch, sc, part);
+}
+
 template <int DT, int MODE>
 void launch_tail(const Launch &ln, const TailArgs &a, int B, size_t lds)
 {
@@ -2903,9 +2979,7 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
     const char *d = static_cast<const char *>(drf);
     const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
     if (MODE == SAMPLING) {
-        const unsigned grid = (unsigned)((size_t)B * (2 * K + 1) * nch);
-        SV_LAUNCH(ln, KIND_STATS, k_stats_sampling<DT>, dim3(grid), dim3(WG), 0, t, d, K, V, nch,
-                  sp, ws.part);
+        launch_stats_sampling<DT>(ln, B, K, V, nch, sp, t, d, ws.part);
     } else {
         const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
         SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>, dim3(grid), dim3(WG), 0, t, d, K, V,
@@ -2969,9 +3043,7 @@ hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, 
     const int *alive = nullptr;
     if (prefix == K + 1) {  // every position is in the prefix: one full pass
         if (MODE == SAMPLING)
-            SV_LAUNCH(ln, KIND_STATS, k_stats_sampling<DT>,
-                      dim3((unsigned)((size_t)B * (2 * K + 1) * nch)), dim3(WG), 0, t, d, K, V,
-                      nch, sp, ws.part);
+            launch_stats_sampling<DT>(ln, B, K, V, nch, sp, t, d, ws.part);
         else
             SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>,
                       dim3((unsigned)((size_t)B * (K + 1) * nch)), dim3(WG), 0, t, d, K, V, nch,
