@@ -195,7 +195,8 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     const size_t b_seq = align_up((size_t)max_batch * sizeof(int));
     const size_t b_gu = align_up((size_t)split_batch * nu_stride * sizeof(double));
     const size_t b_gc = align_up((size_t)split_batch * sizeof(int));
-    const size_t total = b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu + b_gc;
+    const size_t b_tab = align_up((size_t)sv::GTAB_DOUBLES * sizeof(double));
+    const size_t total = b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu + b_gc + b_tab;
 
     specverify_ctx *ctx = new (std::nothrow) specverify_ctx();
     if (!ctx)
@@ -211,6 +212,8 @@ int specverify_create(specverify_ctx **out, int device, int max_batch, int max_k
     ctx->ws.count = reinterpret_cast<int *>(p + b_part + 2 * b_seq);
     ctx->ws.gunits = reinterpret_cast<double *>(p + b_part + 2 * b_seq + align_up(sizeof(int)));
     ctx->ws.gcount = reinterpret_cast<int *>(p + b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu);
+    ctx->ws.gtab = reinterpret_cast<double *>(p + b_part + 2 * b_seq + align_up(sizeof(int)) + b_gu +
+                                              b_gc);
     ctx->ws.split_batch = split_batch;
     ctx->ws.nu_stride = nu_stride;
     ctx->ws.num_cus = cus;
@@ -275,7 +278,8 @@ int specverify_run_sampling_static(void *hip_stream, int dtype, int B, int K, in
         (out_probs && !aligned_to(out_probs, 4)))
         return SPECVERIFY_EINVAL;
     // the scratch layout: the statistics' partials, then (a draw shared by several workgroups,
-    // B <= compute units / 2) the segment sums and arrival counts of each sequence
+    // B <= compute units / 2) the segment sums and arrival counts of each sequence, then the
+    // draw's tables
     const size_t nch = (size_t)sv::num_chunks(sv::NV_STATS, dtype, V);
     const size_t b_part = align_up((size_t)B * (2 * (size_t)K + 1) * nch * sv::WAVES * sizeof(float2));
     const int nu_stride = 2 * sv::EXACT_MAX_SEGS + 3 * sv::TAIL_MAX_SPLIT;
@@ -291,7 +295,8 @@ int specverify_run_sampling_static(void *hip_stream, int dtype, int B, int K, in
     const bool split = B <= cus / 2;
     const size_t b_gu = split ? align_up((size_t)B * nu_stride * sizeof(double)) : 0;
     const size_t b_gc = split ? align_up((size_t)B * sizeof(int)) : 0;
-    if (b_part + b_gu + b_gc > sv::STATIC_SCRATCH_BYTES)
+    const size_t b_tab = align_up((size_t)sv::GTAB_DOUBLES * sizeof(double));
+    if (b_part + b_gu + b_gc + b_tab > sv::STATIC_SCRATCH_BYTES)
         return SPECVERIFY_ECAPACITY;
     void *base = nullptr;
     if (sv::static_scratch(dev, &base) != hipSuccess)
@@ -301,6 +306,7 @@ int specverify_run_sampling_static(void *hip_stream, int dtype, int B, int K, in
     ws.part = reinterpret_cast<float2 *>(p);
     ws.gunits = split ? reinterpret_cast<double *>(p + b_part) : nullptr;
     ws.gcount = split ? reinterpret_cast<int *>(p + b_part + b_gu) : nullptr;
+    ws.gtab = reinterpret_cast<double *>(p + b_part + b_gu + b_gc);
     ws.split_batch = split ? B : 0;
     ws.nu_stride = nu_stride;
     ws.num_cus = cus;

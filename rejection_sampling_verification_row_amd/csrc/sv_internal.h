@@ -41,6 +41,26 @@ constexpr int TAIL_MAX_SPLIT = 8;     // most workgroups that share one sequence
 // segment's unit sums are two fp64 values.  bfloat16 kernels also hold two 64 KiB tables in LDS.
 constexpr int NV_EXACT = 2;
 
+// The bfloat16 tables of the residual draw: one slot per bit pattern with 2^-20 <= |x| < 2^8.
+constexpr int TAB_E0 = 107;               // bfloat16 exponent field of 2^-20
+constexpr int TAB_NE = 28;                // fields 107..134: 2^-20 <= |x| < 2^8
+constexpr int TAB_LO = TAB_E0 << 7;       // the smallest tabulated magnitude's 15 low bits
+constexpr int TAB_HALF = TAB_NE * 128;    // tabulated magnitudes per sign
+// Each sign's block is 4096 doubles: slot 0 takes magnitudes below the tabulated ones, slots
+// 1..TAB_HALF the tabulated ones, slot TAB_HALF + 1 those above; the sign is bit 15 of the
+// slot's byte offset and table 1 lies 64 KiB after table 0.
+constexpr int TAB_SIGN = 4096;
+constexpr int TAB_DOUBLES = 2 * TAB_SIGN;  // one table: 64 KiB
+static_assert(TAB_HALF + 2 <= TAB_SIGN && TAB_SIGN * 8 == 0x8000, "slot byte offsets are 15 bits");
+constexpr double TAB_TINY = 0x1p-80;      // a term this far below the row's largest counts as 0
+// The per-call tables of 2^(x c) (no row maximum, no scale) that the statistics kernels write for
+// the draw: table 0 for the target law's c, table 1 for the draft law's, in the LDS layout.
+constexpr int GTAB_DOUBLES = 2 * TAB_DOUBLES;
+struct TabJob {
+    double *gtab;   // NULL: no tables this call
+    double cp, cq;  // log2(e) / T of the two laws
+};
+
 // test-only switches (specverify_set_test_flags): reach draw paths that data rarely reaches
 enum TestFlag : unsigned {
     TEST_CHUNK_FALLBACK = 1u,   // a draw from p_L alone skips the chunk draw: whole-row pass
@@ -122,6 +142,8 @@ struct Workspace {
     double *gunits;     // [split_batch][nu_stride] fp64 unit sums and per-workgroup totals of a
                         // residual draw shared by workgroups
     int *gcount;        // [split_batch] arrival counts of those workgroups, 0 between calls
+    double *gtab;       // [GTAB_DOUBLES] the draw's tables of 2^(x c), written by the statistics
+                        // kernels of each call (NULL: the draw builds them itself)
     int split_batch;    // largest batch whose draws may be shared (0: never)
     int nu_stride;      // doubles per sequence in gunits
     int num_cus;        // compute units of the device

@@ -720,6 +720,30 @@ __device__ __forceinline__ void sampling_chunk_stats(const char *rp, int V, int 
     }
 }
 
+// The per-call tables of the residual draw (see the draw below): slot k < GTAB_DOUBLES is table
+// k / TAB_DOUBLES (0: the target law's c, 1: the draft law's), sign block and slot i of the LDS
+// layout; i in 1..TAB_HALF holds 2^(v c) in fp64 for the bfloat16 value v of magnitude pattern
+// TAB_LO + i - 1, the sentinel slots 0 and TAB_HALF + 1 hold NaN, the rest 0.  The first
+// workgroups of a statistics launch write them, one slot per thread, before their chunk.
+__device__ inline void global_tables(const TabJob &tj)
+{
+    if (tj.gtab == nullptr)
+        return;
+    const int k = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (k >= GTAB_DOUBLES)
+        return;
+    const int tb = k / TAB_DOUBLES, r = k - tb * TAB_DOUBLES;
+    const int sg = r / TAB_SIGN, i = r - sg * TAB_SIGN;
+    double v = 0.0;
+    if (i == 0 || i == TAB_HALF + 1) {
+        v = __builtin_nan("");
+    } else if (i <= TAB_HALF) {
+        const uint32_t bits = ((uint32_t)(TAB_LO + i - 1) << 16) | (sg ? 0x80000000u : 0u);
+        v = exp2((double)__uint_as_float(bits) * (tb ? tj.cq : tj.cp));
+    }
+    tj.gtab[k] = v;
+}
+
 // rows b*(2K+1)+r: r <= K target row (b, r), else draft row (b, r-K-1).  A workgroup of Q * WG
 // threads reads Q consecutive chunks of one row (quarter, or half, q of the workgroup reads chunk
 // Q g + q); each wave stores its (max, sum) partial at part[(row * nch + chunk) * WAVES + wave].
@@ -729,10 +753,12 @@ __device__ __forceinline__ void sampling_chunk_stats(const char *rp, int V, int 
 template <int DT, int Q>
 __global__ __launch_bounds__(WG * Q) void k_stats_sampling(const char *__restrict__ tgt,
                                                            const char *__restrict__ drf, int K,
-                                                           int V, int nch, Scale sc, float2 *part)
+                                                           int V, int nch, Scale sc, float2 *part,
+                                                           TabJob tj)
 {
     constexpr int BY = Elt<DT>::BYTES;
     const int R = 2 * K + 1;
+    global_tables(tj);
     const int ngrp = (nch + Q - 1) / Q;
     const int row = blockIdx.x / ngrp;
     const int c = (blockIdx.x - row * ngrp) * Q + (int)(threadIdx.x / WG);
@@ -805,8 +831,10 @@ __device__ __forceinline__ void pair_chunk_stats(const char *ex, const char *am,
 template <int DT>
 __global__ __launch_bounds__(WG) void k_stats_contrastive(const char *__restrict__ ex,
                                                           const char *__restrict__ am, int K, int V,
-                                                          int nch, Scale sp, Scale sq, float2 *part)
+                                                          int nch, Scale sp, Scale sq, float2 *part,
+                                                          TabJob tj)
 {
+    global_tables(tj);
     const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
     const int b = pr / (K + 1), j = pr - b * (K + 1);
     pair_chunk_stats<DT>(ex, am, b, j, c, K, V, nch, sp, sq, part);
@@ -1206,17 +1234,6 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
 // term is negligible), which spoils the lane's sums for that step, and the lane weighs the
 // step again id by id with fp64 exp2 for those ids.
 
-constexpr int TAB_E0 = 107;               // bfloat16 exponent field of 2^-20
-constexpr int TAB_NE = 28;                // fields 107..134: 2^-20 <= |x| < 2^8
-constexpr int TAB_LO = TAB_E0 << 7;       // the smallest tabulated magnitude's 15 low bits
-constexpr int TAB_HALF = TAB_NE * 128;    // tabulated magnitudes per sign
-// Each sign's block is 4096 doubles: slot 0 takes magnitudes below the tabulated ones, slots
-// 1..TAB_HALF the tabulated ones, slot TAB_HALF + 1 those above; the sign is bit 15 of the
-// slot's byte offset and table 1 lies 64 KiB after table 0.
-constexpr int TAB_SIGN = 4096;
-constexpr int TAB_DOUBLES = 2 * TAB_SIGN;  // one table: 64 KiB
-static_assert(TAB_HALF + 2 <= TAB_SIGN && TAB_SIGN * 8 == 0x8000, "slot byte offsets are 15 bits");
-constexpr double TAB_TINY = 0x1p-80;      // a term this far below the row's largest counts as 0
 // the ids whose a and b have upper words at most this far apart count as near the threshold
 constexpr uint32_t NEAR_HI = 32;
 constexpr double NEAR_REL = 0x1p-17;      // the largest rel for which NEAR_HI holds every such id
@@ -1269,15 +1286,19 @@ __device__ __forceinline__ uint32_t absdiff(uint32_t x, uint32_t y)
 // registers from the table path
 __device__ __noinline__ double exp2_cold(double a) { return exp2(a); }
 
-// What the fp64 pass needs about the two rows.
+// What the fp64 pass needs about the two rows.  An id's terms are
+// a = 2^((z - ea) c_p) ra and b = 2^((x_q - eb) c_q) rb (z the target-side value): either
+// unscaled (ea = eb = 0, ra = 1, rb = kappa, the tables copied from the per-call tables) or
+// relative to the rows' maxima (ea = M_p, eb = M_q, ra = r, rb = 1, tables built for the row).
 struct ExactRows {
     const char *p0, *p1;     // target (expert) row L, draft (amateur) row L
     __amdgpu_buffer_rsrc_t b0, b1;  // the same rows as buffer resources (see DrawRows)
     bool al;                 // both rows 16-byte aligned
     bool tabled;             // bfloat16 rows with tables built
-    float Mp, Mq;            // the rows' maxima from the statistics (the exps' reference points)
+    float Mp, Mq;            // the rows' maxima from the statistics
     double cp, cq;           // log2(e) / T of each law
-    double r;                // the target-side scale
+    double ea, eb;           // the exps' reference points
+    double ra, rb;           // the terms' scales
     const char *tab;         // LDS: table 0 at +0, table 1 at +64 KiB
 };
 
@@ -1294,8 +1315,8 @@ __device__ __forceinline__ bool exact_tabled(float Mp, double cp, double cq)
     return 512.0 * cp <= 1000.0 && fabsf(Mp) <= 512.0f && cq <= 60.0;
 }
 
-// The LDS tables (bfloat16), by the whole workgroup.  Table 0: sampling a = 2^((x - M_p) c_p) r;
-// contrastive the factors 2^(x c_p) sqrt(2^(-M_p c_p) r).  Table 1: b = 2^((x - M_q) c_q).
+// The LDS tables (bfloat16), by the whole workgroup.  Table 0: sampling a = 2^((x - ea) c_p) ra;
+// contrastive the factors 2^(x c_p) sqrt(2^(-ea c_p) ra).  Table 1: b = 2^((x - eb) c_q) rb.
 // which: 1 table 0, 2 table 1, 3 both.  A slot's value v = +-(128 + 16 jb + j) 2^(E - 134)
 // (exponent field E = TAB_E0 + e, mantissa 16 jb + j) is the product of its group's largest
 // value (j = 15 for +, j = 0 for -) and 2^(-d c 2^(E - 134)), d its mantissa steps below it,
@@ -1325,7 +1346,8 @@ __device__ __forceinline__ double tab_unit(int e)
 
 // Sentinel k (0..7: table k / 4, sign (k / 2) % 2, below or above) of the tables in `which`:
 // NaN (the id takes exp2), or +0.0 above in magnitude for negative values (below -2^8) when
-// such a term is at most 2^((-2^8 - M) c) * scale <= TAB_TINY (not for contrastive factors).
+// such a term is at most TAB_TINY of the row's largest, 2^((-2^8 - M) c) <= TAB_TINY (not for
+// contrastive factors).
 template <int MODE>
 __device__ inline void tab_sentinel(const ExactRows &x, double *tab, int which, int k)
 {
@@ -1336,8 +1358,8 @@ __device__ inline void tab_sentinel(const ExactRows &x, double *tab, int which, 
     if (above && s == 1 && !(MODE == CONTRASTIVE && tb == 0)) {
         const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
         const float M = tb ? x.Mq : x.Mp;
-        const double c = tb ? x.cq : x.cp, sc = tb ? 1.0 : x.r;
-        if (exp2((-top - (double)M) * c) * sc <= TAB_TINY)
+        const double c = tb ? x.cq : x.cp;
+        if (exp2((-top - (double)M) * c) <= TAB_TINY)
             v = 0.0;
     }
     tab[tb * TAB_DOUBLES + s * TAB_SIGN + (above ? TAB_HALF + 1 : 0)] = v;
@@ -1366,9 +1388,9 @@ __device__ inline void exact_tables(const ExactRows &x, double *tab, int which)
                               tab_unit(e);
             double v;
             if (tb == 0 && MODE == CONTRASTIVE)
-                v = exp2(xv * c) * (exp2(-(double)x.Mp * c * 0.5) * sqrt(x.r));
+                v = exp2(xv * c) * (exp2(-x.ea * c * 0.5) * sqrt(x.ra));
             else
-                v = exp2((xv - (double)(tb ? x.Mq : x.Mp)) * c) * (tb ? 1.0 : x.r);
+                v = exp2((xv - (tb ? x.eb : x.ea)) * c) * (tb ? x.rb : x.ra);
             T[s * TAB_SIGN + TAB_SPARE0 + g] = v;
         } else {  // step power: exponent e, d steps
             const int q = r - 2 * TAB_GRP, e = q >> 4, d = q & 15;
@@ -1401,11 +1423,10 @@ template <int MODE> __device__ __forceinline__ bool tables_before_rows(double cp
     return (MODE == SAMPLING ? 256.0 * cp : 512.0 * cp) <= 1000.0 && 256.0 * cq <= 1000.0;
 }
 
-// The tables of 2^(x c) (built with M_p = M_q = 0 and r = 1) turned into row L's: every slot
-// of table 0 times k0 = 2^(-M_p c_p) r (contrastive factors: its square root), of table 1
-// times k1 = 2^(-M_q c_q), and the sentinels for the rows' maxima.  One rounding more than
-// building them for the row.  Also rescales table 0 alone by k0 (k1 = 1, which = 1) when the
-// side-test scale changes.  The caller's barrier (LDS only suffices) follows.
+// Every slot of table 0 times k0 and of table 1 times k1 (the tables in `which`), and their
+// sentinels for the rows' maxima: table 1 takes the draft side's scale kappa when the tables
+// were built without one, and the exact scale when the side test is redone.  The caller's
+// barrier (LDS only suffices) follows.
 template <int MODE>
 __device__ inline void exact_rescale(const ExactRows &x, double *tab, double k0, double k1,
                                      int which)
@@ -1421,8 +1442,30 @@ __device__ inline void exact_rescale(const ExactRows &x, double *tab, double k0,
         for (int m = t; m < TAB_HALF; m += TAIL_WG)
             T[m] *= k;
     }
-    if (t >= TAIL_WG - 8)
-        tab_sentinel<MODE>(x, tab, which, t - (TAIL_WG - 8));
+}
+
+// Table 1's tabulated slots (1..TAB_HALF of each sign) times k, two slots per 16-byte LDS
+// operation: the slot pairs (2 p, 2 p + 1), p = 1 .. TAB_HALF / 2 - 1, hold slots 2 .. TAB_HALF - 1,
+// and slots 1 and TAB_HALF (which share their pairs with the sentinels 0 and TAB_HALF + 1) are
+// taken singly.  The caller's barrier (LDS only suffices) follows.
+__device__ inline void scale_table1(double *tab, double k)
+{
+    static_assert(TAB_HALF % 2 == 0 && TAB_SIGN % 2 == 0, "slot pairs");
+    const int t = threadIdx.x;
+    constexpr int NP = TAB_HALF / 2 - 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        double2 *T = reinterpret_cast<double2 *>(tab + TAB_DOUBLES + s * TAB_SIGN);
+        for (int p = 1 + t; p <= NP; p += TAIL_WG) {
+            const double2 v = T[p];
+            T[p] = make_double2(v.x * k, v.y * k);
+        }
+        if (t == TAIL_WG - 9 - s) {  // slots 1 and TAB_HALF
+            double *S = tab + TAB_DOUBLES + s * TAB_SIGN;
+            S[1] *= k;
+            S[TAB_HALF] *= k;
+        }
+    }
 }
 
 // One id's a and b from its bit patterns (bfloat16: bp, bq; float32: the float bits): the
@@ -1444,16 +1487,16 @@ __device__ __forceinline__ void exact_terms(uint32_t bp, uint32_t bq, const Exac
     }
     const double pv = (DT == 1) ? (double)__uint_as_float(bp << 16) : (double)__uint_as_float(bp);
     const double qv = (DT == 1) ? (double)__uint_as_float(bq << 16) : (double)__uint_as_float(bq);
-    const double ap = ((MODE == SAMPLING ? pv : pv - qv) - (double)x.Mp) * x.cp;
-    const double aq = (qv - (double)x.Mq) * x.cq;
+    const double ap = ((MODE == SAMPLING ? pv : pv - qv) - x.ea) * x.cp;
+    const double aq = (qv - x.eb) * x.cq;
     if (DT == 1) {
         if (da)
-            a = exp2_cold(ap) * x.r;
+            a = exp2_cold(ap) * x.ra;
         if (db)
-            b = exp2_cold(aq);
+            b = exp2_cold(aq) * x.rb;
     } else {
-        a = exp2(ap) * x.r;
-        b = exp2(aq);
+        a = exp2(ap) * x.ra;
+        b = exp2(aq) * x.rb;
     }
 }
 
@@ -1970,6 +2013,7 @@ struct TailArgs {
                         // `prefix` positions were; NULL: every row was read
     double *gunits;     // split > 1: [B][nu_stride] the unit sums of each sequence's row pass
     int *gcount;        // split > 1: [B] workgroups done with their share; 0 between calls
+    const double *gtab; // the per-call tables of 2^(x c) the statistics kernel wrote, or NULL
     Scale sp, sq;
     int K, V, nch, prefix, mask_probs, split, nu_stride;
     unsigned flags;     // TestFlag bits
@@ -2140,29 +2184,48 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     // rows read by this call: every position, or with early exit the first `prefix` ones for
     // a sequence that was not alive after them
     const int npos = (a.alive == nullptr || a.alive[b]) ? K + 1 : a.prefix;
-    // bfloat16 verify: the tables of 2^(x c), which depend on the temperatures alone, are built
-    // while the partials load; row L's maxima and scale are multiplied in once L is known
+    // bfloat16 verify: the tables of 2^(x c), which depend on the temperatures alone, are read
+    // from the per-call tables the statistics kernel wrote (or built, without them, while the
+    // partials load); once L is known, table 1 takes the draft side's scale
     const bool pre_tab = DT == 1 && K > 0 && tables_before_rows<MODE>(a.sp.c, a.sq.c);
+    const bool copy_tab = pre_tab && a.gtab != nullptr;
+    if (copy_tab) {
+        // 128 KiB straight from memory into LDS (LDS DMA, no registers), issued first: the
+        // tables are cache-resident and arrive with the partials, which any wait for the
+        // partials then also covers.  Each wave's load places its lanes' 16-byte pieces at
+        // consecutive addresses from the wave's base, so piece i * TAIL_WG + t of the per-call
+        // tables lands in slot pair i * TAIL_WG + t.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = i * TAIL_WG + w * 64;  // the wave's first piece
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void *>(a.gtab + 2 * (piece + lane)),
+                (__attribute__((address_space(3))) void *)(s_tab + 2 * piece), 16, 0, 0);
+        }
+    }
     struct {
-        bool on;
+        bool build;
         ExactRows x0;
         double *tab;
-        __device__ void operator()() const
+        __device__ void operator()() const  // while the partials load
         {
-            if (on)
+            if (build)
                 exact_tables<MODE>(x0, tab, 3);
         }
-    } build;
-    build.on = pre_tab;
-    build.x0 = {};
-    build.x0.cp = a.sp.c;
-    build.x0.cq = a.sq.c;
-    build.x0.r = 1.0;
-    build.tab = s_tab;
+    } prep;
+    prep.build = pre_tab && !copy_tab;
+    prep.x0 = {};
+    prep.x0.cp = a.sp.c;
+    prep.x0.cq = a.sq.c;
+    prep.x0.ra = 1.0;
+    prep.x0.rb = 1.0;
+    prep.tab = s_tab;
     accept_phase<DT, MODE>(a.tgt, a.drf, a.tokens, a.unif, b, K, V, a.nch, npos,
                            a.mask_probs != 0, g == 0, a.sp, a.sq, a.part,
                            reinterpret_cast<float2 *>(dyn), a.acc_len, a.out_tokens, a.out_probs,
-                           &s_info, build);
+                           &s_info, prep);
+    if (copy_tab)  // the tables' LDS DMA (not tracked by the compiler's waits on LDS reads)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const SeqInfo si = s_info;
     if (si.L < 0)
@@ -2194,20 +2257,38 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     x.Mq = si.Mq;
     x.cp = a.sp.c;
     x.cq = a.sq.c;
-    x.r = si.Sq / si.Sp;  // sorted with the statistics' approximate sums
     x.tabled = (DT == 1) && exact_tabled<MODE>(si.Mp, x.cp, x.cq);
     x.tab = reinterpret_cast<const char *>(s_tab);
-    // this wave's first step, loaded while the tables are built
+    // Unscaled terms when the tables were made before L and every term, and the scale kappa of
+    // the draft side, stay inside the fp64 range (|M c| <= 900 on both rows, and their
+    // difference); else terms relative to the rows' maxima, with tables built for the row.
+    // Either way an id is sorted with the statistics' approximate sums: kappa =
+    // 2^(M_p c_p - M_q c_q) S~_p / S~_q, or r = S~_q / S~_p.
+    const double dp = (double)si.Mp * x.cp, dq = (double)si.Mq * x.cq;
+    const bool unscaled = DT == 1 && x.tabled && pre_tab && fabs(dp) <= 900.0 &&
+                          fabs(dq) <= 900.0 && fabs(dp - dq) <= 900.0;
+    if (unscaled) {
+        x.ea = 0.0;
+        x.eb = 0.0;
+        x.ra = 1.0;
+        x.rb = exp2(dp - dq) * (si.Sp / si.Sq);
+    } else {
+        x.ea = si.Mp;
+        x.eb = si.Mq;
+        x.ra = si.Sq / si.Sp;
+        x.rb = 1.0;
+    }
+    // this wave's first step, loaded while the tables are made
     uint4 p0[NV_EXACT], q0[NV_EXACT];
     const bool pre = x.al && g * TAIL_WAVES + w < gm.nseg;
     if (pre)
         exact_fetch<DT>(x, (g * TAIL_WAVES + w) * gm.nsub, p0, q0);
     if (DT == 1 && x.tabled) {
-        if (pre_tab && fabs((double)si.Mp * x.cp) <= 900.0 &&
-            fabs((double)si.Mq * x.cq) <= 900.0) {
-            const double k0 = exp2(-(double)si.Mp * x.cp) * x.r;
-            exact_rescale<MODE>(x, s_tab, MODE == SAMPLING ? k0 : sqrt(k0),
-                                exp2(-(double)si.Mq * x.cq), 3);
+        if (unscaled) {
+            scale_table1(s_tab, x.rb);  // table 1 times kappa
+            // the sentinels for the rows' maxima (other slots than the scaling's)
+            if (t >= TAIL_WG - 8)
+                tab_sentinel<MODE>(x, s_tab, 3, t - (TAIL_WG - 8));
         } else {
             exact_tables<MODE>(x, s_tab, 3);
         }
@@ -2296,17 +2377,19 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
         // An id may be sorted differently by the exact sums only if a / b lies between 1 and
         // theta = S_a / S_b; each such id moves the weights by at most rel (1 + rel) b / S_b.
         // Keep the draw when the near ids' draft mass bounds that far below the decision scale,
-        // else sort again with r from the exact sums (a' = a S_b / S_a against b).
-        const double rel = fabs(Sa * ib - 1.0);
+        // else sort again with the draft side scaled by theta (b' = b S_a / S_b against a).
+        // theta is a division, not S_a times a rounded 1 / S_b: equal sums (equal rows, an empty
+        // residual) must give exactly 1, or every tied id would cross to one side.
+        const double theta = Sa / Sb;  // the draft side's new scale over the old one
+        const double rel = fabs(theta - 1.0);
         const bool sure = pass == 1 || (rel <= NEAR_REL &&
                                         rel * (1.0 + rel) * near_b * ib <= 0x1p-24 * s_W &&
                                         !(a.flags & TEST_EXACT_TWO_PASS));
         if (sure)
             break;
-        const double rho = Sb * ia;  // the new side-test scale over the old one
-        x.r *= rho;
+        x.rb *= theta;
         if (DT == 1 && x.tabled) {
-            exact_rescale<MODE>(x, s_tab, MODE == SAMPLING ? rho : sqrt(rho), 1.0, 1);
+            exact_rescale<MODE>(x, s_tab, 1.0, theta, 2);
             __syncthreads();
         }
         exact_pass<DT, MODE>(x, V, gm, 0, nseg, units, tot, p0, q0, false);
@@ -2373,9 +2456,10 @@ template <int DT>
 __global__ __launch_bounds__(WG) void k_stats_prefix(const char *__restrict__ tgt,
                                                      const char *__restrict__ drf, int K, int V,
                                                      int nch, int prefix, Scale sc, float2 *part,
-                                                     int *count)
+                                                     int *count, TabJob tj)
 {
     constexpr int BY = Elt<DT>::BYTES;
+    global_tables(tj);
     const int per = 2 * prefix * nch;
     const int b = blockIdx.x / per, rem = blockIdx.x - b * per;
     const int lr = rem / nch, c = rem - lr * nch;
@@ -2459,8 +2543,9 @@ template <int DT>
 __global__ __launch_bounds__(WG) void k_pairs_prefix(const char *__restrict__ ex,
                                                      const char *__restrict__ am, int K, int V,
                                                      int nch, int prefix, Scale sp, Scale sq,
-                                                     float2 *part, int *count)
+                                                     float2 *part, int *count, TabJob tj)
 {
+    global_tables(tj);
     const int pr = blockIdx.x / nch, c = blockIdx.x - pr * nch;
     const int b = pr / prefix, j = pr - b * prefix;
     if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -2899,9 +2984,11 @@ int tail_split(const Workspace &ws, int dtype, int B, int V)
 TailArgs tail_args(const Workspace &ws, int dtype, int B, int K, int V, int nch, const Scale &sp,
                    const Scale &sq, const void *tgt, const void *drf, const int32_t *tokens,
                    const float *unif, int32_t *acc_len, int32_t *out_tokens, float *out_probs,
-                   float *draw_probs, const int *alive, int prefix, int mask_probs)
+                   float *draw_probs, const int *alive, int prefix, int mask_probs,
+                   const double *gtab)
 {
     TailArgs a;
+    a.gtab = gtab;
     a.tgt = static_cast<const char *>(tgt);
     a.drf = static_cast<const char *>(drf);
     a.tokens = tokens;
@@ -2944,18 +3031,34 @@ inline bool timed(const Launch &ln, int kind) { return ln.ev && ((ln.mask >> kin
 
 // The sampling statistics over every row of B sequences (2K+1 rows each): two chunks per
 // 512-thread workgroup when a row has more than one.
+// The draw's per-call tables (bfloat16 verify, K > 0) ride on a statistics launch of `threads`
+// work-items when it has one per slot; else NULL and the draw builds them itself.
+inline TabJob tab_job(const Workspace &ws, int dtype, int K, const Scale &sp, const Scale &sq,
+                      size_t threads)
+{
+    TabJob tj;
+    tj.gtab = (dtype == 1 && K > 0 && threads >= (size_t)GTAB_DOUBLES) ? ws.gtab : nullptr;
+    tj.cp = sp.c;
+    tj.cq = sq.c;
+    return tj;
+}
+
 template <int DT>
-void launch_stats_sampling(const Launch &ln, int B, int K, int V, int nch, const Scale &sc,
-                           const char *t, const char *d, float2 *part)
+TabJob launch_stats_sampling(const Launch &ln, const Workspace &ws, int B, int K, int V, int nch,
+                             const Scale &sc, const char *t, const char *d)
 {
     const size_t rows = (size_t)B * (2 * K + 1);
-    if (nch >= 2)
-        SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 2>),
-                  dim3((unsigned)(rows * (size_t)((nch + 1) / 2))), dim3(2 * WG), 0, t, d, K, V,
-                  nch, sc, part);
-    else
-        SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 1>), dim3((unsigned)rows), dim3(WG), 0,
-                  t, d, K, V, nch, sc, part);
+    if (nch >= 2) {
+        const size_t grid = rows * (size_t)((nch + 1) / 2);
+        const TabJob tj = tab_job(ws, DT, K, sc, sc, grid * 2 * WG);
+        SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 2>), dim3((unsigned)grid), dim3(2 * WG),
+                  0, t, d, K, V, nch, sc, ws.part, tj);
+        return tj;
+    }
+    const TabJob tj = tab_job(ws, DT, K, sc, sc, rows * WG);
+    SV_LAUNCH(ln, KIND_STATS, (k_stats_sampling<DT, 1>), dim3((unsigned)rows), dim3(WG), 0, t, d,
+              K, V, nch, sc, ws.part, tj);
+    return tj;
 }
 
 template <int DT, int MODE>
@@ -2978,15 +3081,17 @@ hipError_t sampling_impl(const Launch &ln, const Workspace &ws, int B, int K, in
     const char *t = static_cast<const char *>(tgt);
     const char *d = static_cast<const char *>(drf);
     const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
+    TabJob tj;
     if (MODE == SAMPLING) {
-        launch_stats_sampling<DT>(ln, B, K, V, nch, sp, t, d, ws.part);
+        tj = launch_stats_sampling<DT>(ln, ws, B, K, V, nch, sp, t, d);
     } else {
-        const unsigned grid = (unsigned)((size_t)B * (K + 1) * nch);
-        SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>, dim3(grid), dim3(WG), 0, t, d, K, V,
-                  nch, sp, sq, ws.part);
+        const size_t grid = (size_t)B * (K + 1) * nch;
+        tj = tab_job(ws, DT, K, sp, sq, grid * WG);
+        SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>, dim3((unsigned)grid), dim3(WG), 0, t, d,
+                  K, V, nch, sp, sq, ws.part, tj);
     }
     const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
-                                 out_tokens, out_probs, draw_probs, nullptr, K + 1, 0);
+                                 out_tokens, out_probs, draw_probs, nullptr, K + 1, 0, tj.gtab);
     launch_tail<DT, MODE>(ln, a, B, tail_lds_bytes(DT, K, V, nch));
     return hipGetLastError();
 }
@@ -3041,22 +3146,28 @@ hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, 
     const int nch = num_chunks(MODE == SAMPLING ? NV_STATS : NV_PAIR, DT, V);
     const int prefix = EARLY_PREFIX < K + 1 ? EARLY_PREFIX : K + 1;
     const int *alive = nullptr;
+    TabJob tj;
     if (prefix == K + 1) {  // every position is in the prefix: one full pass
-        if (MODE == SAMPLING)
-            launch_stats_sampling<DT>(ln, B, K, V, nch, sp, t, d, ws.part);
-        else
-            SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>,
-                      dim3((unsigned)((size_t)B * (K + 1) * nch)), dim3(WG), 0, t, d, K, V, nch,
-                      sp, sq, ws.part);
+        if (MODE == SAMPLING) {
+            tj = launch_stats_sampling<DT>(ln, ws, B, K, V, nch, sp, t, d);
+        } else {
+            const size_t grid = (size_t)B * (K + 1) * nch;
+            tj = tab_job(ws, DT, K, sp, sq, grid * WG);
+            SV_LAUNCH(ln, KIND_STATS, k_stats_contrastive<DT>, dim3((unsigned)grid), dim3(WG), 0,
+                      t, d, K, V, nch, sp, sq, ws.part, tj);
+        }
     } else {
-        if (MODE == SAMPLING)
-            SV_LAUNCH(ln, KIND_STATS, k_stats_prefix<DT>,
-                      dim3((unsigned)((size_t)B * 2 * prefix * nch)), dim3(WG), 0, t, d, K, V, nch,
-                      prefix, sp, ws.part, ws.count);
-        else
-            SV_LAUNCH(ln, KIND_STATS, k_pairs_prefix<DT>,
-                      dim3((unsigned)((size_t)B * prefix * nch)), dim3(WG), 0, t, d, K, V, nch,
-                      prefix, sp, sq, ws.part, ws.count);
+        if (MODE == SAMPLING) {
+            const size_t grid = (size_t)B * 2 * prefix * nch;
+            tj = tab_job(ws, DT, K, sp, sq, grid * WG);
+            SV_LAUNCH(ln, KIND_STATS, k_stats_prefix<DT>, dim3((unsigned)grid), dim3(WG), 0, t, d,
+                      K, V, nch, prefix, sp, ws.part, ws.count, tj);
+        } else {
+            const size_t grid = (size_t)B * prefix * nch;
+            tj = tab_job(ws, DT, K, sp, sq, grid * WG);
+            SV_LAUNCH(ln, KIND_STATS, k_pairs_prefix<DT>, dim3((unsigned)grid), dim3(WG), 0, t, d,
+                      K, V, nch, prefix, sp, sq, ws.part, ws.count, tj);
+        }
         SV_LAUNCH(ln, KIND_EARLY_ACCEPT, (k_alive<DT, MODE>), dim3(B), dim3(WG), 0, t, d, tokens,
                   unif, K, V, nch, prefix, sp, sq, ws.part, ws.alive, ws.list, ws.count);
         const size_t rows = (MODE == SAMPLING) ? (size_t)(2 * K + 1 - 2 * prefix)
@@ -3072,7 +3183,7 @@ hipError_t early_exit_impl(const Launch &ln, const Workspace &ws, int B, int K, 
         alive = ws.alive;
     }
     const TailArgs a = tail_args(ws, DT, B, K, V, nch, sp, sq, tgt, drf, tokens, unif, acc_len,
-                                 out_tokens, out_probs, nullptr, alive, prefix, 1);
+                                 out_tokens, out_probs, nullptr, alive, prefix, 1, tj.gtab);
     launch_tail<DT, MODE>(ln, a, B, tail_lds_bytes(DT, K, V, nch));
     return hipGetLastError();
 }
