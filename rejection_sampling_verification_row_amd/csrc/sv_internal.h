@@ -52,7 +52,7 @@ constexpr int TAB_HALF = TAB_NE * 128;    // tabulated magnitudes per sign
 constexpr int TAB_SIGN = 4096;
 constexpr int TAB_DOUBLES = 2 * TAB_SIGN;  // one table: 64 KiB
 static_assert(TAB_HALF + 2 <= TAB_SIGN && TAB_SIGN * 8 == 0x8000, "slot byte offsets are 15 bits");
-constexpr double TAB_TINY = 0x1p-80;      // a term this far below the row's largest counts as 0
+constexpr double TAB_TINY_LOG2 = -80.0;   // a term 2^-80 or less of the row's largest counts as 0
 // The per-call tables of 2^(x c) (no row maximum, no scale) that the statistics kernels write for
 // the draw: table 0 for the target law's c, table 1 for the draft law's, in the LDS layout.
 constexpr int GTAB_DOUBLES = 2 * TAB_DOUBLES;
@@ -130,6 +130,8 @@ struct SeqInfo {
     float isp, isq;
     float Mp, Mq;    // maximum and merged sum (fp64) of the target row L and the draft row L
     double Sp, Sq;
+    double kappa;    // L < K: 2^(M_p c_p - M_q c_q) S_p / S_q, the residual draw's draft-side
+                     // scale for terms without the rows' maxima (0 if out of range)
 };
 
 enum Mode { SAMPLING = 0, CONTRASTIVE = 1 };

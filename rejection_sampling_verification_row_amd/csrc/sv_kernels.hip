@@ -675,26 +675,50 @@ __device__ __forceinline__ void accept_phase(const char *tgt, const char *drf,
         ot[lane] = d.x;
     else if (write && lane > L && lane <= K)
         ot[lane] = -1;
+    // What the draw needs.  Its fp64 chains run as one exp2 and one division over the lanes
+    // (lane 0: 2^-e_p / S_p, lane 1: 2^-e_q / S_q, lane 2: kappa = 2^(M_p c_p - M_q c_q) times
+    // S_p / S_q, the residual draw's draft-side scale for terms without the rows' maxima).
+    const float Mp = sM[L];
+    const bool dr = L < K;
+    const float Mq = dr ? sM[K + 1 + L] : 0.0f;
+    const double Sp = sS[L], Sq = dr ? sS[K + 1 + L] : 0.0;
+    const float Rp = Mp * sp.hi, Rq = Mq * sq.hi;
+    const float ep = __builtin_fmaf(Mp, sp.lo, __builtin_fmaf(Mp, sp.hi, -Rp));
+    const float eq = __builtin_fmaf(Mq, sq.lo, __builtin_fmaf(Mq, sq.hi, -Rq));
+    const double kd = (double)Mp * sp.c - (double)Mq * sq.c;
+    const bool kok = dr && fabs(kd) <= 900.0;
+    double arg = 0.0, num = 1.0, den = 1.0;
+    if (lane == 0) {
+        arg = -(double)ep;
+        den = Sp;
+    } else if (lane == 1 && dr) {
+        arg = -(double)eq;
+        den = Sq;
+    } else if (lane == 2 && kok) {
+        arg = kd;
+        den = Sq;
+    }
+    const double e = exp2(arg);
+    if (lane == 2)
+        num = Sp;
+    else
+        num = e;
+    const double q = num / den;
     if (lane == 0) {
         if (acc_len)
             acc_len[b] = L;
-        SeqInfo si = {};
-        si.L = L;
-        const float Mp = sM[L];
-        si.Mp = Mp;
-        si.Sp = sS[L];
-        si.Rp = Mp * sp.hi;
-        const float ep = __builtin_fmaf(Mp, sp.lo, __builtin_fmaf(Mp, sp.hi, -si.Rp));
-        si.isp = (float)(exp2(-(double)ep) / sS[L]);
-        if (L < K) {
-            const float Mq = sM[K + 1 + L];
-            si.Mq = Mq;
-            si.Sq = sS[K + 1 + L];
-            si.Rq = Mq * sq.hi;
-            const float eq = __builtin_fmaf(Mq, sq.lo, __builtin_fmaf(Mq, sq.hi, -si.Rq));
-            si.isq = (float)(exp2(-(double)eq) / sS[K + 1 + L]);
-        }
-        *info = si;
+        info->L = L;
+        info->Mp = Mp;
+        info->Sp = Sp;
+        info->Rp = Rp;
+        info->isp = (float)q;
+    } else if (lane == 1) {
+        info->Mq = Mq;
+        info->Sq = Sq;
+        info->Rq = dr ? Rq : 0.0f;
+        info->isq = dr ? (float)q : 0.0f;
+    } else if (lane == 2) {
+        info->kappa = kok ? e * q : 0.0;
     }
 }
 
@@ -1346,8 +1370,8 @@ __device__ __forceinline__ double tab_unit(int e)
 
 // Sentinel k (0..7: table k / 4, sign (k / 2) % 2, below or above) of the tables in `which`:
 // NaN (the id takes exp2), or +0.0 above in magnitude for negative values (below -2^8) when
-// such a term is at most TAB_TINY of the row's largest, 2^((-2^8 - M) c) <= TAB_TINY (not for
-// contrastive factors).
+// such a term is at most 2^TAB_TINY_LOG2 of the row's largest, (-2^8 - M) c <= TAB_TINY_LOG2
+// (not for contrastive factors).
 template <int MODE>
 __device__ inline void tab_sentinel(const ExactRows &x, double *tab, int which, int k)
 {
@@ -1359,7 +1383,7 @@ __device__ inline void tab_sentinel(const ExactRows &x, double *tab, int which, 
         const double top = (double)(1 << (TAB_E0 + TAB_NE - 127));
         const float M = tb ? x.Mq : x.Mp;
         const double c = tb ? x.cq : x.cp;
-        if (exp2((-top - (double)M) * c) <= TAB_TINY)
+        if ((-top - (double)M) * c <= TAB_TINY_LOG2)
             v = 0.0;
     }
     tab[tb * TAB_DOUBLES + s * TAB_SIGN + (above ? TAB_HALF + 1 : 0)] = v;
@@ -1444,26 +1468,30 @@ __device__ inline void exact_rescale(const ExactRows &x, double *tab, double k0,
     }
 }
 
-// Table 1's tabulated slots (1..TAB_HALF of each sign) times k, two slots per 16-byte LDS
-// operation: the slot pairs (2 p, 2 p + 1), p = 1 .. TAB_HALF / 2 - 1, hold slots 2 .. TAB_HALF - 1,
-// and slots 1 and TAB_HALF (which share their pairs with the sentinels 0 and TAB_HALF + 1) are
-// taken singly.  The caller's barrier (LDS only suffices) follows.
-__device__ inline void scale_table1(double *tab, double k)
+// Table 1's tabulated slots (1..TAB_HALF of each sign) times k, from table 1 itself or (from0)
+// from table 0, two slots per 16-byte LDS operation: the slot pairs (2 p, 2 p + 1),
+// p = 1 .. TAB_HALF / 2 - 1, hold slots 2 .. TAB_HALF - 1, and slots 1 and TAB_HALF (which share
+// their pairs with the sentinels 0 and TAB_HALF + 1) are taken singly.  The caller's barrier
+// (LDS only suffices) follows.
+__device__ inline void scale_table1(double *tab, double k, bool from0)
 {
     static_assert(TAB_HALF % 2 == 0 && TAB_SIGN % 2 == 0, "slot pairs");
     const int t = threadIdx.x;
     constexpr int NP = TAB_HALF / 2 - 1;
+    const int src = from0 ? 0 : TAB_DOUBLES;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+        const double2 *F = reinterpret_cast<const double2 *>(tab + src + s * TAB_SIGN);
         double2 *T = reinterpret_cast<double2 *>(tab + TAB_DOUBLES + s * TAB_SIGN);
         for (int p = 1 + t; p <= NP; p += TAIL_WG) {
-            const double2 v = T[p];
+            const double2 v = F[p];
             T[p] = make_double2(v.x * k, v.y * k);
         }
         if (t == TAIL_WG - 9 - s) {  // slots 1 and TAB_HALF
+            const double *G = tab + src + s * TAB_SIGN;
             double *S = tab + TAB_DOUBLES + s * TAB_SIGN;
-            S[1] *= k;
-            S[TAB_HALF] *= k;
+            S[1] = G[1] * k;
+            S[TAB_HALF] = G[TAB_HALF] * k;
         }
     }
 }
@@ -2189,14 +2217,17 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     // partials load); once L is known, table 1 takes the draft side's scale
     const bool pre_tab = DT == 1 && K > 0 && tables_before_rows<MODE>(a.sp.c, a.sq.c);
     const bool copy_tab = pre_tab && a.gtab != nullptr;
+    // one law's table serves both when the two laws have the same scale (sampling verify):
+    // table 1 is then table 0 times kappa
+    const bool one_tab = a.sp.c == a.sq.c;
     if (copy_tab) {
-        // 128 KiB straight from memory into LDS (LDS DMA, no registers), issued first: the
-        // tables are cache-resident and arrive with the partials, which any wait for the
+        // 64 or 128 KiB straight from memory into LDS (LDS DMA, no registers), issued first:
+        // the tables are cache-resident and arrive with the partials, which any wait for the
         // partials then also covers.  Each wave's load places its lanes' 16-byte pieces at
         // consecutive addresses from the wave's base, so piece i * TAIL_WG + t of the per-call
         // tables lands in slot pair i * TAIL_WG + t.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        const int npiece = one_tab ? 4 : 8;
+        for (int i = 0; i < npiece; ++i) {
             const int piece = i * TAIL_WG + w * 64;  // the wave's first piece
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void *>(a.gtab + 2 * (piece + lane)),
@@ -2261,17 +2292,17 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
     x.tab = reinterpret_cast<const char *>(s_tab);
     // Unscaled terms when the tables were made before L and every term, and the scale kappa of
     // the draft side, stay inside the fp64 range (|M c| <= 900 on both rows, and their
-    // difference); else terms relative to the rows' maxima, with tables built for the row.
-    // Either way an id is sorted with the statistics' approximate sums: kappa =
-    // 2^(M_p c_p - M_q c_q) S~_p / S~_q, or r = S~_q / S~_p.
+    // difference, else kappa = 0); else terms relative to the rows' maxima, with tables built
+    // for the row.  Either way an id is sorted with the statistics' approximate sums: kappa =
+    // 2^(M_p c_p - M_q c_q) S~_p / S~_q (the accept phase's), or r = S~_q / S~_p.
     const double dp = (double)si.Mp * x.cp, dq = (double)si.Mq * x.cq;
     const bool unscaled = DT == 1 && x.tabled && pre_tab && fabs(dp) <= 900.0 &&
-                          fabs(dq) <= 900.0 && fabs(dp - dq) <= 900.0;
+                          fabs(dq) <= 900.0 && si.kappa > 0.0;
     if (unscaled) {
         x.ea = 0.0;
         x.eb = 0.0;
         x.ra = 1.0;
-        x.rb = exp2(dp - dq) * (si.Sp / si.Sq);
+        x.rb = si.kappa;
     } else {
         x.ea = si.Mp;
         x.eb = si.Mq;
@@ -2285,7 +2316,7 @@ __global__ __launch_bounds__(TAIL_WG) void k_tail(const TailArgs a)
         exact_fetch<DT>(x, (g * TAIL_WAVES + w) * gm.nsub, p0, q0);
     if (DT == 1 && x.tabled) {
         if (unscaled) {
-            scale_table1(s_tab, x.rb);  // table 1 times kappa
+            scale_table1(s_tab, x.rb, copy_tab && one_tab);  // table 1 times kappa
             // the sentinels for the rows' maxima (other slots than the scaling's)
             if (t >= TAIL_WG - 8)
                 tab_sentinel<MODE>(x, s_tab, 3, t - (TAIL_WG - 8));
