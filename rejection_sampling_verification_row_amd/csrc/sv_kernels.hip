@@ -1708,6 +1708,29 @@ __device__ __forceinline__ void exact_slow_vec(const ExactRows &x, int V, int e0
     }
 }
 
+// One vector of a whole step that read a sentinel: the ids whose two table entries are numbers
+// are weighed from them at once, as in the pass (their lookups in flight together), and only the
+// others one by one with exp2.  Weighing all sixteen one by one would wait for one table lookup
+// at a time while every other wave of the workgroup keeps the LDS busy.
+template <int MODE>
+__device__ __forceinline__ void exact_fix_vec(const ExactRows &x, const uint4 &vp, const uint4 &vq,
+                                              ExactLoc &l)
+{
+    uint32_t bad = 0;
+    exact_vec_terms<MODE>(vp, vq, x.tab, [&](int k, double a, double b) {
+        const bool sent = __builtin_isnan(a) || __builtin_isnan(b);
+        bad |= (sent ? 1u : 0u) << k;
+        exact_acc<false>(sent ? 0.0 : a, sent ? 0.0 : b, l);  // 0 and 0 add nothing
+    });
+    while (bad) {
+        const int k = __builtin_ctz(bad);
+        bad &= bad - 1;
+        double a, b;
+        exact_terms<1, MODE>(id_bits<1>(vp, k), id_bits<1>(vq, k), x, a, b);
+        exact_acc<false>(a, b, l);
+    }
+}
+
 // A step weighed id by id, for one lane: the wave vectors vw0 .. vw0 + NV_EXACT - 1 (ids >= V
 // add nothing), from the fetched words when the step is whole, else by element loads.  Out of
 // line for bfloat16 rows, where only a step with a value outside the tables (or the row's end,
@@ -1837,9 +1860,19 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
         while (redo) {  // rare: values outside the tables, the row's end, an unaligned row
             const int j = __builtin_ctzll(redo);
             redo &= redo - 1;
-            const uint4 none[NV_EXACT] = {};
-            exact_merge(exact_step_ids<DT, MODE>(x, V, vbase + j * NV_EXACT, false, none, none),
-                        A, B, tot);
+            const int vw0 = vbase + j * NV_EXACT;
+            if (x.tabled && x.al && (vw0 + NV_EXACT) * WV <= V) {
+                uint4 rp[NV_EXACT], rq[NV_EXACT];
+                exact_fetch<DT>(x, vw0, rp, rq);
+                ExactLoc l = {0.0, 0.0, 0.0, 0.0, 0.0, false};
+#pragma unroll
+                for (int i = 0; i < NV_EXACT; ++i)
+                    exact_fix_vec<MODE>(x, rp[i], rq[i], l);
+                exact_merge(l, A, B, tot);
+            } else {
+                const uint4 none[NV_EXACT] = {};
+                exact_merge(exact_step_ids<DT, MODE>(x, V, vw0, false, none, none), A, B, tot);
+            }
         }
     }
 }
