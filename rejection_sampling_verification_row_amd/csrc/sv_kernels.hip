@@ -1909,6 +1909,31 @@ __device__ __forceinline__ void exact_vec_weights(const ExactRows &x, int V, int
     constexpr int E = Elt<DT>::EPV;
     const int e0 = vw * 64 * E + (int)(threadIdx.x & 63) * E;
     const uint4 vp = exact_words<DT>(x.p0, x.al, e0, V), vq = exact_words<DT>(x.p1, x.al, e0, V);
+    if constexpr (DT == 1) {
+        if (x.tabled && e0 + E <= V) {
+            // the eight ids' table entries looked up at once (as in the pass), then exp2 for
+            // the ids that read a sentinel: the same terms, products and weights as one by one
+            uint32_t bad = 0;
+            exact_vec_terms<MODE>(vp, vq, x.tab, [&](int k, double a, double b) {
+                const bool sent = __builtin_isnan(a) || __builtin_isnan(b);
+                bad |= (sent ? 1u : 0u) << k;
+                const double d = a * ia - b * ib;
+                wv[k] = (!sent && a > b && d > 0.0) ? d : 0.0;
+            });
+            if (bad) {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if ((bad >> k) & 1u) {
+                        double a, b;
+                        exact_terms<DT, MODE>(id_bits<DT>(vp, k), id_bits<DT>(vq, k), x, a, b);
+                        const double d = a * ia - b * ib;
+                        wv[k] = (a > b && d > 0.0) ? d : 0.0;
+                    }
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         wv[k] = 0.0;
