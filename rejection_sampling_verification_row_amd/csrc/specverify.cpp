@@ -92,7 +92,8 @@ size_t largest_launch(int max_batch, int max_k, int max_vocab)
     const size_t k = (size_t)max_k;
     const size_t nch = (size_t)sv::num_chunks(sv::NV_STATS, 0, max_vocab);
     const size_t stats = (2 * k + 1) * (nch >= 2 ? (nch + 1) / 2 * 2 : nch);
-    const size_t pairs = (k + 1) * (size_t)sv::max_chunks(max_vocab);
+    const size_t mc = (size_t)sv::max_chunks(max_vocab);
+    const size_t pairs = (k + 1) * (mc >= 2 ? (mc + 1) / 2 * 2 : mc);
     const size_t per_seq = std::max(std::max(stats, pairs) * sv::WG, (size_t)sv::TAIL_WG);
     return (size_t)max_batch * per_seq;
 }
