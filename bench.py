@@ -82,13 +82,18 @@ METRIC = "verified draft positions/s + HBM GB/s vs peak at B=256 K=8 V=128256 bf
 
 
 PREHEAT_SECONDS = 0.03  # untimed calls before the warm-up steps, by wall time
+# The first few thousand kernel launches of a process enqueue slowly (about 25 us per call of
+# the sampler against 7-8 us later, through the binding or bare ctypes alike), which made a
+# small workload's loop host-bound; the first preheat therefore also makes this many calls.
+PREHEAT_FIRST_CALLS = 3000
 
 
-def preheat(step, sync, seconds: float = PREHEAT_SECONDS) -> int:
-    """Untimed calls for about `seconds` of wall time, synchronising every 8 calls so that the
-    host does not run ahead of the GPU.  The GPU raises its clocks only after ~12 ms of
-    continuous work, whatever the call size; running this before the warm-up steps keeps a
-    short --warmup from leaving the first timed steps in that ramp.  Returns the calls made."""
+def preheat(step, sync, seconds: float = PREHEAT_SECONDS, calls: int = 0) -> int:
+    """Untimed calls for about `seconds` of wall time and at least `calls` calls, synchronising
+    every 8 calls so that the host does not run ahead of the GPU.  The GPU raises its clocks
+    only after ~12 ms of continuous work, whatever the call size; running this before the
+    warm-up steps keeps a short --warmup from leaving the first timed steps in that ramp.
+    Returns the calls made."""
     t_end = time.perf_counter() + seconds
     n = 0
     while True:
@@ -96,7 +101,7 @@ def preheat(step, sync, seconds: float = PREHEAT_SECONDS) -> int:
             step(n)
             n += 1
         sync()
-        if time.perf_counter() >= t_end:
+        if time.perf_counter() >= t_end and n >= calls:
             return n
 
 
@@ -418,7 +423,7 @@ def main():
             sv.specverify_run_sampling(ctx, sh, w.dtype, B, K, V, w.temperature, tg, dr,
                                        p_toks, p_unif, p_acc, p_out, p_probs)
 
-    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize))
+    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize, calls=PREHEAT_FIRST_CALLS))
     log("warmup %d" % args.warmup)
     for i in range(args.warmup):
         step(i)
@@ -535,7 +540,7 @@ def bench_cut(args, desc, kind, kname):
     def step(i):
         sv.specverify_quantile_cut(ctx, sh, P, N, w.alpha, ps[i & 1], p_cut, p_keep, p_n)
 
-    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize))
+    log("preheat: %d calls" % preheat(step, torch.cuda.synchronize, calls=PREHEAT_FIRST_CALLS))
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
