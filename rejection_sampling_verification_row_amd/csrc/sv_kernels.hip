@@ -372,8 +372,10 @@ __device__ inline float2 wave_stats(float m, float s, const Scale &sc)
 }
 
 // Store the workgroup's four per-wave partials from one thread after a barrier, as a single
-// 32-byte write.  The contrastive statistics kernel is 1.3 us faster per launch this way than
-// with four single-lane writes; the sampling one, which has no second row, is not.
+// 32-byte write (the early-exit row statistics and the argmax kernels).  With one chunk per
+// workgroup the contrastive statistics were 1.3 us faster per launch this way than with four
+// single-lane writes; with two chunks per workgroup they store per wave, as the sampling
+// statistics always have.
 __device__ inline void store_wave_partials(float2 v, float2 *dst)
 {
     __shared__ float4 sp[WAVES / 2];
@@ -1278,8 +1280,8 @@ __device__ __forceinline__ void search_unit(const DrawRows &r, const SeqInfo &si
 // patterns, and the 7168 with 2^-20 <= |x| < 2^8 cover the logits of a language model's head.
 // A slot is found from the bit pattern with packed 16-bit integer operations, two ids at a
 // time; values outside the tables read a NaN sentinel (or +0.0 for values below -2^8 whose
-// term is negligible), which spoils the lane's sums for that step, and the lane weighs the
-// step again id by id with fp64 exp2 for those ids.
+// term is negligible), which spoils the lane's sums for that step; the lane weighs the step
+// again after its segment, the tables' terms for the other ids and fp64 exp2 for those ids.
 
 // The ids whose a and b have upper words at most NEAR_HI apart count as near the threshold.
 // Two positive doubles within a ratio 1 + d have upper words (sign, exponent, 20 mantissa
@@ -1784,8 +1786,10 @@ static_assert((MAX_VOCAB + 64 * 8 - 1) / (64 * 8) <= 64 * TAIL_WAVES * NV_EXACT,
 // totals added to tot.  float32 rows weigh every id with exp2.  For bfloat16 rows with tables a
 // whole step runs without branches; a step in which the lane read a sentinel (its sums turned
 // NaN), and the steps at the row's end or of an unaligned row, only set the step's bit, and
-// after the segment the lane weighs those steps id by id (out of the loop, so that the loop
-// keeps its registers for words in flight).  The buffers rotate through an unrolled loop.
+// after the segment the lane weighs those steps again (out of the loop, so that the loop keeps
+// its registers for words in flight): a whole step of an aligned row from the tables with
+// exp2 for its sentinel ids only, the others id by id.  The buffers rotate through an unrolled
+// loop.
 template <int DT, int MODE>
 __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom &gm, int s,
                                      double &A, double &B, ExactLoc &tot,
@@ -1796,7 +1800,7 @@ __device__ inline void exact_segment(const ExactRows &x, int V, const ExactGeom 
     const int vbase = s * gm.nsub, nst = gm.nst;
     A = 0.0;
     B = 0.0;
-    uint64_t redo = 0;  // bfloat16: steps to weigh id by id
+    uint64_t redo = 0;  // bfloat16: steps to weigh again
     uint64_t nearm = 0; // bfloat16: steps weighed by the tables that hold a near id
     constexpr int EXACT_BUFS = exact_bufs<DT>();
     uint4 bp[EXACT_BUFS][NV_EXACT], bq[EXACT_BUFS][NV_EXACT];
