@@ -25,6 +25,7 @@ its path the same way; the default is the one the headline metric is quoted on.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -105,6 +106,53 @@ def preheat(step, sync, seconds: float = PREHEAT_SECONDS, calls: int = 0) -> int
             return n
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+
+def hip_runtime():
+    """The HIP runtime library this process (torch) has loaded."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("libamdhip64.so is not loaded in this process")
+
+
+def call_times(step, n, torch):
+    """Milliseconds of each of n calls, from a pair of HIP events recorded around it on the
+    current stream.  The events are created with hipEventDisableSystemFence: they serve
+    timing only, so recording them writes back and invalidates no cache (torch's events do,
+    which adds that cost to the call being timed)."""
+    hip = hip_runtime()
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = [ctypes.c_void_p() for _ in range(2 * n)]
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed with HIP error %d" % (what, rc))
+    try:
+        for e in evs:
+            ok(hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                           ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)),
+               "hipEventCreateWithFlags")
+        for i in range(n):
+            ok(hip.hipEventRecord(evs[2 * i], sh), "hipEventRecord")
+            step(i)
+            ok(hip.hipEventRecord(evs[2 * i + 1], sh), "hipEventRecord")
+        torch.cuda.synchronize()
+        ms = []
+        for i in range(n):
+            t = ctypes.c_float()
+            ok(hip.hipEventElapsedTime(ctypes.byref(t), evs[2 * i], evs[2 * i + 1]),
+               "hipEventElapsedTime")
+            ms.append(t.value)
+        return ms
+    finally:
+        for e in evs:
+            if e.value:
+                hip.hipEventDestroy(e)
+
+
 def timed_passes(args, step, ctx, kind, sv, torch):
     """The passes after the wall-clock loop, each after a preheat that brings the clocks back
     up from the idle wait at the end of the previous one:
@@ -112,8 +160,9 @@ def timed_passes(args, step, ctx, kind, sv, torch):
       stream, in every stride-th of max(steps, 25 * stride) calls (at least 25 launches; a
       timed dispatch costs the call a few microseconds, so the events stay out of the
       wall-clock loop);
-    - per-call times: a pair of events around each of max(steps, 100) calls (their marker
+    - per-call times: a pair of HIP events around each of max(steps, 100) calls (their marker
       packets sit between calls, not between a call's kernels), for p10 / median / p90;
+      the events are created without the system-scope fence (`call_times`);
     - the per-kernel breakdown: every kernel of every 8th of 160 calls.
     Returns (dominant-kernel durations ms, per-kind sums ms, per-kind counts, stride,
     per-call ms, breakdown sums ms, breakdown counts)."""
@@ -129,14 +178,7 @@ def timed_passes(args, step, ctx, kind, sv, torch):
 
     n_c = max(args.steps, 100)
     preheat(step, torch.cuda.synchronize)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_c)]
-    for i in range(n_c):
-        ev[i][0].record()
-        step(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    call_ms = [a.elapsed_time(b) for a, b in ev]
+    call_ms = call_times(step, n_c, torch)
 
     nb = 20 * TIMING_STRIDE
     preheat(step, torch.cuda.synchronize)
@@ -491,7 +533,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "per_call_ms": {**percentiles(call_ms), "calls": len(call_ms),
-                        "how": "HIP events around each call in a pass of its own"},
+                        "how": "HIP events (no system-scope fence) around each call in a pass of its own"},
         "config": {"workload": desc, "mode": w.mode, "B": B, "K": K, "V": V,
                    "logits": synth.DTYPE_NAMES[w.dtype], "temperature": w.temperature,
                    "seed": w.seed},
@@ -562,7 +604,7 @@ def bench_cut(args, desc, kind, kname):
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "per_call_ms": {**percentiles(call_ms), "calls": len(call_ms),
-                        "how": "HIP events around each call in a pass of its own"},
+                        "how": "HIP events (no system-scope fence) around each call in a pass of its own"},
         "config": {"workload": desc, "P": P, "N": N, "alpha": w.alpha, "seed": w.seed},
         "roofline": {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
